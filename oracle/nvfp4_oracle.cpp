@@ -313,23 +313,30 @@ void orc_dequantize_bf16(const uint8_t* codes, const uint8_t* scales, float s_t,
 }
 
 // Residual score per channel (QUADS explainer §2.2-B: channels ranked by the
-// magnitude of the quantization residual).  r[m,c] = fl32(x[m,c] - v[m,c]);
-// score[c] = sum over 128-row chunks j ascending of (sum of |r[m,c]| over the
-// rows of chunk j, m ascending).  Both sums are sequential fp32 additions
-// starting from +0.  The 128-row chunking fixes the summation order.
+// magnitude of the quantization residual).  r[m,c] = fl32(x[m,c] - v[m,c]).
+// The pages fix no summation order; this one is fixed so that the score is
+// one exact fp32 value (every addition sequential, starting from +0):
+//   Q[j,i] = sum of |r[m,c]| over rows m of sub-chunk i of chunk j (16 rows,
+//            ascending m; a sub-chunk past the last row is +0),
+//   P[j]   = sum over the 8 sub-chunks i = 0..7 of Q[j,i], ascending i,
+//   score  = sum over the 128-row chunks j ascending of P[j].
 void orc_residual_scores(const void* x, int dtype, int64_t ldx, const uint8_t* codes,
                          const uint8_t* scales, float s_t, int64_t rows, int64_t K,
                          float* scores) {
-  const int64_t R = 128;
+  const int64_t kChunk = 128, kSub = 16;
   parallel_for(K, [&](int64_t c) {
     float score = 0.0f;
-    for (int64_t m0 = 0; m0 < rows; m0 += R) {
+    for (int64_t m0 = 0; m0 < rows; m0 += kChunk) {
       float part = 0.0f;
-      for (int64_t m = m0; m < std::min(rows, m0 + R); ++m) {
-        const float xv = load_elem(x, dtype, m, ldx, c);
-        const float v = dequant_elem(codes, scales, s_t, K, m, c);
-        const float r = xv - v;
-        part += std::fabs(r);
+      for (int64_t s0 = m0; s0 < m0 + kChunk; s0 += kSub) {
+        float sub = 0.0f;
+        for (int64_t m = s0; m < std::min(rows, s0 + kSub); ++m) {
+          const float xv = load_elem(x, dtype, m, ldx, c);
+          const float v = dequant_elem(codes, scales, s_t, K, m, c);
+          const float r = xv - v;
+          sub += std::fabs(r);
+        }
+        part += sub;
       }
       score += part;
     }

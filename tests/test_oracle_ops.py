@@ -20,13 +20,20 @@ def _x(seed, rows, K):
 
 
 def test_residual_scores_follow_chunked_sequential_fp32_order():
-    # 300 rows: chunks of 128, 128 and a ragged 44.
+    # 300 rows: chunks of 128, 128 and a ragged 44 (sub-chunks of 16, last one 12 rows).
     x = _x(0, 300, 64)
     codes, scales, st = oracle.quantize(x)
     v = oracle.dequantize(codes, scales, st)
     r = np.abs(x - v)  # numpy float32 subtraction, IEEE
-    parts = [np.cumsum(r[m0:m0 + 128], axis=0, dtype=np.float32)[-1] for m0 in range(0, 300, 128)]
-    ref = np.cumsum(np.stack(parts), axis=0, dtype=np.float32)[-1]
+
+    def seq(a):  # sequential fp32 sum over axis 0 (cumsum accumulates in order)
+        return np.cumsum(a, axis=0, dtype=np.float32)[-1]
+
+    parts = []
+    for m0 in range(0, 300, 128):
+        subs = [seq(r[s0:min(300, s0 + 16)]) for s0 in range(m0, min(300, m0 + 128), 16)]
+        parts.append(seq(np.stack(subs)))
+    ref = seq(np.stack(parts))
     got = oracle.residual_scores(x, codes, scales, st)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
     # bf16 input path gives the same as its fp32 image
