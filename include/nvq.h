@@ -1,0 +1,231 @@
+/*
+ * nvq.h -- C ABI of libnvq.so: NVFP4 quantization, residual-channel selection,
+ * W4A4 MoE grouped GEMM with residual compensation and asymmetric W4A16 QAT
+ * GEMMs on AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (cited by page and section; the pages print no equations):
+ *  - QUADS explainer ("QUADS: Stabilizing NVFP4 Reinforcement Learning for MoE
+ *    via QUantization-error Alignment across Dual Sides", gist.science):
+ *      §1   NVFP4 W4A4 GEMMs, E2M1 grid with 8 magnitudes per sign;
+ *      §2.1 weights take the same quantize-dequantize path on both sides,
+ *           activations are quantized online;
+ *      §2.2-A asymmetric W4A16 QAT: fake-quantized NVFP4 weights, BF16
+ *           activations in the trainer forward;
+ *      §2.2-B residual activation compensation: the channels with the largest
+ *           quantization residual get a correction added to the W4A4 output.
+ *  - TRACE post ("TRACE : un entraînement conscient de la quantification guidé
+ *    par le rollout ...", sns.style), "Fonctionnement, côté ingénierie" and
+ *    "L'idée centrale de TRACE": block-scaled FP4, the trainer takes its
+ *    rounding from the rollout's recorded quantization (codes and scales).
+ *  - NVFP4 layout the pages leave open: 16-element blocks along K, one E4M3
+ *    (OCP FP8 "FN") scale per block, one fp32 scale per tensor
+ *    s_t = amax / (6 * 448), E2M1 elements (OCP MX v1.0), round to nearest,
+ *    ties to even, two codes per byte with the even element in the low nibble.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, row-major, owned by the caller.
+ *    The library allocates nothing; scratch memory is the caller's workspace
+ *    `ws` of `ws_bytes` bytes (size it with the matching *_workspace_bytes
+ *    query; 256-byte aligned).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work on it; none synchronizes the host.  Calls that share a workspace
+ *    must be ordered on one stream.
+ *  - Checks the host can make (shapes, null pointers, 16-byte alignment of
+ *    vector-loaded tensors, workspace size) return a negative NVQ_E* code and
+ *    enqueue nothing.  A HIP launch failure returns NVQ_EHIP.
+ *  - Conditions only the device sees set bits of a status word kept in the
+ *    workspace (NVQ_STATUS_*), read with nvq_device_status().
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ */
+#ifndef NVQ_H
+#define NVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum nvq_status {
+  NVQ_OK = 0,
+  NVQ_EINVAL = -1,       /* null pointer or bad enum/value */
+  NVQ_ESHAPE = -2,       /* shape not supported (K % 16, k > K, ...) */
+  NVQ_EALIGN = -3,       /* a vector-loaded tensor is not 16-byte aligned */
+  NVQ_EWORKSPACE = -4,   /* workspace missing or too small */
+  NVQ_EHIP = -5,         /* a HIP runtime call failed */
+  NVQ_EUNSUPPORTED = -6  /* valid request this build does not implement */
+};
+
+enum nvq_dtype { NVQ_F32 = 0, NVQ_BF16 = 1 };
+
+/* device status bits (nvq_device_status) */
+enum {
+  NVQ_STATUS_NONFINITE = 1u << 0, /* a quantized input held Inf or NaN */
+  NVQ_STATUS_BAD_EXPERT = 1u << 1 /* a top-k expert id was outside [0, E) */
+};
+
+const char* nvq_status_string(int status);
+
+/* Reads the status word of workspace `ws` after `stream` drains (this call
+ * synchronizes the stream).  *flags receives NVQ_STATUS_* bits. */
+int nvq_device_status(const void* ws, void* stream, uint32_t* flags);
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4 quantization (QUADS §1, §2.1; TRACE "Fonctionnement").
+ *
+ * x        [batch, rows, K] of dtype x_dtype (NVQ_F32 or NVQ_BF16), 16-byte
+ *          aligned; K % 16 == 0.
+ * amax_in  nullable device [batch] fp32: replaces amax_t = max|x| of each
+ *          batch item (e.g. to requantize with a known scale).
+ * codes    [batch, rows, K/2]  E2M1 codes, even element in the low nibble.
+ * scales   [batch, rows, K/16] E4M3 block-scale codes (never 0x7F).
+ * tensor_scale [batch] fp32 s_t = fl32(amax_t / 2688).
+ * chan_score   nullable [K] fp32 (only with batch == 1): per-channel residual
+ *          score, the sum of |x - dequant(q(x))| over rows in a fixed order
+ *          (16-row sequential sub-chunk sums, summed in order within 128-row
+ *          chunks, chunks summed in order; every sum fp32).
+ * Decisions are exact: each scale is the E4M3 value nearest the real quotient
+ * amax_b / (6 s_t) (ties to even, saturating at 448) and each code the E2M1
+ * value nearest |x| / (s_b s_t) (ties to even, saturating at 6).
+ * Each batch item is one tensor with its own s_t (stacked expert weights).
+ * A non-finite input sets NVQ_STATUS_NONFINITE.
+ */
+size_t nvfp4_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t K);
+int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t rows, int64_t K,
+                   const float* amax_in, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                   float* chan_score, void* ws, size_t ws_bytes, void* stream);
+
+/* NVFP4 dequantization: y = sign * fl32(fl32(G * s_b) * s_t), written as fp32
+ * (y_dtype NVQ_F32) or rounded to nearest-even bf16 (NVQ_BF16).  This is the
+ * quantize-dequantize image both sides use for the weights (QUADS §2.1). */
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                     int64_t batch, int64_t rows, int64_t K, void* y, int y_dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Residual-channel selection (QUADS §2.2-B).
+ *
+ * Selects the k channels with the largest residual score (ties to the lower
+ * channel index) and writes them in rank order to idx_out [k] (int32).
+ * scores_in  nullable [K]: the chan_score of nvfp4_quantize.  When NULL the
+ *            score is recomputed from x and its NVFP4 record (codes, scales,
+ *            tensor_scale), in the same order as nvfp4_quantize.
+ * scores_out nullable [K]: receives the score used.
+ * resid_out  nullable [rows, k] bf16: the compensation operand
+ *            bf16(fl32(x - dequant(q(x))))[:, idx_out].
+ * 0 <= k <= K; k == 0 writes nothing to idx_out/resid_out.
+ */
+size_t residual_topk_workspace_bytes(int64_t rows, int64_t K, int32_t k);
+int residual_topk_channels(const void* x, int x_dtype, int64_t rows, int64_t K,
+                           const uint8_t* codes, const uint8_t* scales,
+                           const float* tensor_scale, const float* scores_in, float* scores_out,
+                           int32_t k, int32_t* idx_out, uint16_t* resid_out, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* MoE routing glue (TRACE "Fonctionnement": the router's discrete expert
+ * choice).  Per token: the topk largest of E fp32 logits, descending, ties
+ * to the lower expert id; weights = softmax over the chosen logits.
+ * logits [T, E] fp32; ids [T, topk] int32; weights [T, topk] fp32.
+ * Requires 1 <= topk <= E <= 1024. */
+int nvq_moe_route(const float* logits, int64_t T, int64_t E, int64_t topk, int32_t* ids,
+                  float* weights, void* stream);
+
+/* Token-expert pairs p = t*topk + j sorted stably by expert (histogram,
+ * exclusive scan, stable scatter).  ids [T, topk]; sorted_pair [P];
+ * expert_offsets [E+1] (rows of expert e are [off[e], off[e+1])); pos [P]
+ * the inverse map (sorted position of pair p).  An id outside [0, E) sets
+ * NVQ_STATUS_BAD_EXPERT and that pair is dropped. */
+size_t nvq_moe_permute_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+int nvq_moe_permute(const int32_t* ids, int64_t T, int64_t topk, int64_t E,
+                    int32_t* sorted_pair, int32_t* expert_offsets, int32_t* pos, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* out[t, n] = bf16( sum_j w[t, j] * y[pos[t*topk + j], n] ), j ascending, fp32
+ * accumulation.  y [P, N] bf16 in sorted-pair order. */
+int nvq_moe_combine(const uint16_t* y, const int32_t* pos, const float* weights, int64_t T,
+                    int64_t topk, int64_t N, uint16_t* out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* W4A4 MoE grouped GEMM with residual compensation (QUADS §1, §2.2-B).
+ *
+ * For every sorted row p of expert e (off[e] <= p < off[e+1]) and t = a_row[p]:
+ *   Y[p, n] = s_tA s_tW sum_c G_A[t,c] s_bA[t,c] G_W[e,n,c] s_bW[e,n,c]
+ *           + s_tW sum_j resid[t, j] G_W[e,n,idx_j] s_bW[e,n,idx_j]
+ * i.e. deq(qA) deq(qW_e)^T plus the bf16 residual of the selected channels
+ * times the dequantized weight columns.  fp32 accumulation.
+ * Epilogue NVQ_EPI_NONE writes Y (bf16 [rows, N] and/or fp32 [rows, N]);
+ * NVQ_EPI_SWIGLU writes h = bf16(silu(Y[:, :N/2]) * Y[:, N/2:]) [rows, N/2]
+ * (out_f32, if given, still receives the full pre-activation Y).
+ * Path NVQ_GEMM_DEQ16 dequantizes each NVFP4 tile exactly to 16-bit floats and
+ * feeds 16-bit MFMA; NVQ_GEMM_FP8_BLOCK runs one FP8 MFMA per 16-block and
+ * applies both block scales in fp32 (evaluated alternative). */
+enum { NVQ_EPI_NONE = 0, NVQ_EPI_SWIGLU = 1 };
+enum { NVQ_GEMM_AUTO = 0, NVQ_GEMM_DEQ16 = 1, NVQ_GEMM_FP8_BLOCK = 2 };
+
+typedef struct nvq_moe_gemm_args {
+  size_t struct_size;            /* sizeof(nvq_moe_gemm_args) */
+  int64_t rows;                  /* P: sorted rows */
+  int64_t K, N, E;
+  int64_t a_rows;                /* rows of the A record (tokens) */
+  const int32_t* a_row;          /* [rows] A row of each sorted row; NULL = identity */
+  const int32_t* expert_offsets; /* [E+1] */
+  const uint8_t* a_codes;        /* [a_rows, K/2] */
+  const uint8_t* a_scales;       /* [a_rows, K/16] */
+  const float* a_tensor_scale;   /* [1] */
+  const uint16_t* a_resid;       /* [a_rows, k] bf16 compensation operand (k > 0) */
+  const int32_t* comp_idx;       /* [k] selected channels */
+  int32_t k;
+  const uint8_t* w_codes;        /* [E, N, K/2] */
+  const uint8_t* w_scales;       /* [E, N, K/16] */
+  const float* w_tensor_scale;   /* [E] */
+  int32_t epilogue;
+  int32_t path;
+  uint16_t* out_bf16;            /* [rows, N] or [rows, N/2] (SWIGLU); nullable if out_f32 */
+  float* out_f32;                /* [rows, N] fp32 pre-epilogue; nullable */
+  void* ws;
+  size_t ws_bytes;
+} nvq_moe_gemm_args;
+
+size_t moe_gemm_workspace_bytes(int64_t rows, int64_t E);
+int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Asymmetric W4A16 QAT grouped GEMMs (QUADS §2.2-A; TRACE "L'idée centrale"):
+ * the weight is the dequantized NVFP4 record W^_e = deq(codes, scales, s_t)
+ * taken as-is from the rollout (its rounding is reused, not recomputed);
+ * activations stay bf16.  Identity straight-through gradient.
+ *   FWD   y[p, n]  = sum_c x[a_row[p], c] W^_e[n, c]        -> [rows, N]
+ *   DGRAD dx[p, c] = sum_n dy[p, n] W^_e[n, c]              -> [rows, K]
+ *   WGRAD dw[e, n, c] (+)= sum_{p of e} dy[p, n] x[a_row[p], c]  -> [E, N, K] fp32
+ * fp32 accumulation. */
+enum { NVQ_QAT_FWD = 0, NVQ_QAT_DGRAD = 1, NVQ_QAT_WGRAD = 2 };
+
+typedef struct nvq_qat_gemm_args {
+  size_t struct_size;            /* sizeof(nvq_qat_gemm_args) */
+  int32_t mode;
+  int32_t accumulate;            /* WGRAD: 1 adds to dw, 0 overwrites */
+  int64_t rows, K, N, E;
+  int64_t x_rows;
+  const int32_t* a_row;          /* [rows] row of x for each sorted row; NULL = identity */
+  const int32_t* expert_offsets; /* [E+1] */
+  const uint16_t* x;             /* [x_rows, K] bf16 (FWD, WGRAD) */
+  const uint16_t* dy;            /* [rows, N] bf16 (DGRAD, WGRAD) */
+  const uint8_t* w_codes;        /* [E, N, K/2] */
+  const uint8_t* w_scales;       /* [E, N, K/16] */
+  const float* w_tensor_scale;   /* [E] */
+  uint16_t* out_bf16;            /* FWD y / DGRAD dx, nullable if out_f32 */
+  float* out_f32;                /* FWD y / DGRAD dx fp32, nullable */
+  float* dw;                     /* WGRAD [E, N, K] */
+  void* ws;
+  size_t ws_bytes;
+} nvq_qat_gemm_args;
+
+size_t qat_gemm_workspace_bytes(int64_t rows, int64_t E);
+int qat_fakequant_gemm_w4a16(const nvq_qat_gemm_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVQ_H */

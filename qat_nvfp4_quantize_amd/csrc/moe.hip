@@ -1,0 +1,270 @@
+// MoE routing glue for the grouped GEMMs: top-k expert choice with softmax
+// weights, the stable token-to-expert permutation (histogram, exclusive scan,
+// stable scatter) and the weighted combine back to tokens.
+//
+// Method context: the TRACE post ("Fonctionnement, côté ingénierie") notes
+// that the router's discrete expert choice amplifies rounding differences;
+// QUADS explainer §4 runs an MoE.  The permutation is fully deterministic: no
+// order-dependent atomics decide any position.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "nvq.h"
+#include "nvq_device.h"
+#include "nvq_internal.h"
+
+namespace nvq {
+namespace {
+
+constexpr int kPermChunk = 1024;  // pairs per histogram/scatter chunk
+
+// Order-preserving key of an fp32 logit (non-NaN), -0 folded onto +0.
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) == 0) b = 0;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// One wave per token: topk rounds of a 64-bit (key, ~id) wave max.
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int64_t T, int E,
+                                              int topk, int32_t* __restrict__ ids,
+                                              float* __restrict__ weights) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const float* l = logits + t * E;
+  constexpr int kPer = 16;  // E <= 1024
+  uint64_t key[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = (e < E) ? (((uint64_t)ordered_key(l[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e))
+                     : 0ull;
+  }
+  double lmax = 0.0, den = 0.0;
+  float chosen[8];
+  int32_t chosen_id[8];
+  for (int j = 0; j < topk; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const uint32_t e = 0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (key[i] == best) key[i] = 0ull;
+    const float lv = l[e];
+    if (j == 0) lmax = (double)lv;
+    den += exp((double)lv - lmax);
+    if (j < 8) {
+      chosen[j] = lv;
+      chosen_id[j] = (int32_t)e;
+    }
+    if (lane == 0) ids[t * topk + j] = (int32_t)e;
+  }
+  if (lane == 0) {
+    for (int j = 0; j < topk; ++j) {
+      const float lv = j < 8 ? chosen[j] : l[ids[t * topk + j]];
+      (void)chosen_id;
+      weights[t * topk + j] = (float)(exp((double)lv - lmax) / den);
+    }
+  }
+}
+
+// Per-chunk expert histogram.
+__global__ __launch_bounds__(256) void k_perm_hist(const int32_t* __restrict__ ids, int64_t P, int E,
+                                                  int32_t* __restrict__ counts,
+                                                  uint32_t* __restrict__ status) {
+  extern __shared__ int32_t h[];
+  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int64_t p0 = (int64_t)blockIdx.x * kPermChunk;
+  uint32_t bad = 0;
+  for (int i = threadIdx.x; i < kPermChunk; i += 256) {
+    const int64_t p = p0 + i;
+    if (p < P) {
+      const int32_t e = ids[p];
+      if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+      else bad = 1;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) counts[(int64_t)blockIdx.x * E + e] = h[e];
+  if (bad) atomicOr(status, (uint32_t)NVQ_STATUS_BAD_EXPERT);
+}
+
+// One workgroup: per-expert running sums over chunks, then the exclusive scan
+// over experts.  base[c][e] = offset of expert e + pairs of e in chunks < c.
+__global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts, int64_t nchunks,
+                                                   int E, int32_t* __restrict__ offsets) {
+  __shared__ int32_t tot[1024];
+  __shared__ int32_t off[1025];
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E) {
+    for (int64_t c = 0; c < nchunks; ++c) {
+      const int32_t n = counts[c * E + e];
+      counts[c * E + e] = run;
+      run += n;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t s = 0;
+    for (int i = 0; i < E; ++i) {
+      off[i] = s;
+      s += tot[i];
+    }
+    off[E] = s;
+  }
+  __syncthreads();
+  if (e < E) {
+    for (int64_t c = 0; c < nchunks; ++c) counts[c * E + e] += off[e];
+    offsets[e] = off[e];
+  }
+  if (e == 0) offsets[E] = off[E];
+}
+
+// Stable scatter: one wave per chunk walks its pairs in order 64 at a time;
+// the rank of a pair among equal experts in a step is the popcount of the
+// lower lanes whose expert matches (found with log2(E) ballots).
+__global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__ ids, int64_t P,
+                                                    int E, const int32_t* __restrict__ base,
+                                                    int32_t* __restrict__ sorted_pair,
+                                                    int32_t* __restrict__ pos) {
+  extern __shared__ int32_t cnt[];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) cnt[e] = base[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t p0 = (int64_t)blockIdx.x * kPermChunk;
+  for (int step = 0; step < kPermChunk / 64; ++step) {
+    const int64_t p = p0 + step * 64 + lane;
+    const bool in = p < P;
+    int32_t e = in ? ids[p] : -1;
+    const bool ok = in && e >= 0 && e < E;
+    if (!ok) e = -1;
+    uint64_t match = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t m = __ballot(ok && ((e >> b) & 1));
+      match &= (ok && ((e >> b) & 1)) ? m : ~m;
+    }
+    int32_t dst = -1;
+    if (ok) {
+      const int rank = __popcll(match & lt);
+      dst = cnt[e] + rank;
+    }
+    __syncthreads();
+    if (ok) {
+      const bool last = (match >> lane) == 1ull;  // highest lane of its group
+      if (last) cnt[e] += __popcll(match);
+      sorted_pair[dst] = (int32_t)p;
+    }
+    if (in) pos[p] = dst;
+    __syncthreads();
+  }
+}
+
+// out[t, n..n+8) = bf16(sum_j w[t,j] * y[pos[t,j], n..n+8)), fp32, j ascending.
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
+                                                const int32_t* __restrict__ pos,
+                                                const float* __restrict__ w, int64_t T, int topk,
+                                                int64_t N, uint16_t* __restrict__ out) {
+  const int64_t nvec = N / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * nvec) return;
+  const int64_t t = i / nvec, v = i - t * nvec;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = 0; j < topk; ++j) {
+    const int32_t p = pos[t * topk + j];
+    if (p < 0) continue;
+    const float wj = w[t * topk + j];
+    const uint4 q = reinterpret_cast<const uint4*>(y + (int64_t)p * N)[v];
+    const uint32_t q4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      acc[2 * h] += wj * bf16_lo(q4[h]);
+      acc[2 * h + 1] += wj * bf16_hi(q4[h]);
+    }
+  }
+  uint4 o;
+  o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+  o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+  o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+  o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+  reinterpret_cast<uint4*>(out + t * N)[v] = o;
+}
+
+}  // namespace
+}  // namespace nvq
+
+using namespace nvq;
+
+extern "C" int nvq_moe_route(const float* logits, int64_t T, int64_t E, int64_t topk, int32_t* ids,
+                             float* weights, void* stream) {
+  if (!logits || !ids || !weights) return NVQ_EINVAL;
+  if (T < 0 || E < 1 || E > 1024 || topk < 1 || topk > E) return NVQ_ESHAPE;
+  if (T == 0) return NVQ_OK;
+  hipLaunchKernelGGL(k_route, dim3((unsigned)((T + 3) / 4)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), logits, T, (int)E, (int)topk, ids, weights);
+  return last_launch();
+}
+
+extern "C" size_t nvq_moe_permute_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
+  if (T < 0 || topk < 1 || E < 1) return kAlign;
+  const int64_t nchunks = std::max<int64_t>(1, (T * topk + kPermChunk - 1) / kPermChunk);
+  WsCarve c(nullptr);
+  c.take<int32_t>((size_t)(nchunks * E));
+  return c.off;
+}
+
+extern "C" int nvq_moe_permute(const int32_t* ids, int64_t T, int64_t topk, int64_t E,
+                               int32_t* sorted_pair, int32_t* expert_offsets, int32_t* pos,
+                               void* ws, size_t ws_bytes, void* stream) {
+  if (!ids || !sorted_pair || !expert_offsets || !pos || !ws) return NVQ_EINVAL;
+  if (T < 0 || topk < 1 || E < 1 || E > 1024) return NVQ_ESHAPE;
+  if (!aligned256(ws)) return NVQ_EALIGN;
+  const int64_t P = T * topk;
+  const int64_t nchunks = std::max<int64_t>(1, (P + kPermChunk - 1) / kPermChunk);
+  WsCarve c(ws);
+  int32_t* counts = c.take<int32_t>((size_t)(nchunks * E));
+  if (ws_bytes < c.off) return NVQ_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int rc = clear_status(c.status(), s)) return rc;
+  hipLaunchKernelGGL(k_perm_hist, dim3((unsigned)nchunks), dim3(256), E * sizeof(int32_t), s, ids, P,
+                     (int)E, counts, c.status());
+  if (int rc = last_launch()) return rc;
+  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, counts, nchunks, (int)E,
+                     expert_offsets);
+  if (int rc = last_launch()) return rc;
+  if (P == 0) return NVQ_OK;
+  hipLaunchKernelGGL(k_perm_scatter, dim3((unsigned)nchunks), dim3(64), E * sizeof(int32_t), s, ids,
+                     P, (int)E, counts, sorted_pair, pos);
+  return last_launch();
+}
+
+extern "C" int nvq_moe_combine(const uint16_t* y, const int32_t* pos, const float* weights,
+                               int64_t T, int64_t topk, int64_t N, uint16_t* out, void* stream) {
+  if (!y || !pos || !weights || !out) return NVQ_EINVAL;
+  if (T < 0 || topk < 1 || N <= 0 || (N & 7)) return NVQ_ESHAPE;
+  if (!aligned16(y) || !aligned16(out)) return NVQ_EALIGN;
+  const int64_t n = T * (N / 8);
+  if (n == 0) return NVQ_OK;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), y, pos, weights, T, (int)topk, N, out);
+  return last_launch();
+}

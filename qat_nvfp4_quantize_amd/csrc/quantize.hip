@@ -1,0 +1,603 @@
+// NVFP4 quantization, residual channel scores, top-k channel selection,
+// residual gather and dequantization for gfx950.
+//
+// Method: QUADS explainer §1 (E2M1 grid), §2.1 (online activation
+// quantization, shared weight quantize-dequantize path), §2.2-B (residual
+// channel selection); TRACE post "Fonctionnement, côté ingénierie" (block
+// scaling, per-element up/down rounding).  NVFP4 layout: 16-element blocks
+// along K, E4M3 block scales, fp32 tensor scale s_t = amax / (6 * 448),
+// nearest rounding with ties to even, two codes per byte (even element low).
+//
+// Every decision is exact.  The per-element fast path multiplies by an fp32
+// reciprocal scale and lets the hardware FP4 conversion round; it is taken
+// only when the approximate quotient is provably away from every E2M1
+// decision midpoint (all of which have 21 trailing zero mantissa bits).  Any
+// element near a midpoint (and any block with an extreme tensor scale) is
+// decided in fp64, where the midpoint products are exact.  The E4M3 block
+// scale uses the same scheme with its own midpoints.
+//
+// This translation unit is compiled with -ffp-contract=off: the dequantized
+// value fl32(fl32(G s_b) s_t) and the residual fl32(x - v) are two separate
+// roundings by definition.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "nvq.h"
+#include "nvq_device.h"
+#include "nvq_internal.h"
+
+namespace nvq {
+namespace {
+
+constexpr int kAmaxThreads = 256;
+constexpr int kAmaxWgMax = 1024;     // workgroups per call, split over batch items
+constexpr int kQRows = 128;          // rows per quantize workgroup (one score chunk)
+constexpr int kQSub = 16;            // rows per wave (one score sub-chunk)
+constexpr int kQBlocksPerWave = 64;  // 16-element blocks per wave row (one per lane)
+constexpr int kQCols = kQBlocksPerWave * 16;
+
+// Pass 1 workgroups per batch item; a pure function of the shape so the
+// workspace query and the launch agree.
+int amax_wg_per_item(int64_t batch, int64_t n_vec_per_item) {
+  int64_t per_item = std::max<int64_t>(1, kAmaxWgMax / std::max<int64_t>(batch, 1));
+  int64_t need = (n_vec_per_item + kAmaxThreads * 4 - 1) / (kAmaxThreads * 4);
+  return (int)std::max<int64_t>(1, std::min(per_item, need));
+}
+
+// ---------------------------------------------------------------- pass 1 --
+// Per-wave partial max of |x| (as fp32 bits) over a strided slice of one batch
+// item; reduced with DPP, no LDS.  Non-finite values compare above all finite
+// ones and are reported by pass 2.  Also clears the status word.
+template <bool kBF16>
+__global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4* __restrict__ x,
+                                                      int64_t vec_per_item, int nwg,
+                                                      uint32_t* __restrict__ partial,
+                                                      uint32_t* __restrict__ status) {
+  const int item = blockIdx.y;
+  const uint4* xi = x + (int64_t)item * vec_per_item;
+  const int64_t stride = (int64_t)nwg * kAmaxThreads;
+  int64_t v = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+  uint32_t m = 0;
+  auto fold = [&](uint4 q) {
+    if (kBF16) {
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    } else {
+      m = max(m, max(max(q.x & 0x7FFFFFFFu, q.y & 0x7FFFFFFFu),
+                     max(q.z & 0x7FFFFFFFu, q.w & 0x7FFFFFFFu)));
+    }
+  };
+  for (; v + 3 * stride < vec_per_item; v += 4 * stride) {
+    const uint4 a = xi[v], b = xi[v + stride], c = xi[v + 2 * stride], d = xi[v + 3 * stride];
+    fold(a);
+    fold(b);
+    fold(c);
+    fold(d);
+  }
+  for (; v < vec_per_item; v += stride) fold(xi[v]);
+  if (kBF16) m <<= 16;
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0)
+    partial[(int64_t)item * nwg * (kAmaxThreads / 64) + blockIdx.x * (kAmaxThreads / 64) +
+            (threadIdx.x >> 6)] = m;
+  if (status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;
+}
+
+__global__ void k_clear_status(uint32_t* status) { *status = 0; }
+
+// ---------------------------------------------------------------- pass 2 --
+// Workgroup = 8 waves = one 128-row chunk x 1024 columns; wave w = the 16-row
+// sub-chunk w; lane l = one 16-element block column.  Each lane quantizes its
+// block in each of its 16 rows and keeps 16 per-column residual sums
+// (sequential in row order).  The chunk partial is the in-order sum of the 8
+// wave sums, via LDS.
+template <bool kBF16, bool kScore>
+__global__ __launch_bounds__(512) void k_quantize(
+    const void* __restrict__ xv, int64_t rows, int64_t K, const uint32_t* __restrict__ amax_partial,
+    int n_partial, const float* __restrict__ amax_in, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tensor_scale,
+    float* __restrict__ chunk_partial, uint32_t* __restrict__ status) {
+  __shared__ float s_part[kScore ? 8 * kQCols : 1];
+  __shared__ float s_amax;
+  const int item = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  if (wave == 0) {
+    uint32_t m = 0;
+    if (amax_in) {
+      m = __float_as_uint(amax_in[item]);
+    } else {
+      const uint32_t* p = amax_partial + (int64_t)item * n_partial;
+      for (int i = lane; i < n_partial; i += 64) m = max(m, p[i]);
+      m = wave_max_u32(m);
+    }
+    if (lane == 0) s_amax = __uint_as_float(m);
+  }
+  __syncthreads();
+  const float amax = s_amax;
+  // s_t = fl32(amax / 2688): the fp64 quotient rounded to fp32 equals the
+  // correctly rounded fp32 quotient (53 >= 2*24 + 2).
+  const float s_t = (float)((double)amax / 2688.0);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) tensor_scale[item] = s_t;
+  const double six_st = 6.0 * (double)s_t;  // exact
+  // Extreme tensor scales would overflow the fp32 reciprocals: decide all in fp64.
+  const bool fast = (s_t >= 0x1p-100f) && (s_t <= 0x1p100f);
+  const float g = fast ? (float)(1.0 / six_st) : 0.0f;
+  const float inv_st = fast ? (float)(1.0 / (double)s_t) : 0.0f;
+
+  const int64_t nblk = K >> 4;
+  const int64_t blk = (int64_t)blockIdx.x * kQBlocksPerWave + lane;
+  const int64_t r0 = (int64_t)blockIdx.y * kQRows + wave * kQSub;
+  const bool active = blk < nblk;
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+  uint32_t bad = 0;
+
+  if (active) {
+    const int64_t item_row0 = (int64_t)item * rows;
+    for (int rr = 0; rr < kQSub; ++rr) {
+      const int64_t r = r0 + rr;
+      if (r >= rows) break;
+      const int64_t row = item_row0 + r;
+      float xf[16];
+      if (kBF16) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + row * K + blk * 16);
+        const uint4 a = p[0], b = p[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xf[2 * j] = bf16_lo(w[j]);
+          xf[2 * j + 1] = bf16_hi(w[j]);
+        }
+      } else {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(xv) + row * K + blk * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 q = p[j];
+          xf[4 * j] = q.x;
+          xf[4 * j + 1] = q.y;
+          xf[4 * j + 2] = q.z;
+          xf[4 * j + 3] = q.w;
+        }
+      }
+      float am = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(xf[j]));
+      if (!(am <= 3.40282347e38f)) bad = 1;
+
+      // Block scale: the E4M3 value nearest amax_b / (6 s_t).
+      uint32_t sc = 0;
+      if (s_t > 0.0f) {
+        if (fast) {
+          const float q = am * g;
+          const uint32_t qb = __float_as_uint(q);
+          // E4M3 midpoints have 19 trailing zero mantissa bits; q is within
+          // 2 ulp of the real quotient.
+          const bool near = (uint32_t)((qb << 13) + (8u << 13)) < (16u << 13);
+          sc = near ? e4m3_code_exact(am, six_st) : e4m3_rne_f32(q);
+        } else {
+          sc = e4m3_code_exact(am, six_st);
+        }
+      }
+      const float s_b = e4m3_to_f32(sc);
+
+      // Element codes.
+      uint32_t cw[2] = {0u, 0u};
+      bool need_exact = !fast;
+      if (fast) {
+        const float h = (sc == 0) ? 0.0f : __builtin_amdgcn_rcpf(s_b) * inv_st;
+        uint32_t near_any = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float y0 = xf[2 * j] * h, y1 = xf[2 * j + 1] * h;
+          // E2M1 midpoints (0.25 .. 5) have 21 trailing zero mantissa bits;
+          // |y| is within 4 ulp of the real quotient.  Values below 0.140625
+          // are clamped away from the test (they round to 0 either way).
+          const uint32_t b0 = max(__float_as_uint(y0) & 0x7FFFFFFFu, 0x3E100000u);
+          const uint32_t b1 = max(__float_as_uint(y1) & 0x7FFFFFFFu, 0x3E100000u);
+          near_any |= (uint32_t)((b0 << 11) + (16u << 11) < (32u << 11));
+          near_any |= (uint32_t)((b1 << 11) + (16u << 11) < (32u << 11));
+          uint32_t& w = cw[j >> 2];
+          switch (j & 3) {
+            case 0: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y0, y1, 1.0f, 0); break;
+            case 1: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y0, y1, 1.0f, 1); break;
+            case 2: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y0, y1, 1.0f, 2); break;
+            default: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y0, y1, 1.0f, 3); break;
+          }
+        }
+        need_exact = near_any != 0;
+      }
+      if (need_exact) {
+        const double S = (double)s_b * (double)s_t;  // exact (<= 28 bits)
+        cw[0] = cw[1] = 0u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t idx = (sc == 0) ? 0u : e2m1_index_exact(fabsf(xf[j]), S);
+          const uint32_t nib = idx | ((__float_as_uint(xf[j]) >> 28) & 8u);
+          cw[j >> 3] |= nib << (4 * (j & 7));
+        }
+      }
+      *reinterpret_cast<uint2*>(codes + row * (K >> 1) + blk * 8) = make_uint2(cw[0], cw[1]);
+      scales[row * nblk + blk] = (uint8_t)sc;
+
+      if (kScore) {
+        // v = fl32(fl32(|G| s_b) s_t); |r| = | |x| - v | (= |fl32(x - v)|).
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w = cw[j >> 2];
+          float2 gg;
+          switch (j & 3) {
+            case 0: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); gg = make_float2(t[0], t[1]); break; }
+            case 1: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); gg = make_float2(t[0], t[1]); break; }
+            case 2: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); gg = make_float2(t[0], t[1]); break; }
+            default: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); gg = make_float2(t[0], t[1]); break; }
+          }
+          const float v0 = (fabsf(gg.x) * s_b) * s_t;
+          const float v1 = (fabsf(gg.y) * s_b) * s_t;
+          const float d0 = fabsf(xf[2 * j]) - v0;
+          const float d1 = fabsf(xf[2 * j + 1]) - v1;
+          acc[2 * j] += fabsf(d0);
+          acc[2 * j + 1] += fabsf(d1);
+        }
+      }
+    }
+  }
+
+  if (kScore) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s_part[wave * kQCols + lane * 16 + j] = acc[j];
+    __syncthreads();
+    for (int cc = threadIdx.x; cc < kQCols; cc += 512) {
+      const int64_t col = (int64_t)blockIdx.x * kQCols + cc;
+      if (col < K) {
+        float P = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) P += s_part[w * kQCols + cc];
+        chunk_partial[(int64_t)blockIdx.y * K + col] = P;
+      }
+    }
+  }
+  if (wave_or_u32(bad) && lane == 0) atomicOr(status, (uint32_t)NVQ_STATUS_NONFINITE);
+}
+
+// score[c] = sum over chunks j ascending of P[j][c] (fp32, sequential).
+__global__ __launch_bounds__(256) void k_score_reduce(const float* __restrict__ partial,
+                                                     int64_t nchunks, int64_t K,
+                                                     float* __restrict__ score) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= K) return;
+  float s = 0.0f;
+  for (int64_t j = 0; j < nchunks; ++j) s += partial[j * K + c];
+  score[c] = s;
+}
+
+// Recomputes the residual sub-chunk/chunk partials from an existing NVFP4
+// record (no requantization): same order as k_quantize.
+template <bool kBF16>
+__global__ __launch_bounds__(512) void k_resid_partials(const void* __restrict__ xv, int64_t rows,
+                                                       int64_t K, const uint8_t* __restrict__ codes,
+                                                       const uint8_t* __restrict__ scales,
+                                                       const float* __restrict__ tensor_scale,
+                                                       float* __restrict__ chunk_partial) {
+  __shared__ float s_part[8 * kQCols];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float s_t = tensor_scale[0];
+  const int64_t nblk = K >> 4;
+  const int64_t blk = (int64_t)blockIdx.x * kQBlocksPerWave + lane;
+  const int64_t r0 = (int64_t)blockIdx.y * kQRows + wave * kQSub;
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+  if (blk < nblk) {
+    for (int rr = 0; rr < kQSub; ++rr) {
+      const int64_t r = r0 + rr;
+      if (r >= rows) break;
+      const uint2 cwv = *reinterpret_cast<const uint2*>(codes + r * (K >> 1) + blk * 8);
+      const uint32_t cw[2] = {cwv.x, cwv.y};
+      const float s_b = e4m3_to_f32(scales[r * nblk + blk]);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t c = blk * 16 + j;
+        const float xj = kBF16 ? bf16_to_f32(static_cast<const uint16_t*>(xv)[r * K + c])
+                               : static_cast<const float*>(xv)[r * K + c];
+        const uint32_t nib = (cw[j >> 3] >> (4 * (j & 7))) & 7u;
+        const float v = (e2m1_mag(nib) * s_b) * s_t;
+        acc[j] += fabsf(fabsf(xj) - v);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s_part[wave * kQCols + lane * 16 + j] = acc[j];
+  __syncthreads();
+  for (int cc = threadIdx.x; cc < kQCols; cc += 512) {
+    const int64_t col = (int64_t)blockIdx.x * kQCols + cc;
+    if (col < K) {
+      float P = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) P += s_part[w * kQCols + cc];
+      chunk_partial[(int64_t)blockIdx.y * K + col] = P;
+    }
+  }
+}
+
+// Top-k of K scores by (score desc, index asc) with a bitonic sort of 64-bit
+// keys in LDS; one workgroup.  Kp = padded power of two.
+__global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ score, int K, int Kp,
+                                              int k, int32_t* __restrict__ idx_out) {
+  extern __shared__ uint64_t keys[];
+  for (int i = threadIdx.x; i < Kp; i += 1024)
+    keys[i] = (i < K) ? (((uint64_t)__float_as_uint(score[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i))
+                      : 0ull;
+  __syncthreads();
+  for (int size = 2; size <= Kp; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (Kp >> 1); i += 1024) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t a = keys[lo], b = keys[hi];
+        if ((a < b) == up) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int j = threadIdx.x; j < k; j += 1024)
+    idx_out[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)(keys[j] & 0xFFFFFFFFull));
+}
+
+// resid[m, j] = bf16(fl32(x[m, idx[j]] - v[m, idx[j]])).
+template <bool kBF16>
+__global__ __launch_bounds__(256) void k_resid_gather(const void* __restrict__ xv, int64_t rows,
+                                                     int64_t K, const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales,
+                                                     const float* __restrict__ tensor_scale,
+                                                     const int32_t* __restrict__ idx, int k,
+                                                     uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * k) return;
+  const int64_t m = i / k;
+  const int64_t c = idx[i - m * k];
+  const float xj = kBF16 ? bf16_to_f32(static_cast<const uint16_t*>(xv)[m * K + c])
+                         : static_cast<const float*>(xv)[m * K + c];
+  const uint32_t byte = codes[m * (K >> 1) + (c >> 1)];
+  const uint32_t nib = (c & 1) ? (byte >> 4) : (byte & 15u);
+  const uint32_t mi = nib & 7u;
+  const float mag = (e2m1_mag(mi) * e4m3_to_f32(scales[m * (K >> 4) + (c >> 4)])) * tensor_scale[0];
+  const float v = (nib & 8u) ? -mag : mag;
+  const float r = xj - v;
+  out[i] = (uint16_t)f32_to_bf16_rne(r);
+}
+
+// Dequantize 8 elements (one code word) per thread.
+template <bool kOutBF16>
+__global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ codes,
+                                                const uint8_t* __restrict__ scales,
+                                                const float* __restrict__ tensor_scale,
+                                                int64_t n_words, int64_t words_per_item,
+                                                void* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_words) return;
+  const float s_t = tensor_scale[i / words_per_item];
+  const float s_b = e4m3_to_f32(scales[i >> 1]);
+  const uint32_t w = codes[i];
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float2 gg;
+    switch (j) {
+      case 0: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); gg = make_float2(t[0], t[1]); break; }
+      case 1: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); gg = make_float2(t[0], t[1]); break; }
+      case 2: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); gg = make_float2(t[0], t[1]); break; }
+      default: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); gg = make_float2(t[0], t[1]); break; }
+    }
+    v[2 * j] = (gg.x * s_b) * s_t;
+    v[2 * j + 1] = (gg.y * s_b) * s_t;
+  }
+  if (kOutBF16) {
+    uint4 o;
+    o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+    o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+    o.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
+    o.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
+    static_cast<uint4*>(y)[i] = o;
+  } else {
+    float4* o = static_cast<float4*>(y) + 2 * i;
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+struct QuantLayout {
+  int nwg;        // pass-1 workgroups per item
+  int n_partial;  // pass-1 wave partials per item
+  int64_t nchunks;
+  size_t bytes;
+  uint32_t* status;
+  uint32_t* amax_partial;
+  float* chunk_partial;
+};
+
+QuantLayout quant_layout(void* ws, int64_t batch, int64_t rows, int64_t K, int x_dtype) {
+  QuantLayout L;
+  const int64_t elem_bytes = (x_dtype == NVQ_BF16) ? 2 : 4;
+  const int64_t vec_per_item = rows * K * elem_bytes / 16;
+  L.nwg = amax_wg_per_item(batch, vec_per_item);
+  L.n_partial = L.nwg * (kAmaxThreads / 64);
+  L.nchunks = (rows + kQRows - 1) / kQRows;
+  WsCarve c(ws);
+  L.amax_partial = c.take<uint32_t>((size_t)batch * L.n_partial);
+  L.chunk_partial = c.take<float>((size_t)L.nchunks * K);
+  L.bytes = c.off;
+  L.status = c.status();
+  return L;
+}
+
+}  // namespace
+
+int topk_launch(const float* score, int64_t K, int32_t k, int32_t* idx, hipStream_t s) {
+  if (k == 0) return NVQ_OK;
+  int Kp = 1;
+  while (Kp < K) Kp <<= 1;
+  if (Kp > 8192) return NVQ_EUNSUPPORTED;  // 64 KB of LDS keys
+  if (Kp < 2) Kp = 2;
+  hipLaunchKernelGGL(k_topk, dim3(1), dim3(1024), Kp * sizeof(uint64_t), s, score, (int)K, Kp, (int)k,
+                     idx);
+  return last_launch();
+}
+
+}  // namespace nvq
+
+using namespace nvq;
+
+extern "C" size_t nvfp4_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t K) {
+  if (batch <= 0 || rows < 0 || K <= 0) return kAlign;
+  // sized for the larger (fp32) element type so one query serves both dtypes
+  return std::max(quant_layout(nullptr, batch, rows, K, NVQ_F32).bytes,
+                  quant_layout(nullptr, batch, rows, K, NVQ_BF16).bytes);
+}
+
+extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t rows, int64_t K,
+                              const float* amax_in, uint8_t* codes, uint8_t* scales,
+                              float* tensor_scale, float* chan_score, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!x || !codes || !scales || !tensor_scale || !ws) return NVQ_EINVAL;
+  if (x_dtype != NVQ_F32 && x_dtype != NVQ_BF16) return NVQ_EINVAL;
+  if (batch <= 0 || rows < 0 || K <= 0 || (K & 15)) return NVQ_ESHAPE;
+  if (chan_score && batch != 1) return NVQ_ESHAPE;
+  if (!aligned16(x) || ((uintptr_t)codes & 7u)) return NVQ_EALIGN;
+  if (!aligned256(ws)) return NVQ_EALIGN;
+  QuantLayout L = quant_layout(ws, batch, rows, K, x_dtype);
+  if (ws_bytes < L.bytes) return NVQ_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = x_dtype == NVQ_BF16;
+  if (rows == 0) {
+    hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, s, L.status);
+    return last_launch();
+  }
+  if (!amax_in) {
+    const int64_t vec_per_item = rows * K * (bf16 ? 2 : 4) / 16;
+    dim3 grid(L.nwg, (unsigned)batch);
+    if (bf16)
+      hipLaunchKernelGGL(k_amax<true>, grid, dim3(kAmaxThreads), 0, s,
+                         static_cast<const uint4*>(x), vec_per_item, L.nwg, L.amax_partial, L.status);
+    else
+      hipLaunchKernelGGL(k_amax<false>, grid, dim3(kAmaxThreads), 0, s,
+                         static_cast<const uint4*>(x), vec_per_item, L.nwg, L.amax_partial, L.status);
+  } else {
+    hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, s, L.status);
+  }
+  if (int rc = last_launch()) return rc;
+  dim3 grid((unsigned)((K / 16 + kQBlocksPerWave - 1) / kQBlocksPerWave), (unsigned)L.nchunks,
+            (unsigned)batch);
+  const bool score = chan_score != nullptr;
+#define NVQ_LAUNCH_Q(B, S)                                                                    \
+  hipLaunchKernelGGL((k_quantize<B, S>), grid, dim3(512), 0, s, x, rows, K, L.amax_partial, \
+                     L.n_partial, amax_in, codes, scales, tensor_scale, L.chunk_partial, L.status)
+  if (bf16) {
+    if (score) NVQ_LAUNCH_Q(true, true); else NVQ_LAUNCH_Q(true, false);
+  } else {
+    if (score) NVQ_LAUNCH_Q(false, true); else NVQ_LAUNCH_Q(false, false);
+  }
+#undef NVQ_LAUNCH_Q
+  if (int rc = last_launch()) return rc;
+  if (score) {
+    hipLaunchKernelGGL(k_score_reduce, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s,
+                       L.chunk_partial, L.nchunks, K, chan_score);
+    return last_launch();
+  }
+  return NVQ_OK;
+}
+
+extern "C" int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
+                                const float* tensor_scale, int64_t batch, int64_t rows, int64_t K,
+                                void* y, int y_dtype, void* stream) {
+  if (!codes || !scales || !tensor_scale || !y) return NVQ_EINVAL;
+  if (y_dtype != NVQ_F32 && y_dtype != NVQ_BF16) return NVQ_EINVAL;
+  if (batch <= 0 || rows < 0 || K <= 0 || (K & 15)) return NVQ_ESHAPE;
+  if (((uintptr_t)codes & 3u) || !aligned16(y)) return NVQ_EALIGN;
+  const int64_t n_words = batch * rows * K / 8;
+  if (n_words == 0) return NVQ_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dim3 grid((unsigned)((n_words + 255) / 256));
+  if (y_dtype == NVQ_BF16)
+    hipLaunchKernelGGL(k_dequant<true>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const uint32_t*>(codes), scales, tensor_scale, n_words,
+                       rows * K / 8, y);
+  else
+    hipLaunchKernelGGL(k_dequant<false>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const uint32_t*>(codes), scales, tensor_scale, n_words,
+                       rows * K / 8, y);
+  return last_launch();
+}
+
+extern "C" size_t residual_topk_workspace_bytes(int64_t rows, int64_t K, int32_t k) {
+  (void)k;
+  if (rows < 0 || K <= 0) return kAlign;
+  WsCarve c(nullptr);
+  c.take<float>((size_t)((rows + kQRows - 1) / kQRows) * K);
+  c.take<float>((size_t)K);
+  return c.off;
+}
+
+extern "C" int residual_topk_channels(const void* x, int x_dtype, int64_t rows, int64_t K,
+                                      const uint8_t* codes, const uint8_t* scales,
+                                      const float* tensor_scale, const float* scores_in,
+                                      float* scores_out, int32_t k, int32_t* idx_out,
+                                      uint16_t* resid_out, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  if (x_dtype != NVQ_F32 && x_dtype != NVQ_BF16) return NVQ_EINVAL;
+  if (rows < 0 || K <= 0 || (K & 15) || k < 0 || k > K) return NVQ_ESHAPE;
+  if (k > 0 && !idx_out) return NVQ_EINVAL;
+  if (!ws || !aligned256(ws)) return ws ? NVQ_EALIGN : NVQ_EINVAL;
+  const bool need_record = !scores_in || resid_out;
+  if (need_record && (!x || !codes || !scales || !tensor_scale)) return NVQ_EINVAL;
+  WsCarve c(ws);
+  const int64_t nchunks = (rows + kQRows - 1) / kQRows;
+  float* chunk_partial = c.take<float>((size_t)nchunks * K);
+  float* score_tmp = c.take<float>((size_t)K);
+  if (ws_bytes < c.off) return NVQ_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = x_dtype == NVQ_BF16;
+  const float* score = scores_in;
+  if (!score) {
+    float* dst = scores_out ? scores_out : score_tmp;
+    if (rows > 0) {
+      dim3 grid((unsigned)((K / 16 + kQBlocksPerWave - 1) / kQBlocksPerWave), (unsigned)nchunks);
+      if (bf16)
+        hipLaunchKernelGGL(k_resid_partials<true>, grid, dim3(512), 0, s, x, rows, K, codes, scales,
+                           tensor_scale, chunk_partial);
+      else
+        hipLaunchKernelGGL(k_resid_partials<false>, grid, dim3(512), 0, s, x, rows, K, codes,
+                           scales, tensor_scale, chunk_partial);
+      if (int rc = last_launch()) return rc;
+    }
+    hipLaunchKernelGGL(k_score_reduce, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s,
+                       chunk_partial, nchunks, K, dst);
+    if (int rc = last_launch()) return rc;
+    score = dst;
+  } else if (scores_out && scores_out != scores_in) {
+    if (int rc = hip_status(hipMemcpyAsync(scores_out, scores_in, K * sizeof(float),
+                                           hipMemcpyDeviceToDevice, s)))
+      return rc;
+  }
+  if (int rc = topk_launch(score, K, k, idx_out, s)) return rc;
+  if (resid_out && k > 0 && rows > 0) {
+    const int64_t n = rows * k;
+    dim3 grid((unsigned)((n + 255) / 256));
+    if (bf16)
+      hipLaunchKernelGGL(k_resid_gather<true>, grid, dim3(256), 0, s, x, rows, K, codes, scales,
+                         tensor_scale, idx_out, (int)k, resid_out);
+    else
+      hipLaunchKernelGGL(k_resid_gather<false>, grid, dim3(256), 0, s, x, rows, K, codes, scales,
+                         tensor_scale, idx_out, (int)k, resid_out);
+    return last_launch();
+  }
+  return NVQ_OK;
+}

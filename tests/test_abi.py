@@ -1,0 +1,87 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from qat_nvfp4_quantize_amd import nvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvq.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def _lib():
+    if not os.path.exists(nvq.LIB_PATH):
+        pytest.skip("libnvq.so not built")
+    return nvq.load()
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared_functions()
+    for n in ("nvfp4_quantize", "nvfp4_dequantize", "residual_topk_channels",
+              "moe_grouped_gemm_w4a4_comp", "qat_fakequant_gemm_w4a16"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    missing = [n for n in _declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    assert sorted(nvq.EXPORTED) == _declared_functions()
+
+
+def test_status_strings():
+    L = _lib()
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert L.nvq_status_string(code)
+
+
+def test_host_side_validation_launches_nothing():
+    L = _lib()
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: every call below fails validation first
+    # null x
+    assert L.nvfp4_quantize(None, 1, 1, 4, 32, None, fake, fake, fake, None, fake, 1 << 20, None) == -1
+    # K not a multiple of 16
+    assert L.nvfp4_quantize(fake, 1, 1, 4, 24, None, fake, fake, fake, None, fake, 1 << 20, None) == -2
+    # bad dtype
+    assert L.nvfp4_quantize(fake, 7, 1, 4, 32, None, fake, fake, fake, None, fake, 1 << 20, None) == -1
+    # misaligned x
+    assert L.nvfp4_quantize(P(0x1002), 1, 1, 4, 32, None, fake, fake, fake, None, fake, 1 << 20,
+                            None) == -3
+    # workspace too small
+    need = L.nvfp4_quantize_workspace_bytes(1, 4, 32)
+    assert need >= 256
+    assert L.nvfp4_quantize(fake, 1, 1, 4, 32, None, fake, fake, fake, None, fake, need - 1,
+                            None) == -4
+    # scores need batch == 1
+    assert L.nvfp4_quantize(fake, 1, 2, 4, 32, None, fake, fake, fake, fake, fake, 1 << 20,
+                            None) == -2
+    # k > K
+    assert L.residual_topk_channels(fake, 1, 4, 32, fake, fake, fake, None, None, 33, fake, None,
+                                    fake, 1 << 20, None) == -2
+    # route: topk > E, E too large
+    assert L.nvq_moe_route(fake, 4, 8, 9, fake, fake, None) == -2
+    assert L.nvq_moe_route(fake, 4, 2048, 8, fake, fake, None) == -2
+    assert L.nvq_moe_combine(fake, fake, fake, 4, 2, 12, fake, None) == -2
+    assert L.nvfp4_dequantize(fake, fake, fake, 1, 4, 24, fake, 0, None) == -2
+
+
+def test_gemm_args_validation():
+    L = _lib()
+    a = nvq.MoeGemmArgs()
+    a.struct_size = 8  # too small for this ABI
+    assert L.moe_grouped_gemm_w4a4_comp(ctypes.byref(a), None) in (-1, -6)
+    assert L.moe_grouped_gemm_w4a4_comp(None, None) in (-1, -6)
+    q = nvq.QatGemmArgs()
+    q.struct_size = 8
+    assert L.qat_fakequant_gemm_w4a16(ctypes.byref(q), None) in (-1, -6)

@@ -1,0 +1,80 @@
+"""GPU parity of the MoE glue: routing (bit-exact expert ids, softmax weights
+within fp32 rounding), the stable permutation (bit-exact) and the combine."""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import assert_bits_equal, log, to_gpu, to_np
+from qat_nvfp4_quantize_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _nvq():
+    from qat_nvfp4_quantize_amd import nvq
+
+    return nvq
+
+
+@pytest.mark.parametrize("shape", ["small", "decode", "prefill"])
+def test_route_and_permute(shape):
+    import torch
+
+    nvq = _nvq()
+    s = {"small": inputs.small_moe(), "decode": inputs.DECODE, "prefill": inputs.PREFILL}[shape]
+    log(f"[route] {shape} T={s.T} E={s.E} topk={s.topk}")
+    logits = inputs.logits(s)
+    ids, w = nvq.nvq_moe_route(to_gpu(logits), s.topk)
+    oids, ow = oracle.route(logits, s.topk)
+    assert_bits_equal(to_np(ids), oids, "ids")
+    np.testing.assert_allclose(to_np(w), ow, rtol=4e-7, atol=0)
+    sp, off, pos, ws = nvq.nvq_moe_permute(ids, s.E)
+    torch.cuda.synchronize()
+    osp, ooff, opos = oracle.permute(oids, s.E)
+    assert_bits_equal(to_np(off), ooff, "offsets")
+    assert_bits_equal(to_np(sp), osp, "sorted_pair")
+    assert_bits_equal(to_np(pos), opos, "pos")
+    assert nvq.device_status(ws) == 0
+
+
+def test_route_ties_and_negative_zero():
+    nvq = _nvq()
+    g = np.random.default_rng(3)
+    logits = np.round(g.standard_normal((300, 64))).astype(np.float32)
+    logits[:, 5] = -0.0
+    logits[:, 9] = 0.0
+    ids, w = nvq.nvq_moe_route(to_gpu(logits), 8)
+    oids, ow = oracle.route(logits, 8)
+    assert_bits_equal(to_np(ids), oids, "ids with ties")
+    np.testing.assert_allclose(to_np(w), ow, rtol=4e-7, atol=0)
+
+
+def test_permute_empty_experts_and_bad_ids():
+    nvq = _nvq()
+    g = np.random.default_rng(4)
+    T, topk, E = 777, 3, 40
+    ids = g.integers(0, 10, (T, topk)).astype(np.int32)  # experts 10..39 empty
+    sp, off, pos, ws = nvq.nvq_moe_permute(to_gpu(ids), E)
+    osp, ooff, opos = oracle.permute(ids, E)
+    assert_bits_equal(to_np(off), ooff, "offsets")
+    assert_bits_equal(to_np(sp), osp, "sorted_pair")
+    assert_bits_equal(to_np(pos), opos, "pos")
+    bad = ids.copy()
+    bad[5, 1] = E + 3
+    _, _, pos2, ws2 = nvq.nvq_moe_permute(to_gpu(bad), E)
+    assert nvq.device_status(ws2) & nvq.NVQ_STATUS_BAD_EXPERT
+    assert to_np(pos2)[5 * topk + 1] == -1
+
+
+def test_combine_matches_oracle():
+    nvq = _nvq()
+    s = inputs.small_moe()
+    logits = inputs.logits(s)
+    oids, ow = oracle.route(logits, s.topk)
+    _, _, opos = oracle.permute(oids, s.E)
+    g = np.random.default_rng(5)
+    y = inputs.to_bf16_bits(g.standard_normal((s.P, 64)).astype(np.float32))
+    out = nvq.nvq_moe_combine(to_gpu(y), to_gpu(opos), to_gpu(ow))
+    ref = oracle.combine_bf16(inputs.bf16_bits_to_f32(y), opos, ow)
+    got = inputs.bf16_bits_to_f32(to_np(out))
+    np.testing.assert_allclose(got, inputs.bf16_bits_to_f32(ref), rtol=2 ** -7, atol=1e-6)

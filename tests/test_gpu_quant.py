@@ -1,0 +1,154 @@
+"""GPU parity of the NVFP4 quantizer path (nvfp4_quantize, nvfp4_dequantize,
+residual_topk_channels) against the oracle: bit-exact codes, scales, tensor
+scales, residual scores, top-k indices and compensation residuals."""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import assert_bits_equal, log, to_gpu, to_np
+from qat_nvfp4_quantize_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _nvq():
+    from qat_nvfp4_quantize_amd import nvq
+
+    return nvq
+
+
+def _check_quant(x, k=None, amax_in=None, what=""):
+    """Quantize x (numpy f32 or bf16 bits) on the GPU and compare with the oracle."""
+    import torch
+
+    nvq = _nvq()
+    log(f"[quant] {what} shape={x.shape} dtype={x.dtype} k={k} amax_in={amax_in}")
+    xg = to_gpu(x)
+    amax_g = None if amax_in is None else torch.tensor([amax_in], dtype=torch.float32, device="cuda")
+    codes, scales, st, score, ws = nvq.nvfp4_quantize(xg, amax_in=amax_g, score=True)
+    torch.cuda.synchronize()
+    oc, os_, ost = oracle.quantize(x, amax_in=amax_in)
+    assert_bits_equal(to_np(st), np.array([ost], np.float32), what + " s_t")
+    assert_bits_equal(to_np(scales), os_, what + " scales")
+    assert_bits_equal(to_np(codes), oc, what + " codes")
+    osc = oracle.residual_scores(x, oc, os_, ost)
+    assert_bits_equal(to_np(score), osc, what + " scores")
+    assert nvq.device_status(ws) == 0
+    if k is not None:
+        idx, resid, sc2 = nvq.residual_topk_channels(xg, codes, scales, st, k, scores=score,
+                                                     want_scores=True)
+        oidx = oracle.topk(osc, k)
+        assert_bits_equal(to_np(idx), oidx, what + " topk")
+        assert_bits_equal(to_np(resid), oracle.residual_columns_bf16(x, oc, os_, ost, oidx),
+                          what + " resid")
+        # recomputing the score from the record gives the same bits
+        idx2, _, sc3 = nvq.residual_topk_channels(xg, codes, scales, st, k, want_scores=True,
+                                                  want_resid=False)
+        assert_bits_equal(to_np(sc3), osc, what + " scores (recomputed)")
+        assert_bits_equal(to_np(idx2), oidx, what + " topk (recomputed)")
+    return codes, scales, st
+
+
+def test_dense_check_workload_activation_and_weight():
+    x, w, k = inputs.dense_check()
+    _check_quant(x, k=k, what="dense X")
+    _check_quant(w, k=k, what="dense W^T")
+
+
+def test_quant_sweep_full_size_bit_exact():
+    x = inputs.quant_sweep()
+    _check_quant(x, k=64, what="sweep 8192x7168 bf16")
+
+
+@pytest.mark.parametrize("rows,K", [(1, 16), (15, 48), (17, 784), (300, 2064), (129, 1024)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_shapes(rows, K, dtype):
+    g = np.random.default_rng(rows * 7 + K)
+    x = (g.standard_t(3, (rows, K)) * np.exp(g.uniform(-4, 4, (rows, 1)))).astype(np.float32)
+    x[g.random((rows, K)) < 0.05] = 0.0
+    x[g.random((rows, K)) < 0.02] = -0.0
+    if dtype == "bf16":
+        x = inputs.to_bf16_bits(x)
+    _check_quant(x, k=min(5, K), what=f"ragged {rows}x{K} {dtype}")
+
+
+def test_golden_blocks_and_near_ties():
+    from test_oracle_quant import _golden_blocks, _near_tie_tensor
+
+    blocks = _golden_blocks()
+    x = np.array([v for b in blocks for v in b[1]], np.float32).reshape(1, -1)
+    codes, scales, st = _check_quant(x, what="golden")
+    for i, (name, vals, sc, packed, rsum) in enumerate(blocks):
+        assert to_np(scales)[0, i] == sc, name
+        assert bytes(to_np(codes)[0, 8 * i:8 * i + 8]) == packed, name
+    for seed in range(3):
+        _check_quant(_near_tie_tensor(seed), k=8, what=f"near-ties {seed}")
+    _check_quant(inputs.to_bf16_bits(_near_tie_tensor(9)), what="near-ties bf16")
+
+
+def test_extreme_tensor_scales_and_denormals():
+    g = np.random.default_rng(11)
+    base = g.standard_normal((64, 128)).astype(np.float32)
+    for scale in (1e-38, 1e-30, 1e-12, 1e12, 1e30, 1e37):
+        _check_quant((base * np.float32(scale)).astype(np.float32), what=f"scale {scale}")
+    den = (g.standard_normal((16, 64)) * 1e-40).astype(np.float32)  # fp32 subnormals
+    _check_quant(den, what="subnormal inputs")
+    den[0, 0] = 1.0
+    _check_quant(den, what="subnormal with a normal amax")
+
+
+def test_all_zero_and_negative_zero():
+    x = np.zeros((20, 32), np.float32)
+    x[3] = -0.0
+    _check_quant(x, k=4, what="zeros")
+
+
+def test_amax_override_saturates():
+    g = np.random.default_rng(12)
+    x = (g.standard_normal((40, 64)) * 10).astype(np.float32)
+    _check_quant(x, amax_in=float(np.abs(x).max()) / 7, what="amax_in small")
+    _check_quant(x, amax_in=float(np.abs(x).max()) * 3, what="amax_in large")
+
+
+def test_batched_weights_have_per_item_scales():
+    import torch
+
+    nvq = _nvq()
+    s = inputs.small_moe()
+    w = inputs.weights(s, "gu")  # [E, 2I, H] bf16 bits
+    codes, scales, st, _, ws = nvq.nvfp4_quantize(to_gpu(w))
+    torch.cuda.synchronize()
+    for e in range(s.E):
+        oc, os_, ost = oracle.quantize(w[e])
+        assert_bits_equal(to_np(st)[e:e + 1], np.array([ost], np.float32), f"w s_t {e}")
+        assert_bits_equal(to_np(scales)[e], os_, f"w scales {e}")
+        assert_bits_equal(to_np(codes)[e], oc, f"w codes {e}")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_dequantize_bit_exact(out):
+    import torch
+
+    nvq = _nvq()
+    x = inputs.to_bf16_bits((np.random.default_rng(13).standard_t(3, (96, 512)) * 3).astype(np.float32))
+    codes, scales, st, _, _ = nvq.nvfp4_quantize(to_gpu(x))
+    y = nvq.nvfp4_dequantize(codes, scales, st, torch.float32 if out == "f32" else torch.bfloat16)
+    oc, os_, ost = oracle.quantize(x)
+    assert_bits_equal(to_np(y), oracle.dequantize(oc, os_, ost, out=out), "dequant " + out)
+
+
+def test_nonfinite_input_sets_status():
+    nvq = _nvq()
+    x = np.ones((4, 32), np.float32)
+    x[2, 5] = np.inf
+    _, _, _, _, ws = nvq.nvfp4_quantize(to_gpu(x))
+    assert nvq.device_status(ws) & nvq.NVQ_STATUS_NONFINITE
+
+
+def test_repeat_runs_are_bitwise_identical():
+    nvq = _nvq()
+    x = to_gpu(inputs.quant_sweep(M=1024, K=2048))
+    a = [to_np(t) for t in nvq.nvfp4_quantize(x, score=True)[:4]]
+    b = [to_np(t) for t in nvq.nvfp4_quantize(x, score=True)[:4]]
+    for u, v in zip(a, b):
+        assert_bits_equal(u, v, "repeat")
