@@ -47,8 +47,8 @@ int amax_wg_per_item(int64_t batch, int64_t n_vec_per_item) {
 }
 
 // ---------------------------------------------------------------- pass 1 --
-// Per-wave partial max of |x| (as fp32 bits) over a strided slice of one batch
-// item; reduced with DPP, no LDS.  Non-finite values compare above all finite
+// Per-workgroup partial max of |x| (as fp32 bits) over a strided slice of one
+// batch item; each wave reduces with DPP, the four wave maxima meet in LDS.  Non-finite values compare above all finite
 // ones and are reported by pass 2.  Also clears the status word.
 template <bool kBF16>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4* __restrict__ x,
@@ -80,20 +80,217 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4* __restrict__
   for (; v < vec_per_item; v += stride) fold(xi[v]);
   if (kBF16) m <<= 16;
   m = wave_max_u32(m);
-  if ((threadIdx.x & 63) == 0)
-    partial[(int64_t)item * nwg * (kAmaxThreads / 64) + blockIdx.x * (kAmaxThreads / 64) +
-            (threadIdx.x >> 6)] = m;
+  __shared__ uint32_t s_wmax[kAmaxThreads / 64];
+  if ((threadIdx.x & 63) == 0) s_wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = s_wmax[0];
+#pragma unroll
+    for (int w = 1; w < kAmaxThreads / 64; ++w) r = max(r, s_wmax[w]);
+    partial[(int64_t)item * nwg + blockIdx.x] = r;
+  }
   if (status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;
 }
 
 __global__ void k_clear_status(uint32_t* status) { *status = 0; }
 
 // ---------------------------------------------------------------- pass 2 --
+// E4M3 code (0..0x7E) -> fp32.
+__device__ __forceinline__ float e4m3_value_f32(uint32_t sc) {
+  return (sc >= 8u) ? __uint_as_float((sc + 960u) << 20) : (float)sc * 0x1p-9f;
+}
+
+template <int kSel>
+__device__ __forceinline__ uint32_t cvt_fp4_pair(uint32_t w, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, kSel);
+}
+
+template <int kSel>
+__device__ __forceinline__ float2 fp4_pair_to_f32(uint32_t w) {
+  auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, kSel);
+  return make_float2(t[0], t[1]);
+}
+
+// Quantize one block held as 16 floats; returns the codes, writes *sc_out and
+// (kScore) adds |r| of each element to acc.
+// slot: this lane's 16-float LDS area, used only on the rare exact path so the
+// element loop there can index dynamically without a private-memory array.
+template <bool kScore, bool kFast>
+__device__ __forceinline__ uint2 quantize_block(const float (&xf)[16], float s_t, double six_st,
+                                                float g, float inv_st, uint32_t* sc_out,
+                                                float (&acc)[16], uint32_t& bad, float* slot) {
+  constexpr bool fast = kFast;
+  float am = __builtin_fmaxf(__builtin_fmaxf(fabsf(xf[0]), fabsf(xf[1])), fabsf(xf[2]));
+#pragma unroll
+  for (int j = 3; j < 15; j += 2) am = __builtin_fmaxf(__builtin_fmaxf(am, fabsf(xf[j])), fabsf(xf[j + 1]));
+  am = __builtin_fmaxf(am, fabsf(xf[15]));
+  if (!(am <= 3.40282347e38f)) bad = 1;
+  // Block scale: the E4M3 value nearest amax_b / (6 s_t).  E4M3 midpoints have
+  // 19 trailing zero mantissa bits; q is within 2 ulp of the real quotient.
+  uint32_t sc = 0;
+  if (s_t > 0.0f) {
+    const float q = am * g;
+    const uint32_t qb = __float_as_uint(q);
+    const bool near = !fast || (uint32_t)((qb << 13) + (8u << 13)) < (16u << 13);
+    sc = near ? e4m3_code_exact(am, six_st) : e4m3_rne_f32(q);
+  }
+  *sc_out = sc;
+  const float s_b = e4m3_value_f32(sc);
+  // Element codes: round y = x * h with h bracketed at (1 -+ 2^-20) / (s_b s_t);
+  // both brackets agree unless the real quotient sits within 2^-19 of an E2M1
+  // midpoint, in which case the block is decided in fp64.
+  const float h = (sc == 0 || !fast) ? 0.0f : __builtin_amdgcn_rcpf(s_b) * inv_st;
+  const float h_lo = h * 0.99999904632568359375f;   // 1 - 2^-20
+  const float h_hi = h * 1.00000095367431640625f;   // 1 + 2^-20
+  uint32_t lo0 = 0, lo1 = 0, hi0 = 0, hi1 = 0;
+  lo0 = cvt_fp4_pair<0>(lo0, xf[0] * h_lo, xf[1] * h_lo);
+  lo0 = cvt_fp4_pair<1>(lo0, xf[2] * h_lo, xf[3] * h_lo);
+  lo0 = cvt_fp4_pair<2>(lo0, xf[4] * h_lo, xf[5] * h_lo);
+  lo0 = cvt_fp4_pair<3>(lo0, xf[6] * h_lo, xf[7] * h_lo);
+  lo1 = cvt_fp4_pair<0>(lo1, xf[8] * h_lo, xf[9] * h_lo);
+  lo1 = cvt_fp4_pair<1>(lo1, xf[10] * h_lo, xf[11] * h_lo);
+  lo1 = cvt_fp4_pair<2>(lo1, xf[12] * h_lo, xf[13] * h_lo);
+  lo1 = cvt_fp4_pair<3>(lo1, xf[14] * h_lo, xf[15] * h_lo);
+  hi0 = cvt_fp4_pair<0>(hi0, xf[0] * h_hi, xf[1] * h_hi);
+  hi0 = cvt_fp4_pair<1>(hi0, xf[2] * h_hi, xf[3] * h_hi);
+  hi0 = cvt_fp4_pair<2>(hi0, xf[4] * h_hi, xf[5] * h_hi);
+  hi0 = cvt_fp4_pair<3>(hi0, xf[6] * h_hi, xf[7] * h_hi);
+  hi1 = cvt_fp4_pair<0>(hi1, xf[8] * h_hi, xf[9] * h_hi);
+  hi1 = cvt_fp4_pair<1>(hi1, xf[10] * h_hi, xf[11] * h_hi);
+  hi1 = cvt_fp4_pair<2>(hi1, xf[12] * h_hi, xf[13] * h_hi);
+  hi1 = cvt_fp4_pair<3>(hi1, xf[14] * h_hi, xf[15] * h_hi);
+  uint2 cw = make_uint2(lo0, lo1);
+  uint32_t d0 = lo0 ^ hi0, d1 = lo1 ^ hi1;  // nibbles where the brackets disagree
+  if (!fast) {
+    // Extreme tensor scale: decide every element in fp64, where S = s_b s_t
+    // (<= 28 bits) and every midpoint product is exact.
+#pragma unroll
+    for (int j = 0; j < 16; ++j) slot[j] = xf[j];
+    const double S = (double)s_b * (double)s_t;
+    uint32_t c0 = 0u, c1 = 0u;
+#pragma unroll 1
+    for (int j = 0; j < 16; ++j) {
+      const float v = slot[j];
+      const uint32_t idx = (sc == 0) ? 0u : e2m1_index_exact(fabsf(v), S);
+      const uint32_t nib = (idx | ((__float_as_uint(v) >> 28) & 8u)) << (4 * (j & 7));
+      c0 |= (j < 8) ? nib : 0u;
+      c1 |= (j < 8) ? 0u : nib;
+    }
+    cw = make_uint2(c0, c1);
+  } else if (d0 | d1) {
+    // The real quotient is within 2^-19 of the midpoint m between the lower
+    // bracket's index i and i + 1.  fma(-(m s_b), s_t, |x|) forms |x| - m s_b s_t
+    // exactly (m s_b <= 7 bits is exact in fp32) and rounds once, so its sign
+    // is exact and it is zero exactly on a tie, which goes to the even index.
+#pragma unroll
+    for (int j = 0; j < 16; ++j) slot[j] = xf[j];
+#pragma unroll 1
+    while (d0 | d1) {
+      const bool first = d0 != 0;
+      const uint32_t dm = first ? d0 : d1;
+      const uint32_t sh = __builtin_ctz(dm) & ~3u;  // nibble shift within the word
+      const int j = (first ? 0 : 8) + (int)(sh >> 2);
+      const uint32_t w = first ? cw.x : cw.y;
+      const uint32_t i = (w >> sh) & 7u;  // lower index (magnitude)
+      const float m = 0.5f * (e2m1_mag(i) + e2m1_mag(i + 1u));
+      const float d = __builtin_fmaf(-(m * s_b), s_t, fabsf(slot[j]));
+      const uint32_t up = (d > 0.0f || (d == 0.0f && ((i + 1u) & 1u) == 0u)) ? 1u : 0u;
+      const uint32_t nw = (w & ~(7u << sh)) | ((i + up) << sh);
+      if (first) {
+        cw.x = nw;
+        d0 &= ~(15u << sh);
+      } else {
+        cw.y = nw;
+        d1 &= ~(15u << sh);
+      }
+    }
+  }
+  if (kScore) {
+    // v = fl32(fl32(|G| s_b) s_t); |r| = | |x| - v | (= |fl32(x - v)|).
+    float2 g2[8];
+    g2[0] = fp4_pair_to_f32<0>(cw.x);
+    g2[1] = fp4_pair_to_f32<1>(cw.x);
+    g2[2] = fp4_pair_to_f32<2>(cw.x);
+    g2[3] = fp4_pair_to_f32<3>(cw.x);
+    g2[4] = fp4_pair_to_f32<0>(cw.y);
+    g2[5] = fp4_pair_to_f32<1>(cw.y);
+    g2[6] = fp4_pair_to_f32<2>(cw.y);
+    g2[7] = fp4_pair_to_f32<3>(cw.y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v0 = (fabsf(g2[j].x) * s_b) * s_t;
+      const float v1 = (fabsf(g2[j].y) * s_b) * s_t;
+      acc[2 * j] += fabsf(fabsf(xf[2 * j]) - v0);
+      acc[2 * j + 1] += fabsf(fabsf(xf[2 * j + 1]) - v1);
+    }
+  }
+  return cw;
+}
+
+template <bool kBF16>
+struct RowBlock {
+  uint4 q[kBF16 ? 2 : 4];
+  __device__ __forceinline__ void load(const void* xv, int64_t row, int64_t K, int64_t blk) {
+    const uint4* p = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(xv) + (row * K + blk * 16) * (kBF16 ? 2 : 4));
+#pragma unroll
+    for (int i = 0; i < (kBF16 ? 2 : 4); ++i) q[i] = p[i];
+  }
+  __device__ __forceinline__ void unpack(float (&xf)[16]) const {
+    if (kBF16) {
+      const uint32_t w[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xf[2 * j] = bf16_lo(w[j]);
+        xf[2 * j + 1] = bf16_hi(w[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xf[4 * j] = __uint_as_float(q[j].x);
+        xf[4 * j + 1] = __uint_as_float(q[j].y);
+        xf[4 * j + 2] = __uint_as_float(q[j].z);
+        xf[4 * j + 3] = __uint_as_float(q[j].w);
+      }
+    }
+  }
+};
+
+struct RowsResult {
+  float acc[16];
+  uint32_t bad;
+};
+
+// All rows of one lane decided in fp64 (tensor scale outside [2^-100, 2^100],
+// where the fp32 reciprocals would overflow).  Out of line: never on the hot path.
+template <bool kBF16, bool kScore>
+__device__ __attribute__((noinline)) RowsResult quantize_rows_exact(
+    const void* xv, int64_t row0, int nrows, int64_t K, int64_t blk, float s_t, double six_st,
+    uint8_t* codes, uint8_t* scales, float* slot) {
+  RowsResult res;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) res.acc[j] = 0.0f;
+  res.bad = 0;
+  const int64_t nblk = K >> 4;
+  for (int rr = 0; rr < nrows; ++rr) {
+    RowBlock<kBF16> rb;
+    rb.load(xv, row0 + rr, K, blk);
+    float xf[16];
+    rb.unpack(xf);
+    uint32_t sc;
+    const uint2 cw =
+        quantize_block<kScore, false>(xf, s_t, six_st, 0.0f, 0.0f, &sc, res.acc, res.bad, slot);
+    *reinterpret_cast<uint2*>(codes + (row0 + rr) * (K >> 1) + blk * 8) = cw;
+    scales[(row0 + rr) * nblk + blk] = (uint8_t)sc;
+  }
+  return res;
+}
+
 // Workgroup = 8 waves = one 128-row chunk x 1024 columns; wave w = the 16-row
 // sub-chunk w; lane l = one 16-element block column.  Each lane quantizes its
-// block in each of its 16 rows and keeps 16 per-column residual sums
-// (sequential in row order).  The chunk partial is the in-order sum of the 8
-// wave sums, via LDS.
+// block in each of its rows (next row prefetched) and keeps 16 per-column
+// residual sums, sequential in row order.  The chunk partial is the in-order
+// sum of the 8 wave sums, via LDS.
 template <bool kBF16, bool kScore>
 __global__ __launch_bounds__(512) void k_quantize(
     const void* __restrict__ xv, int64_t rows, int64_t K, const uint32_t* __restrict__ amax_partial,
@@ -101,20 +298,40 @@ __global__ __launch_bounds__(512) void k_quantize(
     uint8_t* __restrict__ scales, float* __restrict__ tensor_scale,
     float* __restrict__ chunk_partial, uint32_t* __restrict__ status) {
   __shared__ float s_part[kScore ? 8 * kQCols : 1];
+  __shared__ float s_slot[512 * 16];
   __shared__ float s_amax;
   const int item = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* slot = s_slot + threadIdx.x * 16;
 
-  if (wave == 0) {
+  const int64_t nblk = K >> 4;
+  const int64_t blk = (int64_t)blockIdx.x * kQBlocksPerWave + lane;
+  const int64_t r0 = (int64_t)blockIdx.y * kQRows + wave * kQSub;
+  const bool active = blk < nblk;
+  const int nrows = (int)max<int64_t>(0, min<int64_t>(kQSub, rows - r0));
+  const int64_t item_row0 = (int64_t)item * rows;
+  RowBlock<kBF16> cur;
+  if (active && nrows > 0) cur.load(xv, item_row0 + r0, K, blk);
+
+  {
+    // Tensor amax: every thread loads its share of the pass-1 partials at once.
+    __shared__ uint32_t s_wmax[8];
     uint32_t m = 0;
     if (amax_in) {
       m = __float_as_uint(amax_in[item]);
     } else {
       const uint32_t* p = amax_partial + (int64_t)item * n_partial;
-      for (int i = lane; i < n_partial; i += 64) m = max(m, p[i]);
+      for (int i = threadIdx.x; i < n_partial; i += 512) m = max(m, p[i]);
       m = wave_max_u32(m);
     }
-    if (lane == 0) s_amax = __uint_as_float(m);
+    if (lane == 0) s_wmax[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t r = s_wmax[0];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) r = max(r, s_wmax[w]);
+      s_amax = __uint_as_float(r);
+    }
   }
   __syncthreads();
   const float amax = s_amax;
@@ -128,121 +345,58 @@ __global__ __launch_bounds__(512) void k_quantize(
   const float g = fast ? (float)(1.0 / six_st) : 0.0f;
   const float inv_st = fast ? (float)(1.0 / (double)s_t) : 0.0f;
 
-  const int64_t nblk = K >> 4;
-  const int64_t blk = (int64_t)blockIdx.x * kQBlocksPerWave + lane;
-  const int64_t r0 = (int64_t)blockIdx.y * kQRows + wave * kQSub;
-  const bool active = blk < nblk;
   float acc[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
   uint32_t bad = 0;
 
-  if (active) {
-    const int64_t item_row0 = (int64_t)item * rows;
-    for (int rr = 0; rr < kQSub; ++rr) {
-      const int64_t r = r0 + rr;
-      if (r >= rows) break;
-      const int64_t row = item_row0 + r;
+  if (active && !fast) {
+    const RowsResult res = quantize_rows_exact<kBF16, kScore>(xv, item_row0 + r0, nrows, K, blk, s_t,
+                                                              six_st, codes, scales, slot);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = res.acc[j];
+    bad = res.bad;
+  } else if (active) {
+    auto process = [&](const RowBlock<kBF16>& rb, int64_t row) {
       float xf[16];
-      if (kBF16) {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + row * K + blk * 16);
-        const uint4 a = p[0], b = p[1];
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          xf[2 * j] = bf16_lo(w[j]);
-          xf[2 * j + 1] = bf16_hi(w[j]);
-        }
-      } else {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(xv) + row * K + blk * 16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 q = p[j];
-          xf[4 * j] = q.x;
-          xf[4 * j + 1] = q.y;
-          xf[4 * j + 2] = q.z;
-          xf[4 * j + 3] = q.w;
-        }
-      }
-      float am = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(xf[j]));
-      if (!(am <= 3.40282347e38f)) bad = 1;
-
-      // Block scale: the E4M3 value nearest amax_b / (6 s_t).
-      uint32_t sc = 0;
-      if (s_t > 0.0f) {
-        if (fast) {
-          const float q = am * g;
-          const uint32_t qb = __float_as_uint(q);
-          // E4M3 midpoints have 19 trailing zero mantissa bits; q is within
-          // 2 ulp of the real quotient.
-          const bool near = (uint32_t)((qb << 13) + (8u << 13)) < (16u << 13);
-          sc = near ? e4m3_code_exact(am, six_st) : e4m3_rne_f32(q);
-        } else {
-          sc = e4m3_code_exact(am, six_st);
-        }
-      }
-      const float s_b = e4m3_to_f32(sc);
-
-      // Element codes.
-      uint32_t cw[2] = {0u, 0u};
-      bool need_exact = !fast;
-      if (fast) {
-        const float h = (sc == 0) ? 0.0f : __builtin_amdgcn_rcpf(s_b) * inv_st;
-        uint32_t near_any = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float y0 = xf[2 * j] * h, y1 = xf[2 * j + 1] * h;
-          // E2M1 midpoints (0.25 .. 5) have 21 trailing zero mantissa bits;
-          // |y| is within 4 ulp of the real quotient.  Values below 0.140625
-          // are clamped away from the test (they round to 0 either way).
-          const uint32_t b0 = max(__float_as_uint(y0) & 0x7FFFFFFFu, 0x3E100000u);
-          const uint32_t b1 = max(__float_as_uint(y1) & 0x7FFFFFFFu, 0x3E100000u);
-          near_any |= (uint32_t)((b0 << 11) + (16u << 11) < (32u << 11));
-          near_any |= (uint32_t)((b1 << 11) + (16u << 11) < (32u << 11));
-          uint32_t& w = cw[j >> 2];
-          switch (j & 3) {
-            case 0: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y0, y1, 1.0f, 0); break;
-            case 1: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y0, y1, 1.0f, 1); break;
-            case 2: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y0, y1, 1.0f, 2); break;
-            default: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y0, y1, 1.0f, 3); break;
-          }
-        }
-        need_exact = near_any != 0;
-      }
-      if (need_exact) {
-        const double S = (double)s_b * (double)s_t;  // exact (<= 28 bits)
-        cw[0] = cw[1] = 0u;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const uint32_t idx = (sc == 0) ? 0u : e2m1_index_exact(fabsf(xf[j]), S);
-          const uint32_t nib = idx | ((__float_as_uint(xf[j]) >> 28) & 8u);
-          cw[j >> 3] |= nib << (4 * (j & 7));
-        }
-      }
-      *reinterpret_cast<uint2*>(codes + row * (K >> 1) + blk * 8) = make_uint2(cw[0], cw[1]);
+      rb.unpack(xf);
+      uint32_t sc;
+      const uint2 cw = quantize_block<kScore, true>(xf, s_t, six_st, g, inv_st, &sc, acc, bad, slot);
+      *reinterpret_cast<uint2*>(codes + row * (K >> 1) + blk * 8) = cw;
       scales[row * nblk + blk] = (uint8_t)sc;
-
-      if (kScore) {
-        // v = fl32(fl32(|G| s_b) s_t); |r| = | |x| - v | (= |fl32(x - v)|).
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t w = cw[j >> 2];
-          float2 gg;
-          switch (j & 3) {
-            case 0: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); gg = make_float2(t[0], t[1]); break; }
-            case 1: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); gg = make_float2(t[0], t[1]); break; }
-            case 2: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); gg = make_float2(t[0], t[1]); break; }
-            default: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); gg = make_float2(t[0], t[1]); break; }
-          }
-          const float v0 = (fabsf(gg.x) * s_b) * s_t;
-          const float v1 = (fabsf(gg.y) * s_b) * s_t;
-          const float d0 = fabsf(xf[2 * j]) - v0;
-          const float d1 = fabsf(xf[2 * j + 1]) - v1;
-          acc[2 * j] += fabsf(d0);
-          acc[2 * j + 1] += fabsf(d1);
-        }
+    };
+    const int64_t row0 = item_row0 + r0;
+    if (nrows == kQSub) {
+      // Four rotating row buffers: row rr + 4 is loaded into a buffer right
+      // after that buffer's row is processed.  Refill addresses are clamped to
+      // the last row instead of branching, so no load sits under a branch and
+      // the waits the compiler places stay exact.
+      RowBlock<kBF16> b0 = cur, b1, b2, b3;
+      b1.load(xv, row0 + 1, K, blk);
+      b2.load(xv, row0 + 2, K, blk);
+      b3.load(xv, row0 + 3, K, blk);
+      const int64_t last = row0 + kQSub - 1;
+#pragma unroll 1
+      for (int rr = 0; rr < kQSub; rr += 4) {
+        const int64_t row = row0 + rr;
+        process(b0, row);
+        b0.load(xv, min(row + 4, last), K, blk);
+        __builtin_amdgcn_sched_barrier(0);
+        process(b1, row + 1);
+        b1.load(xv, min(row + 5, last), K, blk);
+        __builtin_amdgcn_sched_barrier(0);
+        process(b2, row + 2);
+        b2.load(xv, min(row + 6, last), K, blk);
+        __builtin_amdgcn_sched_barrier(0);
+        process(b3, row + 3);
+        b3.load(xv, min(row + 7, last), K, blk);
+      }
+    } else {
+#pragma unroll 1
+      for (int rr = 0; rr < nrows; ++rr) {
+        RowBlock<kBF16> rb;
+        rb.load(xv, row0 + rr, K, blk);
+        process(rb, row0 + rr);
       }
     }
   }
@@ -264,14 +418,22 @@ __global__ __launch_bounds__(512) void k_quantize(
   if (wave_or_u32(bad) && lane == 0) atomicOr(status, (uint32_t)NVQ_STATUS_NONFINITE);
 }
 
-// score[c] = sum over chunks j ascending of P[j][c] (fp32, sequential).
+// score[c] = sum over chunks j ascending of P[j][c] (fp32, sequential).  The
+// partials of a group of 32 chunks are all loaded before the in-order sum.
 __global__ __launch_bounds__(256) void k_score_reduce(const float* __restrict__ partial,
                                                      int64_t nchunks, int64_t K,
                                                      float* __restrict__ score) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= K) return;
   float s = 0.0f;
-  for (int64_t j = 0; j < nchunks; ++j) s += partial[j * K + c];
+  for (int64_t j0 = 0; j0 < nchunks; j0 += 32) {
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = (j0 + j < nchunks) ? partial[(j0 + j) * K + c] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if (j0 + j < nchunks) s += v[j];
+  }
   score[c] = s;
 }
 
@@ -429,7 +591,7 @@ QuantLayout quant_layout(void* ws, int64_t batch, int64_t rows, int64_t K, int x
   const int64_t elem_bytes = (x_dtype == NVQ_BF16) ? 2 : 4;
   const int64_t vec_per_item = rows * K * elem_bytes / 16;
   L.nwg = amax_wg_per_item(batch, vec_per_item);
-  L.n_partial = L.nwg * (kAmaxThreads / 64);
+  L.n_partial = L.nwg;
   L.nchunks = (rows + kQRows - 1) / kQRows;
   WsCarve c(ws);
   L.amax_partial = c.take<uint32_t>((size_t)batch * L.n_partial);
