@@ -1,0 +1,199 @@
+"""GPU parity of moe_grouped_gemm_w4a4_comp against the oracle.
+
+Tolerance (GEMM outputs, fp32-accumulated): |Y_gpu - Y_oracle| /
+(||a_row||_2 * ||w_col||_2) <= 2e-3, with a_row the pre-quantization activation
+row and w_col the dequantized weight row.  Codes, scales, routing and the
+permutation feeding the GEMM are checked bit-exact on the way."""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import assert_bits_equal, log, to_gpu, to_np
+from qat_nvfp4_quantize_amd import inputs
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _nvq():
+    from qat_nvfp4_quantize_amd import nvq
+
+    return nvq
+
+
+def check_tol(got, ref, a_rows_f32, w_deq, what):
+    an = np.linalg.norm(a_rows_f32.astype(np.float64), axis=1)[:, None]
+    wn = np.linalg.norm(w_deq.astype(np.float64), axis=1)[None, :]
+    den = np.maximum(an * wn, 1e-30)
+    err = np.abs(got.astype(np.float64) - ref) / den
+    worst = float(err.max()) if err.size else 0.0
+    log(f"[gemm] {what}: max normalized err {worst:.3e} over {err.size} outputs")
+    assert worst <= TOL, (what, worst, np.unravel_index(np.argmax(err), err.shape))
+
+
+def _w_deq(codes, scales, st):
+    return oracle.dequantize(codes, scales, st).astype(np.float64)
+
+
+def test_dense_check_workload():
+    import torch
+
+    nvq = _nvq()
+    x, w, k = inputs.dense_check()
+    xg, wg = to_gpu(x), to_gpu(w)
+    qa = nvq.nvfp4_quantize(xg, score=True)
+    qw = nvq.nvfp4_quantize(wg[None])
+    idx, resid, _ = nvq.residual_topk_channels(xg, qa[0], qa[1], qa[2], k, scores=qa[3])
+    off = torch.tensor([0, x.shape[0]], dtype=torch.int32, device="cuda")
+    ob, of = nvq.moe_grouped_gemm_w4a4_comp(qa[0], qa[1], qa[2], qw[0], qw[1], qw[2], off,
+                                            rows=x.shape[0], a_resid=resid.contiguous(),
+                                            comp_idx=idx, want_f32=True)
+    torch.cuda.synchronize()
+    oqa, oqw = oracle.quantize(x), oracle.quantize(w)
+    oidx = oracle.topk(oracle.residual_scores(x, *oqa), k)
+    assert_bits_equal(to_np(idx), oidx, "comp idx")
+    ref = oracle.moe_gemm_w4a4(*oqa, x, oidx, *oqw, np.arange(64), np.zeros(64))
+    check_tol(to_np(of), ref, x, _w_deq(*oqw), "dense f32")
+    check_tol(inputs.bf16_bits_to_f32(to_np(ob)), ref, x, _w_deq(*oqw), "dense bf16")
+    # k = 0 reproduces the plain W4A4 product
+    ob0, of0 = nvq.moe_grouped_gemm_w4a4_comp(qa[0], qa[1], qa[2], qw[0], qw[1], qw[2], off,
+                                              rows=x.shape[0], want_f32=True)
+    ref0 = oracle.moe_gemm_w4a4(*oqa, x, None, *oqw, np.arange(64), np.zeros(64))
+    check_tol(to_np(of0), ref0, x, _w_deq(*oqw), "dense k=0")
+
+
+class MoeRun:
+    """Runs a MoE layer stage by stage on the GPU, keeping every intermediate."""
+
+    def __init__(self, s, experts_np=None):
+        import torch
+
+        nvq = _nvq()
+        self.s = s
+        self.logits = inputs.logits(s)
+        self.x = inputs.activations(s)
+        log(f"[moe] generating weights E={s.E} H={s.H} I={s.I}")
+        self.wgu = inputs.weights(s, "gu")
+        self.wdn = inputs.weights(s, "dn")
+        xg = to_gpu(self.x)
+        self.ids, self.w = nvq.nvq_moe_route(to_gpu(self.logits), s.topk)
+        self.sp, self.off, self.pos, _ = nvq.nvq_moe_permute(self.ids, s.E)
+        self.a_row = (self.sp // s.topk).contiguous()
+        self.qx = nvq.nvfp4_quantize(xg, score=True)
+        self.idx1, self.r1, _ = nvq.residual_topk_channels(xg, *self.qx[:3], s.k, scores=self.qx[3])
+        self.qgu = nvq.nvfp4_quantize(to_gpu(self.wgu))
+        self.qdn = nvq.nvfp4_quantize(to_gpu(self.wdn))
+        self.h, self.y1 = nvq.moe_grouped_gemm_w4a4_comp(
+            self.qx[0], self.qx[1], self.qx[2], self.qgu[0], self.qgu[1], self.qgu[2], self.off,
+            rows=s.P, a_row=self.a_row, a_resid=self.r1.contiguous(), comp_idx=self.idx1,
+            epilogue=nvq.NVQ_EPI_SWIGLU, want_f32=True)
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("shape", ["small", "small_ragged"])
+def test_small_moe_layer_stagewise(shape):
+    import torch
+
+    nvq = _nvq()
+    s = inputs.small_moe() if shape == "small" else inputs.small_moe(wid=101, T=77, E=5, topk=3, k=24)
+    run = MoeRun(s)
+    x = run.x
+    xf = inputs.bf16_bits_to_f32(x)
+    oids, ow = oracle.route(run.logits, s.topk)
+    assert_bits_equal(to_np(run.ids), oids, "ids")
+    osp, ooff, opos = oracle.permute(oids, s.E)
+    assert_bits_equal(to_np(run.sp), osp, "sorted pairs")
+    oqx = oracle.quantize(x)
+    oidx1 = oracle.topk(oracle.residual_scores(x, *oqx), s.k)
+    assert_bits_equal(to_np(run.idx1), oidx1, "S1")
+    wq = [oracle.quantize(run.wgu[e]) for e in range(s.E)]
+    wc = np.stack([q[0] for q in wq])
+    wsc = np.stack([q[1] for q in wq])
+    wst = np.array([q[2] for q in wq], np.float32)
+    assert_bits_equal(to_np(run.qgu[0]), wc, "W_gu codes")
+    row_tok = osp // s.topk
+    row_e = np.repeat(np.arange(s.E), np.diff(ooff)).astype(np.int32)
+    ref_y1 = oracle.moe_gemm_w4a4(*oqx, x, oidx1, wc, wsc, wst, row_tok, row_e)
+    wdeq = [_w_deq(wc[e], wsc[e], wst[e]) for e in range(s.E)]
+    y1 = to_np(run.y1)
+    for e in range(s.E):
+        rows = slice(ooff[e], ooff[e + 1])
+        if ooff[e + 1] > ooff[e]:
+            check_tol(y1[rows], ref_y1[rows], xf[row_tok[rows]], wdeq[e], f"gate/up e={e}")
+    # SwiGLU epilogue: h = bf16(silu(g) u) on the GPU's own fp32 pre-activation
+    h_ref = oracle.swiglu_bf16(y1.astype(np.float64))
+    h = to_np(run.h)
+    hf, hr = inputs.bf16_bits_to_f32(h), inputs.bf16_bits_to_f32(h_ref)
+    np.testing.assert_allclose(hf, hr, rtol=2 ** -7, atol=1e-6)
+    # down projection on the oracle's own H (independent input): qH bit-exact, GEMM in tolerance
+    H = oracle.swiglu_bf16(ref_y1)
+    Hg = to_gpu(H)
+    qh = nvq.nvfp4_quantize(Hg, score=True)
+    oqh = oracle.quantize(H)
+    assert_bits_equal(to_np(qh[0]), oqh[0], "qH codes")
+    idx2, r2, _ = nvq.residual_topk_channels(Hg, *qh[:3], s.k, scores=qh[3])
+    oidx2 = oracle.topk(oracle.residual_scores(H, *oqh), s.k)
+    assert_bits_equal(to_np(idx2), oidx2, "S2")
+    qdn = [oracle.quantize(run.wdn[e]) for e in range(s.E)]
+    dc = np.stack([q[0] for q in qdn])
+    dsc = np.stack([q[1] for q in qdn])
+    dst = np.array([q[2] for q in qdn], np.float32)
+    ob, of = nvq.moe_grouped_gemm_w4a4_comp(qh[0], qh[1], qh[2], run.qdn[0], run.qdn[1],
+                                            run.qdn[2], run.off, rows=s.P,
+                                            a_resid=r2.contiguous(), comp_idx=idx2, want_f32=True)
+    torch.cuda.synchronize()
+    ref_y2 = oracle.moe_gemm_w4a4(*oqh, H, oidx2, dc, dsc, dst, np.arange(s.P), row_e)
+    Hf = inputs.bf16_bits_to_f32(H)
+    y2 = to_np(of)
+    for e in range(s.E):
+        rows = slice(ooff[e], ooff[e + 1])
+        if ooff[e + 1] > ooff[e]:
+            check_tol(y2[rows], ref_y2[rows], Hf[rows], _w_deq(dc[e], dsc[e], dst[e]), f"down e={e}")
+    # combine, both sides on the GEMM's bf16 output: fp32 vs fp64 accumulation of
+    # topk terms, then one bf16 rounding -> at most one bf16 ulp apart
+    out = nvq.nvq_moe_combine(ob, run.pos, run.w)
+    y2b = inputs.bf16_bits_to_f32(to_np(ob))
+    ref_out = inputs.bf16_bits_to_f32(oracle.combine_bf16(y2b, opos, ow))
+    got = inputs.bf16_bits_to_f32(to_np(out))
+    mag = np.einsum("tj,tjn->tn", np.abs(ow), np.abs(y2b[opos.reshape(-1, s.topk)]))
+    bound = 2.0 ** -7 * np.maximum(np.abs(got), np.abs(ref_out)) + 2.0 ** -20 * mag + 1e-30
+    assert np.all(np.abs(got - ref_out) <= bound), float(np.max(np.abs(got - ref_out) / bound))
+
+
+def _sample_rows(off, every=97):
+    rows = set()
+    for e in range(len(off) - 1):
+        if off[e + 1] > off[e]:
+            rows.add(int(off[e]))
+            rows.add(int(off[e + 1] - 1))
+    rows.update(range(0, int(off[-1]), every))
+    return np.array(sorted(rows), np.int64)
+
+
+def test_decode_layer_gate_up_sampled():
+    """Full-size decode layer (T=4096, H=2048, E=128, I=768, top-8, k=64): gate/up
+    GEMM in the launch configuration of the benchmark, checked on sampled rows."""
+    s = inputs.DECODE
+    run = MoeRun(s)
+    x = run.x
+    oqx = oracle.quantize(x)
+    oidx1 = oracle.topk(oracle.residual_scores(x, *oqx), s.k)
+    assert_bits_equal(to_np(run.idx1), oidx1, "S1")
+    off = to_np(run.off)
+    sp = to_np(run.sp)
+    rows = _sample_rows(off, every=211)
+    row_e = np.searchsorted(off, rows, side="right") - 1
+    row_tok = sp[rows] // s.topk
+    experts = sorted(set(row_e.tolist()))
+    wq = {e: oracle.quantize(run.wgu[e]) for e in experts}
+    wc = np.stack([wq[e][0] for e in experts])
+    wsc = np.stack([wq[e][1] for e in experts])
+    wst = np.array([wq[e][2] for e in experts], np.float32)
+    local_e = np.array([experts.index(e) for e in row_e], np.int32)
+    log(f"[decode] oracle on {len(rows)} sampled rows x {2 * s.I} cols")
+    ref = oracle.moe_gemm_w4a4(*oqx, x, oidx1, wc, wsc, wst, row_tok, local_e)
+    y1 = to_np(run.y1)[rows]
+    xf = inputs.bf16_bits_to_f32(x)
+    for i, e in enumerate(experts):
+        sel = local_e == i
+        check_tol(y1[sel], ref[sel], xf[row_tok[sel]], _w_deq(wc[i], wsc[i], wst[i]), f"decode e={e}")
