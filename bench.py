@@ -132,6 +132,108 @@ class QuantLeg:
                           "exhaustive-search quantizer + residual scores (%.1f s)" % dt}
 
 
+class MoeLeg:
+    """One W4A4 MoE layer with residual compensation: route, permute, quantize X
+    (+ residual scores), top-k channels + residual columns, gate/up grouped GEMM
+    with SwiGLU epilogue, quantize H (+ scores), top-k + residuals, down grouped
+    GEMM, combine.  Expert weights are quantized once outside the timed step
+    (they are static during a rollout)."""
+
+    def __init__(self, shape):
+        import torch
+
+        from qat_nvfp4_quantize_amd import inputs, nvq
+
+        self.nvq = nvq
+        s = self.s = shape
+        self.name = "moe_%s" % ("decode" if s.wid == inputs.DECODE.wid else "prefill")
+        dev = torch.device("cuda")
+        log(f"[bench] {self.name}: generating inputs")
+        self.logits = torch.from_numpy(inputs.logits(s)).to(dev)
+        self.x = torch.from_numpy(inputs.activations(s).view(np.int16)).view(torch.bfloat16).to(dev)
+        self.qw = {}
+        for proj in ("gu", "dn"):
+            w = inputs.weights_device(s, proj, dev)
+            codes, scales, st, _, _ = nvq.nvfp4_quantize(w)
+            self.qw[proj] = (codes, scales, st)
+            del w
+        torch.cuda.synchronize()
+        P, H, I, k = s.P, s.H, s.I, s.k
+        u8, i32, f32, bf = torch.uint8, torch.int32, torch.float32, torch.bfloat16
+        self.ids = torch.empty(s.T, s.topk, dtype=i32, device=dev)
+        L = nvq.load()
+        self.ws_perm = nvq.workspace(L.nvq_moe_permute_workspace_bytes(s.T, s.topk, s.E), dev)
+        self.ws_q1 = nvq.workspace(L.nvfp4_quantize_workspace_bytes(1, s.T, H), dev)
+        self.ws_q2 = nvq.workspace(L.nvfp4_quantize_workspace_bytes(1, P, I), dev)
+        self.ws_t1 = nvq.workspace(L.residual_topk_workspace_bytes(s.T, H, k), dev)
+        self.ws_t2 = nvq.workspace(L.residual_topk_workspace_bytes(P, I, k), dev)
+        self.ws_g = nvq.workspace(max(L.moe_gemm_workspace_bytes(P, s.E, 2 * I, k),
+                                      L.moe_gemm_workspace_bytes(P, s.E, H, k)), dev)
+        self.qx = (torch.empty(s.T, H // 2, dtype=u8, device=dev), torch.empty(s.T, H // 16, dtype=u8, device=dev),
+                   torch.empty(1, dtype=f32, device=dev), torch.empty(H, dtype=f32, device=dev))
+        self.qh = (torch.empty(P, I // 2, dtype=u8, device=dev), torch.empty(P, I // 16, dtype=u8, device=dev),
+                   torch.empty(1, dtype=f32, device=dev), torch.empty(I, dtype=f32, device=dev))
+        self.h = torch.empty(P, I, dtype=bf, device=dev)
+        self.y2 = torch.empty(P, H, dtype=bf, device=dev)
+        self.flops_gu = 2.0 * P * H * 2 * I
+        self.flops_dn = 2.0 * P * I * H
+        self.flops_comp = 2.0 * P * k * 2 * I + 2.0 * P * k * H
+
+    def gemm(self, proj, a, rows, a_row, resid, idx, out, epi, comp=True):
+        nvq = self.nvq
+        codes, scales, st = self.qw[proj]
+        return nvq.moe_grouped_gemm_w4a4_comp(
+            a[0], a[1], a[2], codes, scales, st, self.off, rows=rows, a_row=a_row,
+            a_resid=resid if comp else None, comp_idx=idx if comp else None, epilogue=epi,
+            ws=self.ws_g, a_row_div=self.s.topk if a_row is not None else 0, out=out)
+
+    def step(self, timer_, comp=True):
+        nvq, s = self.nvq, self.s
+        tag = "" if comp else "_k0"
+        timer = lambda label, fn: timer_(self.name + "/" + label, fn)
+        r = timer("route", lambda: nvq.nvq_moe_route(self.logits, s.topk))
+        self.ids, self.w = r
+        self.sp, self.off, self.pos, _ = timer("permute", lambda: nvq.nvq_moe_permute(self.ids, s.E, ws=self.ws_perm))
+        timer("quant_x", lambda: nvq.nvfp4_quantize(self.x, score=True, ws=self.ws_q1, out=self.qx))
+        idx1, r1, _ = timer("topk_x", lambda: nvq.residual_topk_channels(
+            self.x, self.qx[0], self.qx[1], self.qx[2], s.k, scores=self.qx[3], ws=self.ws_t1))
+        timer("gemm_gu" + tag, lambda: self.gemm("gu", self.qx, s.P, self.sp, r1, idx1, (self.h, None),
+                                                  nvq.NVQ_EPI_SWIGLU, comp))
+        timer("quant_h", lambda: nvq.nvfp4_quantize(self.h, score=True, ws=self.ws_q2, out=self.qh))
+        idx2, r2, _ = timer("topk_h", lambda: nvq.residual_topk_channels(
+            self.h, self.qh[0], self.qh[1], self.qh[2], s.k, scores=self.qh[3], ws=self.ws_t2))
+        timer("gemm_dn" + tag, lambda: self.gemm("dn", self.qh, s.P, None, r2, idx2, (self.y2, None),
+                                                  nvq.NVQ_EPI_NONE, comp))
+        timer("combine", lambda: nvq.nvq_moe_combine(self.y2, self.pos, self.w))
+
+    def report(self, timer_):
+        class _T:
+            total = {k.split("/", 1)[1]: v for k, v in timer_.total.items() if k.startswith(self.name + "/")}
+
+            @staticmethod
+            def avg_ms(label):
+                return timer_.avg_ms(self.name + "/" + label)
+        timer = _T
+        gu, dn = timer.avg_ms("gemm_gu"), timer.avg_ms("gemm_dn")
+        layer = sum(timer.avg_ms(k) for k in ("route", "permute", "quant_x", "topk_x", "gemm_gu",
+                                                  "quant_h", "topk_h", "gemm_dn", "combine"))
+        tf = (self.flops_gu + self.flops_dn) / ((gu + dn) * 1e-3) / 1e12
+        out = {"layer_ms": round(layer, 4), "gemm_gu_ms": round(gu, 4), "gemm_dn_ms": round(dn, 4),
+               "gemm_tflops": round(tf, 1),
+               "gemm_gu_tflops": round(self.flops_gu / (gu * 1e-3) / 1e12, 1),
+               "gemm_dn_tflops": round(self.flops_dn / (dn * 1e-3) / 1e12, 1),
+               "gemm_frac_fp16_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+               "gemm_frac_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4),
+               "algorithmic_gflop": round((self.flops_gu + self.flops_dn) / 1e9, 1),
+               "comp_gflop": round(self.flops_comp / 1e9, 1),
+               "stages_ms": {k: round(timer.avg_ms(k), 4) for k in
+                             ("route", "permute", "quant_x", "topk_x", "quant_h", "topk_h", "combine")}}
+        if "gemm_gu_k0" in timer.total:
+            k0 = timer.avg_ms("gemm_gu_k0") + timer.avg_ms("gemm_dn_k0")
+            out["comp_overhead_vs_k0"] = round((gu + dn) / k0 - 1.0, 4)
+        return out
+
+
 class CopyLeg:
     """Plain elementwise copy of a known size: calibrates the FETCH_SIZE /
     WRITE_SIZE counters (and measures achievable HBM bandwidth)."""
@@ -169,6 +271,11 @@ def main():
         legs.append(QuantLeg())
     if "copy" in wanted:
         legs.append(CopyLeg())
+    from qat_nvfp4_quantize_amd import inputs as _inputs
+    if "moe" in wanted or "decode" in wanted:
+        legs.append(MoeLeg(_inputs.DECODE))
+    if "moe" in wanted or "prefill" in wanted:
+        legs.append(MoeLeg(_inputs.PREFILL))
     timer = EventTimer()
     for _ in range(args.warmup):
         for leg in legs:
@@ -184,6 +291,13 @@ def main():
     wall = time.perf_counter() - t0
     timer.collect()
     ms_step = wall * 1e3 / args.steps
+    # k = 0 reference runs of the MoE legs (outside the timed steps): the
+    # compensation overhead is the GEMM time at k > 0 over the time at k = 0
+    for leg in legs:
+        if leg.name.startswith("moe"):
+            for _ in range(2):
+                leg.step(timer, comp=False)
+    timer.collect()
 
     q = next(l for l in legs if l.name == "quant")
     q_ms = timer.avg_ms("quantize")
@@ -210,6 +324,17 @@ def main():
                      "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
     }
+    for leg in legs:
+        if leg.name.startswith("moe"):
+            result["legs"][leg.name] = leg.report(timer)
+    moe_main = [l for l in legs if l.name == "moe_prefill"] or [l for l in legs if l.name == "moe_decode"]
+    if moe_main:
+        r = result["legs"][moe_main[0].name]
+        result["roofline_gemm"] = {"kernel": "k_moe_gemm_deq16 (%s gate/up + down)" % moe_main[0].name,
+                                   "bound": "mfma", "achieved": r["gemm_tflops"],
+                                   "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": r["gemm_frac_fp16_mfma_peak"], "traffic": None,
+                                   "frac_of_fp4_peak": r["gemm_frac_fp4_peak"]}
     if any(l.name == "copy" for l in legs):
         c = next(l for l in legs if l.name == "copy")
         result["legs"]["copy"] = {"ms": round(timer.avg_ms("copy"), 5), "bytes": c.bytes,

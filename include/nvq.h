@@ -175,7 +175,7 @@ typedef struct nvq_moe_gemm_args {
   const float* a_tensor_scale;   /* [1] */
   const uint16_t* a_resid;       /* [a_rows, k] bf16 compensation operand (k > 0) */
   const int32_t* comp_idx;       /* [k] selected channels */
-  int32_t k;
+  int32_t k;                     /* multiple of 8; 0 disables the compensation */
   const uint8_t* w_codes;        /* [E, N, K/2] */
   const uint8_t* w_scales;       /* [E, N, K/16] */
   const float* w_tensor_scale;   /* [E] */
@@ -185,9 +185,12 @@ typedef struct nvq_moe_gemm_args {
   float* out_f32;                /* [rows, N] fp32 pre-epilogue; nullable */
   void* ws;
   size_t ws_bytes;
+  int32_t a_row_div;             /* > 0: A row of sorted row p is a_row[p] / a_row_div
+                                    (pass sorted pair ids with topk); 0: a_row[p] */
 } nvq_moe_gemm_args;
 
-size_t moe_gemm_workspace_bytes(int64_t rows, int64_t E);
+/* Workspace: tile table plus the packed compensation weights [E, N, k16] bf16. */
+size_t moe_gemm_workspace_bytes(int64_t rows, int64_t E, int64_t N, int32_t k);
 int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */

@@ -56,6 +56,7 @@ constexpr int KB = BK / 16;   // scale bytes per row per stage (8)
 struct GemmParams {
   int64_t rows, K, N, E, a_rows;
   const int32_t* a_row;
+  int a_row_div;
   const int32_t* off;
   const uint8_t* a_codes;
   const uint8_t* a_scales;
@@ -63,6 +64,8 @@ struct GemmParams {
   const uint16_t* a_resid;
   const int32_t* comp_idx;
   int k;
+  int kpad;                 // k rounded up to 16 (row stride of wcomp)
+  const uint16_t* wcomp;    // [E, N, kpad] bf16: dequantized weight at the selected channels
   const uint8_t* w_codes;
   const uint8_t* w_scales;
   const float* w_st;
@@ -98,6 +101,13 @@ __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__
       tiles[2 * (base + t) + 1] = off[e] + t * BM;
     }
   }
+}
+
+// Row of the A record (token) feeding sorted row pr.
+__device__ __forceinline__ int64_t a_source_row(const GemmParams& p, int64_t pr) {
+  if (!p.a_row) return pr;
+  const int64_t v = p.a_row[pr];
+  return p.a_row_div > 0 ? v / p.a_row_div : v;
 }
 
 // Weight row (column n of Y) held at local B row r of a workgroup.  With the
@@ -140,6 +150,22 @@ __device__ __forceinline__ uint32_t w_comp_bf16(const uint8_t* codes_row, const 
   return (__float_as_uint(v) >> 16) | ((nib & 8u) << 12);
 }
 
+// Packs the selected weight columns once per call: wcomp[e, n, j] = bf16 of
+// the exact dequantized weight G * s_b at channel idx[j] (0 for j >= k).  One
+// wave per weight row; the row's code bytes are fetched once and then hit L2.
+__global__ __launch_bounds__(256) void k_gather_wcomp(const uint8_t* __restrict__ w_codes,
+                                                     const uint8_t* __restrict__ w_scales,
+                                                     int64_t rows_total, int64_t K,
+                                                     const int32_t* __restrict__ idx, int k, int kpad,
+                                                     uint16_t* __restrict__ wcomp) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows_total) return;
+  const uint8_t* cr = w_codes + row * (K >> 1);
+  const uint8_t* sr = w_scales + row * (K >> 4);
+  for (int j = threadIdx.x & 63; j < kpad; j += 64)
+    wcomp[row * kpad + j] = (uint16_t)((j < k) ? w_comp_bf16(cr, sr, idx[j]) : 0u);
+}
+
 template <int kSwiglu>
 __global__ __launch_bounds__(NTHR) void k_moe_gemm_deq16(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][KQ][BM][16];
@@ -172,7 +198,7 @@ __global__ __launch_bounds__(NTHR) void k_moe_gemm_deq16(GemmParams p) {
     const int r = (t >> 2) + 32 * u;
     const int64_t pr = row0 + r;
     a_ok[u] = pr < row_end;
-    const int64_t ar = a_ok[u] ? (p.a_row ? (int64_t)p.a_row[pr] : pr) : 0;
+    const int64_t ar = a_ok[u] ? a_source_row(p, pr) : 0;
     a_src[u] = p.a_codes + ar * Kh + (t & 3) * 16;
   }
   const uint8_t* as_src;
@@ -180,7 +206,7 @@ __global__ __launch_bounds__(NTHR) void k_moe_gemm_deq16(GemmParams p) {
   {
     const int64_t pr = row0 + t;
     as_ok = pr < row_end;
-    const int64_t ar = as_ok ? (p.a_row ? (int64_t)p.a_row[pr] : pr) : 0;
+    const int64_t ar = as_ok ? a_source_row(p, pr) : 0;
     as_src = p.a_scales + ar * Kb;
   }
   const uint8_t* wcodes_e = p.w_codes + (int64_t)e * N * Kh;
@@ -307,50 +333,31 @@ __global__ __launch_bounds__(NTHR) void k_moe_gemm_deq16(GemmParams p) {
     for (int i = 0; i < 4; ++i) {
       const int64_t pr = row0 + 32 * i + l32;
       arow_ok[i] = pr < row_end;
-      arow_i[i] = arow_ok[i] ? (p.a_row ? (int64_t)p.a_row[pr] : pr) : 0;
+      arow_i[i] = arow_ok[i] ? a_source_row(p, pr) : 0;
     }
-    const uint8_t* wrow[4];
-    const uint8_t* wsrow[4];
+    const uint16_t* wrow[4];
     bool wok[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t n = b_row_to_n(128 * wave + 32 * j + l32, nt, kSwiglu, N);
       wok[j] = n < N;
-      wrow[j] = wcodes_e + (wok[j] ? n : 0) * Kh;
-      wsrow[j] = wscales_e + (wok[j] ? n : 0) * Kb;
+      wrow[j] = p.wcomp + ((int64_t)e * N + (wok[j] ? n : 0)) * p.kpad;
     }
     for (int st = 0; st < nsteps; ++st) {
-      const int c0 = 16 * st + 8 * h;  // this lane's 8 compensation channels
+      const int c0 = 16 * st + 8 * h;  // this lane's 8 compensation channels (k % 8 == 0)
       bf16x8_t af[4], bf[4];
+      const bool cin = c0 < p.k;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        uint32_t wv[4] = {0u, 0u, 0u, 0u};
-        if (arow_ok[i]) {
-          const uint16_t* src = p.a_resid + arow_i[i] * p.k;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c = c0 + 2 * q;
-            const uint32_t lo = (c < p.k) ? src[c] : 0u;
-            const uint32_t hi = (c + 1 < p.k) ? src[c + 1] : 0u;
-            wv[q] = lo | (hi << 16);
-          }
-        }
-        __builtin_memcpy(&af[i], wv, 16);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (arow_ok[i] && cin) v = *reinterpret_cast<const uint4*>(p.a_resid + arow_i[i] * p.k + c0);
+        __builtin_memcpy(&af[i], &v, 16);
       }
-      int ch[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) ch[q] = (c0 + q < p.k) ? p.comp_idx[c0 + q] : -1;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t wv[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = (ch[2 * q] >= 0 && wok[j]) ? w_comp_bf16(wrow[j], wsrow[j], ch[2 * q]) : 0u;
-          const uint32_t hi =
-              (ch[2 * q + 1] >= 0 && wok[j]) ? w_comp_bf16(wrow[j], wsrow[j], ch[2 * q + 1]) : 0u;
-          wv[q] = lo | (hi << 16);
-        }
-        __builtin_memcpy(&bf[j], wv, 16);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (wok[j]) v = *reinterpret_cast<const uint4*>(wrow[j] + c0);
+        __builtin_memcpy(&bf[j], &v, 16);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -405,17 +412,21 @@ __global__ __launch_bounds__(NTHR) void k_moe_gemm_deq16(GemmParams p) {
 
 struct MoeLayout {
   int max_tiles;
+  int kpad;
   int32_t* tiles;
   int32_t* ntiles;
+  uint16_t* wcomp;
   size_t bytes;
 };
 
-MoeLayout moe_layout(void* ws, int64_t rows, int64_t E) {
+MoeLayout moe_layout(void* ws, int64_t rows, int64_t E, int64_t N, int64_t k) {
   MoeLayout L;
   L.max_tiles = (int)((rows + BM - 1) / BM + E);
+  L.kpad = (int)((k + 15) / 16 * 16);
   WsCarve c(ws);
   L.tiles = c.take<int32_t>((size_t)L.max_tiles * 2);
   L.ntiles = c.take<int32_t>(1);
+  L.wcomp = c.take<uint16_t>((size_t)(E * N * L.kpad));
   L.bytes = c.off;
   return L;
 }
@@ -425,9 +436,9 @@ MoeLayout moe_layout(void* ws, int64_t rows, int64_t E) {
 
 using namespace nvq;
 
-extern "C" size_t moe_gemm_workspace_bytes(int64_t rows, int64_t E) {
-  if (rows < 0 || E < 1) return kAlign;
-  return moe_layout(nullptr, rows, E).bytes;
+extern "C" size_t moe_gemm_workspace_bytes(int64_t rows, int64_t E, int64_t N, int32_t k) {
+  if (rows < 0 || E < 1 || N < 1 || k < 0) return kAlign;
+  return moe_layout(nullptr, rows, E, N, k).bytes;
 }
 
 extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stream) {
@@ -443,13 +454,15 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   if (a->rows < 0 || a->E < 1 || a->E > 1024 || a->N <= 0 || a->K <= 0) return NVQ_ESHAPE;
   if (a->K % BK != 0) return NVQ_ESHAPE;  // the FP4 stage is 128 elements of K
   if (a->epilogue == NVQ_EPI_SWIGLU && (a->N % 2 != 0)) return NVQ_ESHAPE;
-  if (a->k < 0 || a->k > a->K) return NVQ_ESHAPE;
+  if (a->k < 0 || a->k > a->K || (a->k & 7)) return NVQ_ESHAPE;
   if (a->k > 0 && (!a->a_resid || !a->comp_idx)) return NVQ_EINVAL;
+  if (a->a_row_div < 0) return NVQ_EINVAL;
   if (((uintptr_t)a->a_codes & 15u) || ((uintptr_t)a->w_codes & 15u) ||
+      (a->k > 0 && ((uintptr_t)a->a_resid & 15u)) ||
       ((uintptr_t)a->a_scales & 7u) || ((uintptr_t)a->w_scales & 7u))
     return NVQ_EALIGN;
   if (!aligned256(a->ws)) return NVQ_EALIGN;
-  MoeLayout L = moe_layout(a->ws, a->rows, a->E);
+  MoeLayout L = moe_layout(a->ws, a->rows, a->E, a->N, a->k);
   if (a->ws_bytes < L.bytes) return NVQ_EWORKSPACE;
   if (a->rows == 0) return NVQ_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -458,9 +471,16 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   if (int rc = last_launch()) return rc;
   GemmParams p;
   p.rows = a->rows; p.K = a->K; p.N = a->N; p.E = a->E; p.a_rows = a->a_rows;
-  p.a_row = a->a_row; p.off = a->expert_offsets;
+  p.a_row = a->a_row; p.a_row_div = a->a_row_div; p.off = a->expert_offsets;
   p.a_codes = a->a_codes; p.a_scales = a->a_scales; p.a_st = a->a_tensor_scale;
   p.a_resid = a->a_resid; p.comp_idx = a->comp_idx; p.k = a->k;
+  p.kpad = L.kpad; p.wcomp = L.wcomp;
+  if (a->k > 0) {
+    const int64_t wrows = a->E * a->N;
+    hipLaunchKernelGGL(k_gather_wcomp, dim3((unsigned)((wrows + 3) / 4)), dim3(256), 0, s, a->w_codes,
+                       a->w_scales, wrows, a->K, a->comp_idx, (int)a->k, L.kpad, L.wcomp);
+    if (int rc = last_launch()) return rc;
+  }
   p.w_codes = a->w_codes; p.w_scales = a->w_scales; p.w_st = a->w_tensor_scale;
   p.out_bf16 = a->out_bf16; p.out_f32 = a->out_f32;
   p.tiles = L.tiles; p.ntiles = L.ntiles; p.max_tiles = L.max_tiles;

@@ -141,3 +141,25 @@ def grad_out(s: MoEShape, proj: str) -> np.ndarray:
 def small_moe(wid=100, T=96, H=256, E=8, I=128, topk=2, k=16) -> MoEShape:
     """A reduced MoE shape for fast parity tests (several tiles plus ragged tails)."""
     return MoEShape(wid=wid, T=T, H=H, E=E, I=I, topk=topk, k=k)
+
+
+def weights_device(s: MoEShape, proj: str, device="cuda"):
+    """bf16 [E, N, K] expert weights drawn on the GPU (torch Philox generator,
+    seeded per workload and tensor): same recipe as expert_weight_f32, another
+    random stream.  Used where the full-size weights are only timed, never
+    compared with the oracle."""
+    import torch
+
+    tid = _WGU if proj == "gu" else _WDN
+    N, K = (2 * s.I, s.H) if proj == "gu" else (s.H, s.I)
+    g = torch.Generator(device=device)
+    g.manual_seed(BASE_SEED * 1_000_003 + s.wid * 1009 + tid)
+    w = torch.empty(s.E, N, K, dtype=torch.bfloat16, device=device)
+    for e in range(s.E):
+        we = torch.randn(N, K, generator=g, device=device, dtype=torch.float32) * 0.02
+        if s.wid == PREFILL.wid:
+            n_out = max(1, int(round(0.01 * K)))
+            cols = torch.randperm(K, generator=g, device=device)[:n_out]
+            we[:, cols] *= 10.0
+        w[e] = we.to(torch.bfloat16)
+    return w

@@ -43,7 +43,7 @@ class MoeGemmArgs(ctypes.Structure):
         ("a_scales", _P), ("a_tensor_scale", _P), ("a_resid", _P), ("comp_idx", _P),
         ("k", _I32), ("w_codes", _P), ("w_scales", _P), ("w_tensor_scale", _P),
         ("epilogue", _I32), ("path", _I32), ("out_bf16", _P), ("out_f32", _P),
-        ("ws", _P), ("ws_bytes", _SZ),
+        ("ws", _P), ("ws_bytes", _SZ), ("a_row_div", _I32),
     ]
 
 
@@ -71,7 +71,7 @@ _SIGS = [
     ("nvq_moe_permute_workspace_bytes", _SZ, [_I64, _I64, _I64]),
     ("nvq_moe_permute", ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     ("nvq_moe_combine", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
-    ("moe_gemm_workspace_bytes", _SZ, [_I64, _I64]),
+    ("moe_gemm_workspace_bytes", _SZ, [_I64, _I64, _I64, _I32]),
     ("moe_grouped_gemm_w4a4_comp", ctypes.c_int, [ctypes.POINTER(MoeGemmArgs), _P]),
     ("qat_gemm_workspace_bytes", _SZ, [_I64, _I64]),
     ("qat_fakequant_gemm_w4a16", ctypes.c_int, [ctypes.POINTER(QatGemmArgs), _P]),
@@ -241,7 +241,7 @@ def nvq_moe_combine(y, pos, weights):
 def moe_grouped_gemm_w4a4_comp(a_codes, a_scales, a_tensor_scale, w_codes, w_scales,
                                w_tensor_scale, expert_offsets, rows, a_row=None, a_resid=None,
                                comp_idx=None, epilogue=NVQ_EPI_NONE, path=NVQ_GEMM_AUTO,
-                               want_bf16=True, want_f32=False, ws=None):
+                               want_bf16=True, want_f32=False, ws=None, a_row_div=0, out=None):
     """Returns (out_bf16 or None, out_f32 or None)."""
     L = load()
     E, N, Kh = w_codes.shape
@@ -249,10 +249,13 @@ def moe_grouped_gemm_w4a4_comp(a_codes, a_scales, a_tensor_scale, w_codes, w_sca
     dev = w_codes.device
     k = 0 if comp_idx is None else int(comp_idx.numel())
     n_out = N // 2 if epilogue == NVQ_EPI_SWIGLU else N
-    ob = torch.empty(rows, n_out, dtype=torch.bfloat16, device=dev) if want_bf16 else None
-    of = torch.empty(rows, N, dtype=torch.float32, device=dev) if want_f32 else None
+    if out is not None:
+        ob, of = out
+    else:
+        ob = torch.empty(rows, n_out, dtype=torch.bfloat16, device=dev) if want_bf16 else None
+        of = torch.empty(rows, N, dtype=torch.float32, device=dev) if want_f32 else None
     if ws is None:
-        ws = workspace(L.moe_gemm_workspace_bytes(rows, E), dev)
+        ws = workspace(L.moe_gemm_workspace_bytes(rows, E, N, k), dev)
     a = MoeGemmArgs()
     a.struct_size = ctypes.sizeof(MoeGemmArgs)
     a.rows, a.K, a.N, a.E = rows, K, N, E
@@ -267,6 +270,7 @@ def moe_grouped_gemm_w4a4_comp(a_codes, a_scales, a_tensor_scale, w_codes, w_sca
     a.epilogue, a.path = epilogue, path
     a.out_bf16, a.out_f32 = _ptr(ob), _ptr(of)
     a.ws, a.ws_bytes = _ptr(ws), ws.numel()
+    a.a_row_div = int(a_row_div)
     _check("moe_grouped_gemm_w4a4_comp", L.moe_grouped_gemm_w4a4_comp(ctypes.byref(a), _stream()))
     return ob, of
 
