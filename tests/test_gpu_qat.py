@@ -1,0 +1,181 @@
+"""GPU parity of qat_fakequant_gemm_w4a16 (forward, input gradient, weight
+gradient) against the oracle.  Tolerance as for the W4A4 GEMM:
+|err| / (||a||_2 * ||b||_2) <= 2e-3 with a, b the two contracted vectors."""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import assert_bits_equal, log, to_gpu, to_np
+from qat_nvfp4_quantize_amd import inputs
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _nvq():
+    from qat_nvfp4_quantize_amd import nvq
+
+    return nvq
+
+
+def _norm_err(got, ref, an, bn, what):
+    den = np.maximum(np.outer(an, bn), 1e-30)
+    err = np.abs(got.astype(np.float64) - ref) / den
+    worst = float(err.max()) if err.size else 0.0
+    log(f"[qat] {what}: max normalized err {worst:.3e} over {err.size} outputs")
+    assert worst <= TOL, (what, worst)
+
+
+def _setup(s, proj):
+    """Routing, permutation, x, dy and the quantized weight cache for one projection."""
+    import torch
+
+    nvq = _nvq()
+    logits = inputs.logits(s)
+    ids, w = nvq.nvq_moe_route(to_gpu(logits), s.topk)
+    sp, off, pos, _ = nvq.nvq_moe_permute(ids, s.E)
+    a_row = (sp // s.topk).to(torch.int32).contiguous()
+    K, N = (s.H, 2 * s.I) if proj == "gu" else (s.I, s.H)
+    g = np.random.default_rng(1234 + s.wid)
+    x = inputs.to_bf16_bits(g.standard_normal((s.T if proj == "gu" else s.P, K)).astype(np.float32))
+    dy = inputs.to_bf16_bits(g.standard_normal((s.P, N)).astype(np.float32))
+    wm = inputs.weights(s, proj)  # bf16 master weights [E, N, K]
+    q = nvq.nvfp4_quantize(to_gpu(wm))  # the rollout's cached record
+    torch.cuda.synchronize()
+    return dict(ids=ids, sp=sp, off=off, a_row=a_row, x=x, dy=dy, wm=wm, q=q, K=K, N=N,
+                row_tok=to_np(sp) // s.topk, offn=to_np(off))
+
+
+@pytest.mark.parametrize("proj", ["gu", "dn"])
+def test_small_qat_all_modes(proj):
+    import torch
+
+    nvq = _nvq()
+    s = inputs.small_moe(wid=102, T=120, H=256, E=6, I=128, topk=2)
+    d = _setup(s, proj)
+    K, N = d["K"], d["N"]
+    wq = [oracle.quantize(d["wm"][e]) for e in range(s.E)]
+    wc = np.stack([q[0] for q in wq])
+    wsc = np.stack([q[1] for q in wq])
+    wst = np.array([q[2] for q in wq], np.float32)
+    assert_bits_equal(to_np(d["q"][0]), wc, "weight cache codes")
+    off = d["offn"]
+    row_e = np.repeat(np.arange(s.E), np.diff(off)).astype(np.int32)
+    # forward rows: gate/up gathers token rows, down reads sorted rows directly
+    x_row = d["row_tok"] if proj == "gu" else np.arange(s.P)
+    a_row = d["a_row"] if proj == "gu" else None
+    xg, dyg = to_gpu(d["x"]), to_gpu(d["dy"])
+    yb, yf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_FWD, *d["q"][:3], d["off"], s.P, x=xg,
+                                         a_row=a_row, want_f32=True)
+    dxb, dxf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *d["q"][:3], d["off"], s.P, dy=dyg,
+                                           want_f32=True)
+    dw = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *d["q"][:3], d["off"], s.P, x=xg, dy=dyg,
+                                      a_row=a_row)
+    torch.cuda.synchronize()
+    X = inputs.bf16_bits_to_f32(d["x"]).astype(np.float64)
+    DY = inputs.bf16_bits_to_f32(d["dy"]).astype(np.float64)
+    ref_y = oracle.qat_fwd(d["x"], x_row, row_e, wc, wsc, wst)
+    ref_dx = oracle.qat_dgrad(d["dy"], np.arange(s.P), row_e, wc, wsc, wst)
+    y, dx, dwn = to_np(yf), to_np(dxf), to_np(dw)
+    for e in range(s.E):
+        rows = slice(off[e], off[e + 1])
+        if off[e + 1] == off[e]:
+            continue
+        W = oracle.dequantize(wc[e], wsc[e], wst[e]).astype(np.float64)
+        _norm_err(y[rows], ref_y[rows], np.linalg.norm(X[x_row[rows]], axis=1),
+                  np.linalg.norm(W, axis=1), f"{proj} fwd e={e}")
+        _norm_err(dx[rows], ref_dx[rows], np.linalg.norm(DY[rows], axis=1),
+                  np.linalg.norm(W, axis=0), f"{proj} dgrad e={e}")
+        nn, cc = np.meshgrid(np.arange(N), np.arange(K), indexing="ij")
+        ref_w = oracle.qat_wgrad(d["dy"], d["x"], x_row, off[e], off[e + 1], nn.ravel(), cc.ravel())
+        _norm_err(dwn[e], ref_w.reshape(N, K), np.linalg.norm(DY[rows], axis=0),
+                  np.linalg.norm(X[x_row[rows]], axis=0), f"{proj} wgrad e={e}")
+    # bf16 outputs are the rounded fp32 outputs
+    np.testing.assert_array_equal(to_np(yb), inputs.to_bf16_bits(y))
+    np.testing.assert_array_equal(to_np(dxb), inputs.to_bf16_bits(dx))
+    # accumulate: dw += dW
+    dw2 = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *d["q"][:3], d["off"], s.P, x=xg, dy=dyg,
+                                       a_row=a_row, dw=dw.clone(), accumulate=True)
+    np.testing.assert_allclose(to_np(dw2), 2 * dwn, rtol=1e-6, atol=1e-6)
+
+
+def test_forward_uses_the_cached_rounding():
+    """The forward's weight equals the rollout's dequantized record (QUADS §2.1:
+    same quantize-dequantize path): FWD on the cache == dense GEMM on
+    nvfp4_dequantize(cache), up to fp32 summation order."""
+    import torch
+
+    nvq = _nvq()
+    s = inputs.small_moe(wid=103, T=64, H=256, E=1, I=128, topk=1)
+    d = _setup(s, "gu")
+    wdq = nvq.nvfp4_dequantize(*d["q"][:3], out_dtype=torch.float32)  # [1, N, K]
+    xg = to_gpu(d["x"])
+    _, yf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_FWD, *d["q"][:3], d["off"], s.P, x=xg,
+                                        a_row=d["a_row"], want_f32=True)
+    ref = xg.float()[d["a_row"].long()] @ wdq[0].T
+    torch.cuda.synchronize()
+    X = inputs.bf16_bits_to_f32(d["x"]).astype(np.float64)[d["row_tok"]]
+    W = to_np(wdq[0]).astype(np.float64)
+    _norm_err(to_np(yf), to_np(ref).astype(np.float64), np.linalg.norm(X, axis=1),
+              np.linalg.norm(W, axis=1), "fwd vs dense on dequantized cache")
+
+
+def test_qat_layer_full_size_sampled():
+    """Trainer QAT layer at full size (T=16384, H=4096, E=128, I=1536, top-8):
+    gate/up forward, input and weight gradients on sampled outputs."""
+    import torch
+
+    nvq = _nvq()
+    s = inputs.QAT
+    log("[qat] full size: generating on device")
+    logits = inputs.logits(s)
+    ids, _ = nvq.nvq_moe_route(to_gpu(logits), s.topk)
+    sp, off, _, _ = nvq.nvq_moe_permute(ids, s.E)
+    a_row = (sp // s.topk).to(torch.int32).contiguous()
+    K, N = s.H, 2 * s.I
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    x = torch.randn(s.T, K, generator=gen, device="cuda").to(torch.bfloat16)
+    dy = torch.randn(s.P, N, generator=gen, device="cuda").to(torch.bfloat16)
+    wm = inputs.weights_device(s, "gu")
+    q = nvq.nvfp4_quantize(wm)
+    yb, yf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_FWD, *q[:3], off, s.P, x=x, a_row=a_row,
+                                         want_f32=True)
+    dxb, dxf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *q[:3], off, s.P, dy=dy, want_f32=True)
+    dw = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *q[:3], off, s.P, x=x, dy=dy, a_row=a_row)
+    torch.cuda.synchronize()
+    offn = to_np(off)
+    row_tok = to_np(sp) // s.topk
+    xn = to_np(x)
+    for e in (0, 37, 127):
+        rows = np.arange(offn[e], offn[e + 1])
+        if rows.size == 0:
+            continue
+        samp = rows[:: max(1, rows.size // 24)]
+        wmb = to_np(wm[e])
+        oq = oracle.quantize(wmb)
+        assert_bits_equal(to_np(q[0][e]), oq[0], f"cache codes e={e}")
+        W = oracle.dequantize(*oq).astype(np.float64)
+        cols = np.arange(0, N, 97)
+        ref = oracle.qat_fwd(xn, row_tok[samp], np.zeros(samp.size, np.int32), oq[0], oq[1],
+                             np.float32(oq[2]), cols=cols)
+        X = inputs.bf16_bits_to_f32(xn).astype(np.float64)
+        _norm_err(to_np(yf)[samp][:, cols], ref, np.linalg.norm(X[row_tok[samp]], axis=1),
+                  np.linalg.norm(W[cols], axis=1), f"full fwd e={e}")
+        dyn = to_np(dy[samp])
+        cc = np.arange(0, K, 101)
+        refd = oracle.qat_dgrad(dyn, np.arange(samp.size), np.zeros(samp.size, np.int32), oq[0],
+                                oq[1], np.float32(oq[2]), cols=cc)
+        DY = inputs.bf16_bits_to_f32(dyn).astype(np.float64)
+        _norm_err(to_np(dxf)[samp][:, cc], refd, np.linalg.norm(DY, axis=1),
+                  np.linalg.norm(W[:, cc], axis=0), f"full dgrad e={e}")
+        ns = np.arange(0, N, 211)
+        cs = np.arange(0, K, 223)
+        nn, ccw = np.meshgrid(ns, cs, indexing="ij")
+        dye = to_np(dy[offn[e]:offn[e + 1]])
+        refw = oracle.qat_wgrad(dye, xn, row_tok[rows], 0, rows.size, nn.ravel(), ccw.ravel())
+        DYe = inputs.bf16_bits_to_f32(dye).astype(np.float64)
+        Xe = X[row_tok[rows]]
+        _norm_err(to_np(dw[e])[np.ix_(ns, cs)], refw.reshape(ns.size, cs.size),
+                  np.linalg.norm(DYe[:, ns], axis=0), np.linalg.norm(Xe[:, cs], axis=0),
+                  f"full wgrad e={e}")
