@@ -234,6 +234,84 @@ class MoeLeg:
         return out
 
 
+class QatLeg:
+    """Trainer-side asymmetric W4A16 QAT layer on the cached NVFP4 weight
+    record: forward, input gradient and weight gradient of the gate/up and
+    down projections (upstream gradients and the down projection's input are
+    seeded independently; the SwiGLU backward is not on this path)."""
+
+    name = "qat"
+
+    def __init__(self):
+        import torch
+
+        from qat_nvfp4_quantize_amd import inputs, nvq
+
+        self.nvq = nvq
+        s = self.s = inputs.QAT
+        dev = torch.device("cuda")
+        log("[bench] qat: generating inputs")
+        ids, _ = nvq.nvq_moe_route(torch.from_numpy(inputs.logits(s)).to(dev), s.topk)
+        self.sp, self.off, _, _ = nvq.nvq_moe_permute(ids, s.E)
+        self.a_row = (self.sp // s.topk).to(torch.int32).contiguous()
+        g = torch.Generator(device=dev)
+        g.manual_seed(5)
+        bf = torch.bfloat16
+        self.x = torch.randn(s.T, s.H, generator=g, device=dev).to(bf)
+        self.hin = torch.randn(s.P, s.I, generator=g, device=dev).to(bf)
+        self.dy_gu = torch.randn(s.P, 2 * s.I, generator=g, device=dev).to(bf)
+        self.dy_dn = torch.randn(s.P, s.H, generator=g, device=dev).to(bf)
+        self.q = {}
+        for proj in ("gu", "dn"):
+            w = inputs.weights_device(s, proj, dev)
+            self.q[proj] = nvq.nvfp4_quantize(w)[:3]
+            del w
+        P = s.P
+        self.y_gu = torch.empty(P, 2 * s.I, dtype=bf, device=dev)
+        self.y_dn = torch.empty(P, s.H, dtype=bf, device=dev)
+        self.dx = torch.empty(P, s.H, dtype=bf, device=dev)
+        self.dh = torch.empty(P, s.I, dtype=bf, device=dev)
+        self.dw_gu = torch.empty(s.E, 2 * s.I, s.H, dtype=torch.float32, device=dev)
+        self.dw_dn = torch.empty(s.E, s.H, s.I, dtype=torch.float32, device=dev)
+        L = nvq.load()
+        self.ws = nvq.workspace(L.qat_gemm_workspace_bytes(P, s.E), dev)
+        f_gu = 2.0 * P * s.H * 2 * s.I
+        f_dn = 2.0 * P * s.I * s.H
+        self.flops = {"fwd_gu": f_gu, "dgrad_gu": f_gu, "wgrad_gu": f_gu,
+                      "fwd_dn": f_dn, "dgrad_dn": f_dn, "wgrad_dn": f_dn}
+
+    def step(self, timer_):
+        nvq, s = self.nvq, self.s
+        timer = lambda label, fn: timer_("qat/" + label, fn)
+        F, D, W = nvq.NVQ_QAT_FWD, nvq.NVQ_QAT_DGRAD, nvq.NVQ_QAT_WGRAD
+        qg, qd = self.q["gu"], self.q["dn"]
+        call = nvq.qat_fakequant_gemm_w4a16
+        timer("fwd_gu", lambda: call(F, *qg, self.off, s.P, x=self.x, a_row=self.a_row, ws=self.ws,
+                                     out=(self.y_gu, None)))
+        timer("fwd_dn", lambda: call(F, *qd, self.off, s.P, x=self.hin, ws=self.ws, out=(self.y_dn, None)))
+        timer("dgrad_dn", lambda: call(D, *qd, self.off, s.P, dy=self.dy_dn, ws=self.ws, out=(self.dh, None)))
+        timer("wgrad_dn", lambda: call(W, *qd, self.off, s.P, x=self.hin, dy=self.dy_dn, dw=self.dw_dn,
+                                       ws=self.ws))
+        timer("dgrad_gu", lambda: call(D, *qg, self.off, s.P, dy=self.dy_gu, ws=self.ws, out=(self.dx, None)))
+        timer("wgrad_gu", lambda: call(W, *qg, self.off, s.P, x=self.x, dy=self.dy_gu, a_row=self.a_row,
+                                       dw=self.dw_gu, ws=self.ws))
+
+    def report(self, timer):
+        out = {}
+        tot_ms, tot_f = 0.0, 0.0
+        for k, f in self.flops.items():
+            ms = timer.avg_ms("qat/" + k)
+            out[k + "_ms"] = round(ms, 4)
+            out[k + "_tflops"] = round(f / (ms * 1e-3) / 1e12, 1)
+            tot_ms += ms
+            tot_f += f
+        out["total_ms"] = round(tot_ms, 4)
+        out["tflops"] = round(tot_f / (tot_ms * 1e-3) / 1e12, 1)
+        out["frac_bf16_mfma_peak"] = round(out["tflops"] / BF16_PEAK_TFLOPS, 4)
+        out["algorithmic_tflop"] = round(tot_f / 1e12, 3)
+        return out
+
+
 class CopyLeg:
     """Plain elementwise copy of a known size: calibrates the FETCH_SIZE /
     WRITE_SIZE counters (and measures achievable HBM bandwidth)."""
@@ -276,6 +354,8 @@ def main():
         legs.append(MoeLeg(_inputs.DECODE))
     if "moe" in wanted or "prefill" in wanted:
         legs.append(MoeLeg(_inputs.PREFILL))
+    if "qat" in wanted:
+        legs.append(QatLeg())
     timer = EventTimer()
     for _ in range(args.warmup):
         for leg in legs:
@@ -325,7 +405,7 @@ def main():
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
     }
     for leg in legs:
-        if leg.name.startswith("moe"):
+        if leg.name.startswith("moe") or leg.name == "qat":
             result["legs"][leg.name] = leg.report(timer)
     moe_main = [l for l in legs if l.name == "moe_prefill"] or [l for l in legs if l.name == "moe_decode"]
     if moe_main:

@@ -38,7 +38,7 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int QBM = 128;   // output rows per workgroup
 constexpr int QBN = 256;   // output columns per workgroup (2 waves x 128)
-constexpr int QBK = 64;    // contraction per LDS stage
+constexpr int QBK = 32;    // contraction per LDS stage (48 KB of LDS: two workgroups per CU)
 constexpr int QT = 128;    // threads
 constexpr int QQ = QBK / 8;
 
@@ -112,127 +112,167 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);  // [b.hi : a.hi]
 }
 
-// One operand tile of `nrows` rows (128 or 256) x QBK contraction values.
+// One operand tile: kRows tile rows x QBK contraction values, staged as
+// [QQ][kRows][8] bf16 in LDS.  Each loader splits into load() (global ->
+// registers, issued before the MFMA work of the current stage) and store()
+// (registers -> LDS, with any dequantization or transposition).
 struct TileSrc {
-  int kind;
-  const uint16_t* bf;          // bf16 source base
-  int64_t ld;                  // row stride of the source (elements)
-  const int32_t* row_map;      // LD_ROWS / LD_ROWS_T: source row of local row / contraction index
-  int row_map_div;             // divide row_map values (sorted pair -> token)
-  int64_t row_base;            // first output row (LD_ROWS) or first contraction index (LD_ROWS_T)
-  int64_t row_end;             // end of valid rows / contraction indices
-  int64_t col_base;            // LD_ROWS_T / LD_FP4_T: first output column in the source
-  int64_t col_end;             // valid columns end
-  const uint8_t* codes;        // LD_FP4 / LD_FP4_T: weight codes of the expert [N, K/2]
-  const uint8_t* scales;       // [N, K/16]
-  int64_t wK;                  // weight K
-  int64_t wN;                  // weight N
-  int swap_nc;                 // unused (reserved)
-  const int32_t* nmap;         // LD_FP4: weight row of local row (nullptr: identity from col_base)
+  const uint16_t* bf;      // bf16 source
+  int64_t ld;              // its row stride (elements)
+  const int32_t* row_map;  // source row of a logical row (nullptr: identity)
+  int64_t row_base;        // first logical row (LD_ROWS) / first contraction row (LD_ROWS_T)
+  int64_t row_end;         // end of valid logical rows / contraction rows
+  int64_t col_base;        // first source column of the tile (LD_ROWS_T, LD_FP4*)
+  int64_t col_end;
+  const uint8_t* codes;    // FP4 weight of the expert [wN, wK/2]
+  const uint8_t* scales;   // [wN, wK/16]
+  int64_t wK, wN;
 };
 
 __device__ __forceinline__ int64_t src_row(const TileSrc& s, int64_t i) {
-  if (!s.row_map) return i;
-  const int64_t v = s.row_map[i];
-  return s.row_map_div > 0 ? v / s.row_map_div : v;
+  return s.row_map ? (int64_t)s.row_map[i] : i;
 }
 
-// Fill tile `dst` ([QQ][nrows][8] bf16) for contraction step ks.
+template <int kKind, int kRows>
+struct Loader;
+
+// bf16 rows, contraction contiguous: 8 threads per row, 16 B each.
 template <int kRows>
-__device__ __forceinline__ void fill_tile(const TileSrc& s, int ks, uint16_t* dst, int t) {
-  const int64_t k0 = (int64_t)ks * QBK;
-  if (s.kind == LD_ROWS) {
-    // rows of the tile are output rows; 8 threads per row, 16 B each
-    constexpr int kChunks = kRows * QQ;
+struct Loader<LD_ROWS, kRows> {
+  static constexpr int kN = kRows * QQ / QT;
+  uint4 v[kN];
+  __device__ __forceinline__ void load(const TileSrc& s, int ks, int t) {
+    const int64_t k0 = (int64_t)ks * QBK;
 #pragma unroll
-    for (int u = 0; u < kChunks / QT; ++u) {
-      const int c = t + QT * u;
-      const int r = c / QQ, q = c % QQ;
+    for (int u = 0; u < kN; ++u) {
+      const int c = t + QT * u, r = c / QQ, q = c % QQ;
       const int64_t gr = s.row_base + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (gr < s.row_end) v = *reinterpret_cast<const uint4*>(s.bf + src_row(s, gr) * s.ld + k0 + q * 8);
-      *reinterpret_cast<uint4*>(dst + ((size_t)q * kRows + r) * 8) = v;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (gr < s.row_end) v[u] = *reinterpret_cast<const uint4*>(s.bf + src_row(s, gr) * s.ld + k0 + q * 8);
     }
-  } else if (s.kind == LD_ROWS_T) {
-    // tile row = source column (col_base + r); contraction = source rows
-    // (k0 + 4j .. +4).  Task = 4 source rows x 8 columns, transposed.
-    constexpr int kTasks = (QBK / 4) * (kRows / 8);
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int t) const {
 #pragma unroll
-    for (int u = 0; u < kTasks / QT; ++u) {
-      const int task = t + QT * u;
-      const int cg = task % (kRows / 8), pg = task / (kRows / 8);
-      uint4 v[4];
+    for (int u = 0; u < kN; ++u) {
+      const int c = t + QT * u, r = c / QQ, q = c % QQ;
+      *reinterpret_cast<uint4*>(dst + ((size_t)q * kRows + r) * 8) = v[u];
+    }
+  }
+};
+
+// bf16 source whose rows are the contraction: task = 4 source rows x 8
+// columns, transposed with byte permutes into 4-value runs.
+template <int kRows>
+struct Loader<LD_ROWS_T, kRows> {
+  static constexpr int kN = (QBK / 4) * (kRows / 8) / QT;
+  uint4 v[kN][4];
+  __device__ __forceinline__ void load(const TileSrc& s, int ks, int t) {
+    const int64_t k0 = (int64_t)ks * QBK;
+#pragma unroll
+    for (int u = 0; u < kN; ++u) {
+      const int task = t + QT * u, cg = task % (kRows / 8), pg = task / (kRows / 8);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t p = k0 + 4 * pg + i;
-        v[i] = make_uint4(0, 0, 0, 0);
-        if (p < s.row_end - s.row_base && s.col_base + 8 * cg < s.col_end)
-          v[i] = *reinterpret_cast<const uint4*>(s.bf + src_row(s, s.row_base + p) * s.ld + s.col_base + 8 * cg);
+        const int64_t pr = s.row_base + k0 + 4 * pg + i;
+        v[u][i] = make_uint4(0, 0, 0, 0);
+        if (pr < s.row_end && s.col_base + 8 * cg < s.col_end)
+          v[u][i] = *reinterpret_cast<const uint4*>(s.bf + src_row(s, pr) * s.ld + s.col_base + 8 * cg);
       }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int t) const {
+#pragma unroll
+    for (int u = 0; u < kN; ++u) {
+      const int task = t + QT * u, cg = task % (kRows / 8), pg = task / (kRows / 8);
       const int q = (4 * pg) / 8, off4 = (4 * pg) % 8;
-      const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-      const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
-      const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
-      const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
+      const uint32_t w0[4] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w};
+      const uint32_t w1[4] = {v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+      const uint32_t w2[4] = {v[u][2].x, v[u][2].y, v[u][2].z, v[u][2].w};
+      const uint32_t w3[4] = {v[u][3].x, v[u][3].y, v[u][3].z, v[u][3].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // columns 2j (low halves) and 2j+1 (high halves)
         const uint2 lo = make_uint2(pack_lo(w0[j], w1[j]), pack_lo(w2[j], w3[j]));
         const uint2 hi = make_uint2(pack_hi(w0[j], w1[j]), pack_hi(w2[j], w3[j]));
         *reinterpret_cast<uint2*>(dst + ((size_t)q * kRows + 8 * cg + 2 * j) * 8 + off4) = lo;
         *reinterpret_cast<uint2*>(dst + ((size_t)q * kRows + 8 * cg + 2 * j + 1) * 8 + off4) = hi;
       }
     }
-  } else if (s.kind == LD_FP4) {
-    // tile row = weight row n; contraction = weight K.  Task = one row x 32
-    // values (16 B of codes, 2 block scales) -> 4 chunks of 8 bf16.
-    const float st = 1.0f;  // tensor scale applied to the accumulators
-    (void)st;
-    constexpr int kTasks = kRows * (QBK / 32);
+  }
+};
+
+// FP4 weight rows (tile row = weight row), contraction along the weight's K:
+// task = one row x 32 values (16 B codes, 2 block scales); dequantized once.
+template <int kRows>
+struct Loader<LD_FP4, kRows> {
+  static constexpr int kN = kRows * (QBK / 32) / QT;
+  uint4 cw[kN];
+  uint32_t sc[kN];
+  __device__ __forceinline__ void load(const TileSrc& s, int ks, int t) {
+    const int64_t k0 = (int64_t)ks * QBK;
 #pragma unroll
-    for (int u = 0; u < kTasks / QT; ++u) {
-      const int task = t + QT * u;
-      const int r = task / (QBK / 32), hq = task % (QBK / 32);
-      const int64_t n = s.nmap ? (int64_t)s.nmap[r] : s.col_base + r;
-      uint4 o0 = make_uint4(0, 0, 0, 0), o1 = o0, o2 = o0, o3 = o0;
-      if (n >= 0 && n < s.wN) {
-        const int64_t kk = k0 + 32 * hq;
-        const uint4 cw = *reinterpret_cast<const uint4*>(s.codes + n * (s.wK >> 1) + (kk >> 1));
-        const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(s.scales + n * (s.wK >> 4) + (kk >> 4));
-        const float sb0 = e4m3_to_f32(sc2 & 0xFFu), sb1 = e4m3_to_f32(sc2 >> 8);
-        o0 = fp4x8_to_bf16(cw.x, sb0);
-        o1 = fp4x8_to_bf16(cw.y, sb0);
-        o2 = fp4x8_to_bf16(cw.z, sb1);
-        o3 = fp4x8_to_bf16(cw.w, sb1);
+    for (int u = 0; u < kN; ++u) {
+      const int task = t + QT * u, r = task / (QBK / 32), hq = task % (QBK / 32);
+      const int64_t n = s.col_base + r;
+      const int64_t kk = k0 + 32 * hq;
+      cw[u] = make_uint4(0, 0, 0, 0);
+      sc[u] = 0;
+      if (n < s.wN) {
+        cw[u] = *reinterpret_cast<const uint4*>(s.codes + n * (s.wK >> 1) + (kk >> 1));
+        sc[u] = *reinterpret_cast<const uint16_t*>(s.scales + n * (s.wK >> 4) + (kk >> 4));
       }
-      const int q0 = 4 * hq;
-      *reinterpret_cast<uint4*>(dst + ((size_t)(q0 + 0) * kRows + r) * 8) = o0;
-      *reinterpret_cast<uint4*>(dst + ((size_t)(q0 + 1) * kRows + r) * 8) = o1;
-      *reinterpret_cast<uint4*>(dst + ((size_t)(q0 + 2) * kRows + r) * 8) = o2;
-      *reinterpret_cast<uint4*>(dst + ((size_t)(q0 + 3) * kRows + r) * 8) = o3;
     }
-  } else {  // LD_FP4_T
-    // tile row = weight column c (col_base + r); contraction = weight rows n
-    // (k0 ..).  Task = 4 weight rows x 16 columns (one block), transposed.
-    constexpr int kTasks = (QBK / 4) * (kRows / 16);
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int t) const {
 #pragma unroll
-    for (int u = 0; u < kTasks / QT; ++u) {
-      const int task = t + QT * u;
-      const int cb = task % (kRows / 16), ng = task / (kRows / 16);
+    for (int u = 0; u < kN; ++u) {
+      const int task = t + QT * u, r = task / (QBK / 32), hq = task % (QBK / 32);
+      const float sb0 = e4m3_to_f32(sc[u] & 0xFFu), sb1 = e4m3_to_f32(sc[u] >> 8);
+      const int q0 = 4 * hq;
+      *reinterpret_cast<uint4*>(dst + ((size_t)(q0 + 0) * kRows + r) * 8) = fp4x8_to_bf16(cw[u].x, sb0);
+      *reinterpret_cast<uint4*>(dst + ((size_t)(q0 + 1) * kRows + r) * 8) = fp4x8_to_bf16(cw[u].y, sb0);
+      *reinterpret_cast<uint4*>(dst + ((size_t)(q0 + 2) * kRows + r) * 8) = fp4x8_to_bf16(cw[u].z, sb1);
+      *reinterpret_cast<uint4*>(dst + ((size_t)(q0 + 3) * kRows + r) * 8) = fp4x8_to_bf16(cw[u].w, sb1);
+    }
+  }
+};
+
+// FP4 weight with the contraction over the weight's rows (tile row = weight
+// column): task = 4 weight rows x 16 columns (one block per row), dequantized
+// and transposed.
+template <int kRows>
+struct Loader<LD_FP4_T, kRows> {
+  static constexpr int kN = (QBK / 4) * (kRows / 16) / QT;
+  uint2 cw[kN][4];
+  uint32_t sc[kN][4];
+  __device__ __forceinline__ void load(const TileSrc& s, int ks, int t) {
+    const int64_t k0 = (int64_t)ks * QBK;
+#pragma unroll
+    for (int u = 0; u < kN; ++u) {
+      const int task = t + QT * u, cb = task % (kRows / 16), ng = task / (kRows / 16);
       const int64_t c0 = s.col_base + 16 * cb;
-      uint32_t rowv[4][8];  // [weight row][column pair] packed bf16
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t n = k0 + 4 * ng + i;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rowv[i][j] = 0u;
+        cw[u][i] = make_uint2(0, 0);
+        sc[u][i] = 0;
         if (n < s.wN && c0 < s.col_end) {
-          const uint2 cw = *reinterpret_cast<const uint2*>(s.codes + n * (s.wK >> 1) + (c0 >> 1));
-          const float sb = e4m3_to_f32(s.scales[n * (s.wK >> 4) + (c0 >> 4)]);
-          const uint4 a = fp4x8_to_bf16(cw.x, sb), b = fp4x8_to_bf16(cw.y, sb);
-          rowv[i][0] = a.x; rowv[i][1] = a.y; rowv[i][2] = a.z; rowv[i][3] = a.w;
-          rowv[i][4] = b.x; rowv[i][5] = b.y; rowv[i][6] = b.z; rowv[i][7] = b.w;
+          cw[u][i] = *reinterpret_cast<const uint2*>(s.codes + n * (s.wK >> 1) + (c0 >> 1));
+          sc[u][i] = s.scales[n * (s.wK >> 4) + (c0 >> 4)];
         }
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int t) const {
+#pragma unroll
+    for (int u = 0; u < kN; ++u) {
+      const int task = t + QT * u, cb = task % (kRows / 16), ng = task / (kRows / 16);
+      uint32_t rowv[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sb = e4m3_to_f32(sc[u][i]);
+        const uint4 a = fp4x8_to_bf16(cw[u][i].x, sb), b = fp4x8_to_bf16(cw[u][i].y, sb);
+        rowv[i][0] = a.x; rowv[i][1] = a.y; rowv[i][2] = a.z; rowv[i][3] = a.w;
+        rowv[i][4] = b.x; rowv[i][5] = b.y; rowv[i][6] = b.z; rowv[i][7] = b.w;
       }
       const int q = (4 * ng) / 8, off4 = (4 * ng) % 8;
 #pragma unroll
@@ -244,27 +284,55 @@ __device__ __forceinline__ void fill_tile(const TileSrc& s, int ks, uint16_t* ds
       }
     }
   }
+};
+
+// acc += A[QBM x QBK] * B[QBK x (this wave's 128 columns)] from one LDS stage.
+__device__ __forceinline__ void mfma_stage(const uint16_t* sa, const uint16_t* sb, int wave, int l32,
+                                           int h, floatx16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int s = 0; s < QBK / 16; ++s) {
+    const int q = 2 * s + h;
+    bf16x8_t af[4], bf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&sa[((size_t)q * QBM + 32 * i + l32) * 8]);
+      __builtin_memcpy(&af[i], &v, 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&sb[((size_t)q * QBN + 128 * wave + 32 * j + l32) * 8]);
+      __builtin_memcpy(&bf[j], &v, 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  }
 }
 
-// Output tile QBM x QBN = (rows of A) x (rows of B); contraction nk stages.
-template <int kMode>
+// Output tile QBM x QBN = (rows of A) x (rows of B); contraction nk stages,
+// software-pipelined: stage ks + 1 is read from global memory before the
+// MFMA work of stage ks and written to the other LDS buffer after it (the
+// last stage re-reads itself into the idle buffer, which nobody reads).
+template <int kMode, int kKA, int kKB>
 __global__ __launch_bounds__(QT) void k_qat_gemm(QatParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][QQ * QBM * 8];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][QQ * QBN * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sA0[QQ * QBM * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sA1[QQ * QBM * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sB0[QQ * QBN * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sB1[QQ * QBN * 8];
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, l32 = lane & 31, h = lane >> 5;
 
   TileSrc A, B;
-  A.row_map = nullptr; A.row_map_div = 0; A.nmap = nullptr;
-  B.row_map = nullptr; B.row_map_div = 0; B.nmap = nullptr;
+  A.row_map = nullptr;
+  B.row_map = nullptr;
   int e;
   int64_t out_r0, out_r_end, out_c0, out_c_end, nk;
-  __shared__ int32_t s_nmap[QBN];
+  const int G = gridDim.x, per = G >> 3;
+  const int logical = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
 
   if (kMode == NVQ_QAT_WGRAD) {
-    // grid: E x n_tiles_m (over N) x n_tiles_n (over K); XCD-aware
-    const int G = gridDim.x, per = G >> 3;
-    const int logical = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     const int per_e = p.n_tiles_m * p.n_tiles_n;
     e = logical / per_e;
     if (e >= p.E) return;
@@ -274,37 +342,32 @@ __global__ __launch_bounds__(QT) void k_qat_gemm(QatParams p) {
     out_r0 = (int64_t)mt * QBM; out_r_end = p.N;
     out_c0 = (int64_t)nt * QBN; out_c_end = p.K;
     nk = (pe1 - pe0 + QBK - 1) / QBK;
-    A.kind = LD_ROWS_T; A.bf = p.dy; A.ld = p.N; A.row_base = pe0; A.row_end = pe1;
-    A.col_base = out_r0; A.col_end = p.N;
-    B.kind = LD_ROWS_T; B.bf = p.x; B.ld = p.K; B.row_base = pe0; B.row_end = pe1;
-    B.col_base = out_c0; B.col_end = p.K; B.row_map = p.a_row; B.row_map_div = p.a_row ? 0 : 0;
+    A.bf = p.dy; A.ld = p.N; A.row_base = pe0; A.row_end = pe1; A.col_base = out_r0; A.col_end = p.N;
+    B.bf = p.x; B.ld = p.K; B.row_base = pe0; B.row_end = pe1; B.col_base = out_c0; B.col_end = p.K;
+    B.row_map = p.a_row;
   } else {
-    const int G = gridDim.x, per = G >> 3;
-    const int logical = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     const int mt = logical % p.max_tiles, nt = logical / p.max_tiles;
     if (nt >= p.n_tiles_n || mt >= *p.ntiles) return;
     e = p.tiles[2 * mt];
     out_r0 = p.tiles[2 * mt + 1];
     out_r_end = p.off[e + 1];
     out_c0 = (int64_t)nt * QBN;
-    const uint8_t* wc = p.w_codes + (int64_t)e * p.N * (p.K >> 1);
-    const uint8_t* ws = p.w_scales + (int64_t)e * p.N * (p.K >> 4);
+    B.codes = p.w_codes + (int64_t)e * p.N * (p.K >> 1);
+    B.scales = p.w_scales + (int64_t)e * p.N * (p.K >> 4);
+    B.wK = p.K; B.wN = p.N; B.col_base = out_c0;
+    A.row_base = out_r0; A.row_end = out_r_end;
     if (kMode == NVQ_QAT_FWD) {
       out_c_end = p.N;
       nk = p.K / QBK;
-      A.kind = LD_ROWS; A.bf = p.x; A.ld = p.K; A.row_map = p.a_row; A.row_base = out_r0;
-      A.row_end = out_r_end;
-      B.kind = LD_FP4; B.codes = wc; B.scales = ws; B.wK = p.K; B.wN = p.N; B.col_base = out_c0;
+      A.bf = p.x; A.ld = p.K; A.row_map = p.a_row;
       B.col_end = p.N;
-    } else {  // DGRAD
+    } else {
       out_c_end = p.K;
       nk = p.N / QBK;
-      A.kind = LD_ROWS; A.bf = p.dy; A.ld = p.N; A.row_base = out_r0; A.row_end = out_r_end;
-      B.kind = LD_FP4_T; B.codes = wc; B.scales = ws; B.wK = p.K; B.wN = p.N; B.col_base = out_c0;
+      A.bf = p.dy; A.ld = p.N;
       B.col_end = p.K;
     }
   }
-  (void)s_nmap;
 
   floatx16_t acc[4][4];
 #pragma unroll
@@ -314,40 +377,24 @@ __global__ __launch_bounds__(QT) void k_qat_gemm(QatParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+  Loader<kKA, QBM> la;
+  Loader<kKB, QBN> lb;
   if (nk > 0) {
-    fill_tile<QBM>(A, 0, sA[0], t);
-    fill_tile<QBN>(B, 0, sB[0], t);
+    la.load(A, 0, t);
+    lb.load(B, 0, t);
+    la.store(sA0, t);
+    lb.store(sB0, t);
   }
   __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-#pragma unroll
-    for (int s = 0; s < QBK / 16; ++s) {
-      const int q = 2 * s + h;
-      bf16x8_t af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&sA[buf][((size_t)q * QBM + 32 * i + l32) * 8]);
-        __builtin_memcpy(&af[i], &v, 16);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 v =
-            *reinterpret_cast<const uint4*>(&sB[buf][((size_t)q * QBN + 128 * wave + 32 * j + l32) * 8]);
-        __builtin_memcpy(&bf[j], &v, 16);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (ks + 1 < nk) {
-      // the other buffer was last read one step ago; everyone has passed the
-      // barrier at the end of that step
-      fill_tile<QBM>(A, ks + 1, sA[buf ^ 1], t);
-      fill_tile<QBN>(B, ks + 1, sB[buf ^ 1], t);
-    }
+    const bool odd = ks & 1;
+    // Next stage (clamped to the last one, so no load sits under a branch).
+    const int nx = ks + 1 < nk ? ks + 1 : ks;
+    la.load(A, nx, t);
+    lb.load(B, nx, t);
+    mfma_stage(odd ? sA1 : sA0, odd ? sB1 : sB0, wave, l32, h, acc);
+    la.store(odd ? sA0 : sA1, t);
+    lb.store(odd ? sB0 : sB1, t);
     __syncthreads();
   }
 
@@ -409,7 +456,7 @@ extern "C" int qat_fakequant_gemm_w4a16(const nvq_qat_gemm_args* a, void* stream
     return NVQ_EINVAL;
   if (!a->expert_offsets || !a->ws) return NVQ_EINVAL;
   if (a->rows < 0 || a->E < 1 || a->E > 1024 || a->N <= 0 || a->K <= 0) return NVQ_ESHAPE;
-  if (a->K % QBK != 0 || a->N % QBK != 0) return NVQ_ESHAPE;  // 64-element contraction stages
+  if (a->K % QBK != 0 || a->N % QBK != 0) return NVQ_ESHAPE;  // 32-element contraction stages
   const bool wgrad = a->mode == NVQ_QAT_WGRAD;
   if (a->mode != NVQ_QAT_DGRAD && !a->x) return NVQ_EINVAL;
   if (a->mode != NVQ_QAT_FWD && !a->dy) return NVQ_EINVAL;
@@ -436,7 +483,8 @@ extern "C" int qat_fakequant_gemm_w4a16(const nvq_qat_gemm_args* a, void* stream
     p.n_tiles_n = (int)((a->K + QBN - 1) / QBN);
     const int64_t G0 = a->E * p.n_tiles_m * p.n_tiles_n;
     const int64_t G = (G0 + 7) / 8 * 8;
-    hipLaunchKernelGGL(k_qat_gemm<NVQ_QAT_WGRAD>, dim3((unsigned)G), dim3(QT), 0, s, p);
+    hipLaunchKernelGGL((k_qat_gemm<NVQ_QAT_WGRAD, LD_ROWS_T, LD_ROWS_T>), dim3((unsigned)G), dim3(QT), 0,
+                       s, p);
     return last_launch();
   }
   if (a->rows == 0) return NVQ_OK;
@@ -449,8 +497,9 @@ extern "C" int qat_fakequant_gemm_w4a16(const nvq_qat_gemm_args* a, void* stream
   const int64_t G0 = (int64_t)L.max_tiles * p.n_tiles_n;
   const int64_t G = (G0 + 7) / 8 * 8;
   if (a->mode == NVQ_QAT_FWD)
-    hipLaunchKernelGGL(k_qat_gemm<NVQ_QAT_FWD>, dim3((unsigned)G), dim3(QT), 0, s, p);
+    hipLaunchKernelGGL((k_qat_gemm<NVQ_QAT_FWD, LD_ROWS, LD_FP4>), dim3((unsigned)G), dim3(QT), 0, s, p);
   else
-    hipLaunchKernelGGL(k_qat_gemm<NVQ_QAT_DGRAD>, dim3((unsigned)G), dim3(QT), 0, s, p);
+    hipLaunchKernelGGL((k_qat_gemm<NVQ_QAT_DGRAD, LD_ROWS, LD_FP4_T>), dim3((unsigned)G), dim3(QT), 0, s,
+                       p);
   return last_launch();
 }

@@ -277,7 +277,7 @@ def moe_grouped_gemm_w4a4_comp(a_codes, a_scales, a_tensor_scale, w_codes, w_sca
 
 def qat_fakequant_gemm_w4a16(mode, w_codes, w_scales, w_tensor_scale, expert_offsets, rows,
                              x=None, dy=None, a_row=None, dw=None, accumulate=False,
-                             want_bf16=True, want_f32=False, ws=None):
+                             want_bf16=True, want_f32=False, ws=None, out=None):
     """FWD: returns (y_bf16, y_f32); DGRAD: (dx_bf16, dx_f32); WGRAD: dw [E, N, K] fp32."""
     L = load()
     E, N, Kh = w_codes.shape
@@ -286,8 +286,11 @@ def qat_fakequant_gemm_w4a16(mode, w_codes, w_scales, w_tensor_scale, expert_off
     ob = of = None
     if mode in (NVQ_QAT_FWD, NVQ_QAT_DGRAD):
         cols = N if mode == NVQ_QAT_FWD else K
-        ob = torch.empty(rows, cols, dtype=torch.bfloat16, device=dev) if want_bf16 else None
-        of = torch.empty(rows, cols, dtype=torch.float32, device=dev) if want_f32 else None
+        if out is not None:
+            ob, of = out
+        else:
+            ob = torch.empty(rows, cols, dtype=torch.bfloat16, device=dev) if want_bf16 else None
+            of = torch.empty(rows, cols, dtype=torch.float32, device=dev) if want_f32 else None
     elif dw is None:
         dw = torch.empty(E, N, K, dtype=torch.float32, device=dev)
     if ws is None:
