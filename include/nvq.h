@@ -113,7 +113,9 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
  * scores_out nullable [K]: receives the score used.
  * resid_out  nullable [rows, k] bf16: the compensation operand
  *            bf16(fl32(x - dequant(q(x))))[:, idx_out].
- * 0 <= k <= K; k == 0 writes nothing to idx_out/resid_out.
+ * 0 <= k <= K; k == 0 writes nothing to idx_out/resid_out.  k <= 1024 takes
+ * any K (radix select); k > 1024 needs K <= 8192, else NVQ_EUNSUPPORTED.
+ * Scores compare as numbers (-0 equals +0); they must not be NaN.
  */
 size_t residual_topk_workspace_bytes(int64_t rows, int64_t K, int32_t k);
 int residual_topk_channels(const void* x, int x_dtype, int64_t rows, int64_t K,

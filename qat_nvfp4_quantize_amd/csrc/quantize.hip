@@ -111,37 +111,126 @@ __device__ __forceinline__ float2 fp4_pair_to_f32(uint32_t w) {
   return make_float2(t[0], t[1]);
 }
 
-// Quantize one block held as 16 floats; returns the codes, writes *sc_out and
-// (kScore) adds |r| of each element to acc.
-// slot: this lane's 16-float LDS area, used only on the rare exact path so the
-// element loop there can index dynamically without a private-memory array.
-template <bool kScore, bool kFast>
-__device__ __forceinline__ uint2 quantize_block(const float (&xf)[16], float s_t, double six_st,
-                                                float g, float inv_st, uint32_t* sc_out,
-                                                float (&acc)[16], uint32_t& bad, float* slot) {
-  constexpr bool fast = kFast;
+// Block scale for a tensor scale in the fast range: the E4M3 value nearest the
+// real quotient am / (6 s_t), ties to even, saturating at 0x7E (448).
+// q = fl(am * g), g = fl(1 / (6 s_t)), is within about 1 ulp of the quotient,
+// so it decides alone unless it lies within 8 ulp of an E4M3 midpoint (a
+// value with one more significant bit than the grid).  There, the sign of
+// am - 6 mid s_t decides: 6 mid has at most 7 significant bits, so
+// fma(-(6 mid), s_t, am) rounds the exact difference once and keeps its sign,
+// and it is zero exactly on a tie, which goes to the even code.
+__device__ __forceinline__ uint32_t e4m3_code_fast(float am, float g, float s_t) {
+  const float q = am * g;
+  if (!(q < 448.0f)) return 0x7E;
+  const uint32_t qb = __float_as_uint(q);
+  uint32_t c_lo;
+  float mid;
+  if (q >= 0.015625f) {
+    // normal E4M3: grid = 3 mantissa bits; midpoints have bit 19 set and the
+    // low 19 bits clear
+    if ((qb & 0xFFFFFu) - 0x80000u + 8u >= 16u)
+      return (qb - (120u << 23) + 0x7FFFFu + ((qb >> 20) & 1u)) >> 20;
+    mid = __uint_as_float((qb & 0xFFF00000u) | 0x80000u);
+    c_lo = ((qb & 0xFFF00000u) - (120u << 23)) >> 20;
+  } else {
+    // subnormal E4M3: grid 2^-9, midpoints at odd multiples of 2^-10
+    const float t = q * 512.0f;
+    const float fl = __builtin_floorf(t);
+    if (!(fabsf((t - fl) - 0.5f) < 0x1p-16f)) return (uint32_t)__builtin_rintf(t);
+    mid = (fl + 0.5f) * 0x1p-9f;
+    c_lo = (uint32_t)fl;
+  }
+  const float d = __builtin_fmaf(-(6.0f * mid), s_t, am);
+  return c_lo + ((d > 0.0f || (d == 0.0f && (c_lo & 1u))) ? 1u : 0u);
+}
+
+template <bool kBF16>
+struct RowBlock {
+  uint4 q[kBF16 ? 2 : 4];
+  __device__ __forceinline__ void load(const void* xv, int64_t row, int64_t K, int64_t blk) {
+    const uint4* p = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(xv) + (row * K + blk * 16) * (kBF16 ? 2 : 4));
+#pragma unroll
+    for (int i = 0; i < (kBF16 ? 2 : 4); ++i) q[i] = p[i];
+  }
+  __device__ __forceinline__ uint32_t word(int i) const {
+    const uint4& v = q[i >> 2];
+    return (i & 3) == 0 ? v.x : (i & 3) == 1 ? v.y : (i & 3) == 2 ? v.z : v.w;
+  }
+  __device__ __forceinline__ void unpack(float (&xf)[16]) const {
+    if (kBF16) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xf[2 * j] = bf16_lo(word(j));
+        xf[2 * j + 1] = bf16_hi(word(j));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xf[j] = __uint_as_float(word(j));
+    }
+  }
+  // Stores the raw words into this lane's LDS slot (element j readable by slot_elem).
+  __device__ __forceinline__ void to_slot(uint32_t* slot) const {
+    uint4* s4 = reinterpret_cast<uint4*>(slot);
+#pragma unroll
+    for (int i = 0; i < (kBF16 ? 2 : 4); ++i) s4[i] = q[i];
+  }
+  __device__ static __forceinline__ float slot_elem(const uint32_t* slot, int j) {
+    if (kBF16) {
+      const uint32_t w = slot[j >> 1];
+      return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+    return __uint_as_float(slot[j]);
+  }
+};
+
+// v = fl32(fl32(|G| s_b) s_t) for the 16 codes of a block; acc[j] += |r_j| with
+// r_j = fl32(x_j - v_j) (|r| = | |x| - v | since v carries the sign of x).
+__device__ __forceinline__ void add_residual(const float (&xf)[16], uint2 cw, float s_b, float s_t,
+                                             float (&acc)[16]) {
+  float2 g2[8];
+  g2[0] = fp4_pair_to_f32<0>(cw.x);
+  g2[1] = fp4_pair_to_f32<1>(cw.x);
+  g2[2] = fp4_pair_to_f32<2>(cw.x);
+  g2[3] = fp4_pair_to_f32<3>(cw.x);
+  g2[4] = fp4_pair_to_f32<0>(cw.y);
+  g2[5] = fp4_pair_to_f32<1>(cw.y);
+  g2[6] = fp4_pair_to_f32<2>(cw.y);
+  g2[7] = fp4_pair_to_f32<3>(cw.y);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float v0 = (fabsf(g2[j].x) * s_b) * s_t;
+    const float v1 = (fabsf(g2[j].y) * s_b) * s_t;
+    acc[2 * j] += fabsf(fabsf(xf[2 * j]) - v0);
+    acc[2 * j + 1] += fabsf(fabsf(xf[2 * j + 1]) - v1);
+  }
+}
+
+// One block, tensor scale in the fast range.  Element codes: the hardware FP4
+// conversion rounds y = x h with h bracketed at (1 -+ 2^-20) / (s_b s_t); y is
+// within 2^-21.5 of the real quotient, so both brackets agree unless the
+// quotient is within 2^-19 of an E2M1 midpoint.  Where they disagree the
+// upper index is the lower plus one and the sign of |x| - m s_b s_t (m the
+// midpoint between them; m s_b has at most 7 significant bits, so one fma
+// rounds the exact difference once) decides; zero is a tie, which goes to the
+// even index.  slot: this lane's LDS words for the rare fix-up.
+template <bool kBF16, bool kScore>
+__device__ __forceinline__ void encode_block_fast(const RowBlock<kBF16>& rb, float s_t, float g,
+                                                  float inv_st, uint32_t& sc_out, uint2& cw_out,
+                                                  float (&acc)[16], uint32_t& bad, uint32_t* slot) {
+  float xf[16];
+  rb.unpack(xf);
   float am = __builtin_fmaxf(__builtin_fmaxf(fabsf(xf[0]), fabsf(xf[1])), fabsf(xf[2]));
 #pragma unroll
   for (int j = 3; j < 15; j += 2) am = __builtin_fmaxf(__builtin_fmaxf(am, fabsf(xf[j])), fabsf(xf[j + 1]));
   am = __builtin_fmaxf(am, fabsf(xf[15]));
   if (!(am <= 3.40282347e38f)) bad = 1;
-  // Block scale: the E4M3 value nearest amax_b / (6 s_t).  E4M3 midpoints have
-  // 19 trailing zero mantissa bits; q is within 2 ulp of the real quotient.
-  uint32_t sc = 0;
-  if (s_t > 0.0f) {
-    const float q = am * g;
-    const uint32_t qb = __float_as_uint(q);
-    const bool near = !fast || (uint32_t)((qb << 13) + (8u << 13)) < (16u << 13);
-    sc = near ? e4m3_code_exact(am, six_st) : e4m3_rne_f32(q);
-  }
-  *sc_out = sc;
+  const uint32_t sc = e4m3_code_fast(am, g, s_t);
+  sc_out = sc;
   const float s_b = e4m3_value_f32(sc);
-  // Element codes: round y = x * h with h bracketed at (1 -+ 2^-20) / (s_b s_t);
-  // both brackets agree unless the real quotient sits within 2^-19 of an E2M1
-  // midpoint, in which case the block is decided in fp64.
-  const float h = (sc == 0 || !fast) ? 0.0f : __builtin_amdgcn_rcpf(s_b) * inv_st;
-  const float h_lo = h * 0.99999904632568359375f;   // 1 - 2^-20
-  const float h_hi = h * 1.00000095367431640625f;   // 1 + 2^-20
+  const float h = sc == 0 ? 0.0f : __builtin_amdgcn_rcpf(s_b) * inv_st;
+  const float h_lo = h * 0.99999904632568359375f;  // 1 - 2^-20
+  const float h_hi = h * 1.00000095367431640625f;  // 1 + 2^-20
   uint32_t lo0 = 0, lo1 = 0, hi0 = 0, hi1 = 0;
   lo0 = cvt_fp4_pair<0>(lo0, xf[0] * h_lo, xf[1] * h_lo);
   lo0 = cvt_fp4_pair<1>(lo0, xf[2] * h_lo, xf[3] * h_lo);
@@ -159,114 +248,76 @@ __device__ __forceinline__ uint2 quantize_block(const float (&xf)[16], float s_t
   hi1 = cvt_fp4_pair<1>(hi1, xf[10] * h_hi, xf[11] * h_hi);
   hi1 = cvt_fp4_pair<2>(hi1, xf[12] * h_hi, xf[13] * h_hi);
   hi1 = cvt_fp4_pair<3>(hi1, xf[14] * h_hi, xf[15] * h_hi);
-  uint2 cw = make_uint2(lo0, lo1);
-  uint32_t d0 = lo0 ^ hi0, d1 = lo1 ^ hi1;  // nibbles where the brackets disagree
-  if (!fast) {
-    // Extreme tensor scale: decide every element in fp64, where S = s_b s_t
-    // (<= 28 bits) and every midpoint product is exact.
-#pragma unroll
-    for (int j = 0; j < 16; ++j) slot[j] = xf[j];
-    const double S = (double)s_b * (double)s_t;
-    uint32_t c0 = 0u, c1 = 0u;
-#pragma unroll 1
-    for (int j = 0; j < 16; ++j) {
-      const float v = slot[j];
-      const uint32_t idx = (sc == 0) ? 0u : e2m1_index_exact(fabsf(v), S);
-      const uint32_t nib = (idx | ((__float_as_uint(v) >> 28) & 8u)) << (4 * (j & 7));
-      c0 |= (j < 8) ? nib : 0u;
-      c1 |= (j < 8) ? 0u : nib;
-    }
-    cw = make_uint2(c0, c1);
-  } else if (d0 | d1) {
-    // The real quotient is within 2^-19 of the midpoint m between the lower
-    // bracket's index i and i + 1.  fma(-(m s_b), s_t, |x|) forms |x| - m s_b s_t
-    // exactly (m s_b <= 7 bits is exact in fp32) and rounds once, so its sign
-    // is exact and it is zero exactly on a tie, which goes to the even index.
-#pragma unroll
-    for (int j = 0; j < 16; ++j) slot[j] = xf[j];
+  uint32_t d0 = lo0 ^ hi0, d1 = lo1 ^ hi1;
+  if (d0 | d1) {
+    rb.to_slot(slot);
+    const float half_sb = 0.5f * s_b;
 #pragma unroll 1
     while (d0 | d1) {
       const bool first = d0 != 0;
-      const uint32_t dm = first ? d0 : d1;
-      const uint32_t sh = __builtin_ctz(dm) & ~3u;  // nibble shift within the word
+      const uint32_t sh = __builtin_ctz(first ? d0 : d1) & ~3u;
       const int j = (first ? 0 : 8) + (int)(sh >> 2);
-      const uint32_t w = first ? cw.x : cw.y;
-      const uint32_t i = (w >> sh) & 7u;  // lower index (magnitude)
-      const float m = 0.5f * (e2m1_mag(i) + e2m1_mag(i + 1u));
-      const float d = __builtin_fmaf(-(m * s_b), s_t, fabsf(slot[j]));
-      const uint32_t up = (d > 0.0f || (d == 0.0f && ((i + 1u) & 1u) == 0u)) ? 1u : 0u;
-      const uint32_t nw = (w & ~(7u << sh)) | ((i + up) << sh);
+      const uint32_t wl = first ? lo0 : lo1;
+      const uint32_t il = (wl >> sh) & 7u, ih = ((first ? hi0 : hi1) >> sh) & 7u;
+      // |G_lo| and |G_hi| from one conversion of the byte (il, ih)
+      const float2 gg = fp4_pair_to_f32<0>(il | (ih << 4));
+      const float d = __builtin_fmaf(-((gg.x + gg.y) * half_sb), s_t,
+                                     fabsf(RowBlock<kBF16>::slot_elem(slot, j)));
+      const uint32_t pick = (d > 0.0f || (d == 0.0f && !(ih & 1u))) ? ih : il;
+      const uint32_t nw = (wl & ~(7u << sh)) | (pick << sh);
       if (first) {
-        cw.x = nw;
+        lo0 = nw;
         d0 &= ~(15u << sh);
       } else {
-        cw.y = nw;
+        lo1 = nw;
         d1 &= ~(15u << sh);
       }
     }
   }
-  if (kScore) {
-    // v = fl32(fl32(|G| s_b) s_t); |r| = | |x| - v | (= |fl32(x - v)|).
-    float2 g2[8];
-    g2[0] = fp4_pair_to_f32<0>(cw.x);
-    g2[1] = fp4_pair_to_f32<1>(cw.x);
-    g2[2] = fp4_pair_to_f32<2>(cw.x);
-    g2[3] = fp4_pair_to_f32<3>(cw.x);
-    g2[4] = fp4_pair_to_f32<0>(cw.y);
-    g2[5] = fp4_pair_to_f32<1>(cw.y);
-    g2[6] = fp4_pair_to_f32<2>(cw.y);
-    g2[7] = fp4_pair_to_f32<3>(cw.y);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float v0 = (fabsf(g2[j].x) * s_b) * s_t;
-      const float v1 = (fabsf(g2[j].y) * s_b) * s_t;
-      acc[2 * j] += fabsf(fabsf(xf[2 * j]) - v0);
-      acc[2 * j + 1] += fabsf(fabsf(xf[2 * j + 1]) - v1);
-    }
-  }
-  return cw;
+  cw_out = make_uint2(lo0, lo1);
+  if (kScore) add_residual(xf, cw_out, s_b, s_t, acc);
 }
 
-template <bool kBF16>
-struct RowBlock {
-  uint4 q[kBF16 ? 2 : 4];
-  __device__ __forceinline__ void load(const void* xv, int64_t row, int64_t K, int64_t blk) {
-    const uint4* p = reinterpret_cast<const uint4*>(
-        static_cast<const char*>(xv) + (row * K + blk * 16) * (kBF16 ? 2 : 4));
+// One block decided entirely in fp64 (tensor scale outside [2^-100, 2^100],
+// where the fp32 reciprocals would overflow).  Off the hot path.
+template <bool kBF16, bool kScore>
+__device__ __forceinline__ void encode_block_exact(const RowBlock<kBF16>& rb, float s_t,
+                                                   double six_st, uint32_t& sc_out,
+                                                   uint2& cw_out, float (&acc)[16],
+                                                   uint32_t& bad, uint32_t* slot) {
+  float xf[16];
+  rb.unpack(xf);
+  float am = 0.0f;
 #pragma unroll
-    for (int i = 0; i < (kBF16 ? 2 : 4); ++i) q[i] = p[i];
+  for (int j = 0; j < 16; ++j) am = __builtin_fmaxf(am, fabsf(xf[j]));
+  if (!(am <= 3.40282347e38f)) bad = 1;
+  const uint32_t sc = s_t > 0.0f ? e4m3_code_exact(am, six_st) : 0u;
+  sc_out = sc;
+  const float s_b = e4m3_value_f32(sc);
+  rb.to_slot(slot);
+  const double S = (double)s_b * (double)s_t;
+  uint32_t c0 = 0u, c1 = 0u;
+#pragma unroll 1
+  for (int j = 0; j < 16; ++j) {
+    const float v = RowBlock<kBF16>::slot_elem(slot, j);
+    const uint32_t idx = (sc == 0) ? 0u : e2m1_index_exact(fabsf(v), S);
+    const uint32_t nib = (idx | ((__float_as_uint(v) >> 28) & 8u)) << (4 * (j & 7));
+    c0 |= (j < 8) ? nib : 0u;
+    c1 |= (j < 8) ? 0u : nib;
   }
-  __device__ __forceinline__ void unpack(float (&xf)[16]) const {
-    if (kBF16) {
-      const uint32_t w[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        xf[2 * j] = bf16_lo(w[j]);
-        xf[2 * j + 1] = bf16_hi(w[j]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xf[4 * j] = __uint_as_float(q[j].x);
-        xf[4 * j + 1] = __uint_as_float(q[j].y);
-        xf[4 * j + 2] = __uint_as_float(q[j].z);
-        xf[4 * j + 3] = __uint_as_float(q[j].w);
-      }
-    }
-  }
-};
+  cw_out = make_uint2(c0, c1);
+  if (kScore) add_residual(xf, cw_out, s_b, s_t, acc);
+}
 
 struct RowsResult {
   float acc[16];
   uint32_t bad;
 };
 
-// All rows of one lane decided in fp64 (tensor scale outside [2^-100, 2^100],
-// where the fp32 reciprocals would overflow).  Out of line: never on the hot path.
 template <bool kBF16, bool kScore>
 __device__ __attribute__((noinline)) RowsResult quantize_rows_exact(
     const void* xv, int64_t row0, int nrows, int64_t K, int64_t blk, float s_t, double six_st,
-    uint8_t* codes, uint8_t* scales, float* slot) {
+    uint8_t* codes, uint8_t* scales, uint32_t* slot) {
   RowsResult res;
 #pragma unroll
   for (int j = 0; j < 16; ++j) res.acc[j] = 0.0f;
@@ -275,11 +326,9 @@ __device__ __attribute__((noinline)) RowsResult quantize_rows_exact(
   for (int rr = 0; rr < nrows; ++rr) {
     RowBlock<kBF16> rb;
     rb.load(xv, row0 + rr, K, blk);
-    float xf[16];
-    rb.unpack(xf);
     uint32_t sc;
-    const uint2 cw =
-        quantize_block<kScore, false>(xf, s_t, six_st, 0.0f, 0.0f, &sc, res.acc, res.bad, slot);
+    uint2 cw;
+    encode_block_exact<kBF16, kScore>(rb, s_t, six_st, sc, cw, res.acc, res.bad, slot);
     *reinterpret_cast<uint2*>(codes + (row0 + rr) * (K >> 1) + blk * 8) = cw;
     scales[(row0 + rr) * nblk + blk] = (uint8_t)sc;
   }
@@ -288,30 +337,36 @@ __device__ __attribute__((noinline)) RowsResult quantize_rows_exact(
 
 // Workgroup = 8 waves = one 128-row chunk x 1024 columns; wave w = the 16-row
 // sub-chunk w; lane l = one 16-element block column.  Each lane quantizes its
-// block in each of its rows (next row prefetched) and keeps 16 per-column
+// block in each of its rows (three rows in flight) and keeps 16 per-column
 // residual sums, sequential in row order.  The chunk partial is the in-order
 // sum of the 8 wave sums, via LDS.
 template <bool kBF16, bool kScore>
-__global__ __launch_bounds__(512) void k_quantize(
+__global__ __launch_bounds__(512, 2) void k_quantize(
     const void* __restrict__ xv, int64_t rows, int64_t K, const uint32_t* __restrict__ amax_partial,
     int n_partial, const float* __restrict__ amax_in, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tensor_scale,
     float* __restrict__ chunk_partial, uint32_t* __restrict__ status) {
   __shared__ float s_part[kScore ? 8 * kQCols : 1];
-  __shared__ float s_slot[512 * 16];
+  __shared__ uint32_t s_slot[512 * (kBF16 ? 8 : 16)];
   __shared__ float s_amax;
   const int item = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float* slot = s_slot + threadIdx.x * 16;
+  uint32_t* slot = s_slot + threadIdx.x * (kBF16 ? 8 : 16);
 
   const int64_t nblk = K >> 4;
   const int64_t blk = (int64_t)blockIdx.x * kQBlocksPerWave + lane;
   const int64_t r0 = (int64_t)blockIdx.y * kQRows + wave * kQSub;
   const bool active = blk < nblk;
   const int nrows = (int)max<int64_t>(0, min<int64_t>(kQSub, rows - r0));
-  const int64_t item_row0 = (int64_t)item * rows;
-  RowBlock<kBF16> cur;
-  if (active && nrows > 0) cur.load(xv, item_row0 + r0, K, blk);
+  const int64_t row0 = (int64_t)item * rows + r0;
+  const int64_t last = row0 + max(nrows, 1) - 1;
+  // first rows in flight before the tensor amax is known
+  RowBlock<kBF16> b0, b1, b2;
+  if (active && nrows > 0) {
+    b0.load(xv, row0, K, blk);
+    b1.load(xv, min(row0 + 1, last), K, blk);
+    b2.load(xv, min(row0 + 2, last), K, blk);
+  }
 
   {
     // Tensor amax: every thread loads its share of the pass-1 partials at once.
@@ -351,53 +406,36 @@ __global__ __launch_bounds__(512) void k_quantize(
   uint32_t bad = 0;
 
   if (active && !fast) {
-    const RowsResult res = quantize_rows_exact<kBF16, kScore>(xv, item_row0 + r0, nrows, K, blk, s_t,
-                                                              six_st, codes, scales, slot);
+    const RowsResult res = quantize_rows_exact<kBF16, kScore>(xv, row0, nrows, K, blk, s_t, six_st,
+                                                              codes, scales, slot);
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = res.acc[j];
     bad = res.bad;
-  } else if (active) {
+  } else if (active && nrows > 0) {
     auto process = [&](const RowBlock<kBF16>& rb, int64_t row) {
-      float xf[16];
-      rb.unpack(xf);
       uint32_t sc;
-      const uint2 cw = quantize_block<kScore, true>(xf, s_t, six_st, g, inv_st, &sc, acc, bad, slot);
+      uint2 cw;
+      encode_block_fast<kBF16, kScore>(rb, s_t, g, inv_st, sc, cw, acc, bad, slot);
       *reinterpret_cast<uint2*>(codes + row * (K >> 1) + blk * 8) = cw;
       scales[row * nblk + blk] = (uint8_t)sc;
     };
-    const int64_t row0 = item_row0 + r0;
-    if (nrows == kQSub) {
-      // Four rotating row buffers: row rr + 4 is loaded into a buffer right
-      // after that buffer's row is processed.  Refill addresses are clamped to
-      // the last row instead of branching, so no load sits under a branch and
-      // the waits the compiler places stay exact.
-      RowBlock<kBF16> b0 = cur, b1, b2, b3;
-      b1.load(xv, row0 + 1, K, blk);
-      b2.load(xv, row0 + 2, K, blk);
-      b3.load(xv, row0 + 3, K, blk);
-      const int64_t last = row0 + kQSub - 1;
+    // Three rotating row buffers: row rr + 3 is loaded into a buffer right
+    // after that buffer's row is processed.  Refill addresses are clamped to
+    // the last row instead of branching, so no load sits under a branch and
+    // the waits the compiler places stay exact.  Rows past nrows are loaded
+    // (clamped) but never processed.
 #pragma unroll 1
-      for (int rr = 0; rr < kQSub; rr += 4) {
-        const int64_t row = row0 + rr;
-        process(b0, row);
-        b0.load(xv, min(row + 4, last), K, blk);
-        __builtin_amdgcn_sched_barrier(0);
-        process(b1, row + 1);
-        b1.load(xv, min(row + 5, last), K, blk);
-        __builtin_amdgcn_sched_barrier(0);
-        process(b2, row + 2);
-        b2.load(xv, min(row + 6, last), K, blk);
-        __builtin_amdgcn_sched_barrier(0);
-        process(b3, row + 3);
-        b3.load(xv, min(row + 7, last), K, blk);
-      }
-    } else {
-#pragma unroll 1
-      for (int rr = 0; rr < nrows; ++rr) {
-        RowBlock<kBF16> rb;
-        rb.load(xv, row0 + rr, K, blk);
-        process(rb, row0 + rr);
-      }
+    for (int rr = 0; rr < nrows; rr += 3) {
+      const int64_t row = row0 + rr;
+      process(b0, row);
+      b0.load(xv, min(row + 3, last), K, blk);
+      __builtin_amdgcn_sched_barrier(0);
+      if (rr + 1 < nrows) process(b1, row + 1);
+      b1.load(xv, min(row + 4, last), K, blk);
+      __builtin_amdgcn_sched_barrier(0);
+      if (rr + 2 < nrows) process(b2, row + 2);
+      b2.load(xv, min(row + 5, last), K, blk);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -418,20 +456,24 @@ __global__ __launch_bounds__(512) void k_quantize(
   if (wave_or_u32(bad) && lane == 0) atomicOr(status, (uint32_t)NVQ_STATUS_NONFINITE);
 }
 
-// score[c] = sum over chunks j ascending of P[j][c] (fp32, sequential).  The
-// partials of a group of 32 chunks are all loaded before the in-order sum.
-__global__ __launch_bounds__(256) void k_score_reduce(const float* __restrict__ partial,
-                                                     int64_t nchunks, int64_t K,
-                                                     float* __restrict__ score) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// score[c] = sum over chunks j ascending of P[j][c] (fp32, sequential).  One
+// column per thread, 64-thread workgroups so the columns spread over many CUs;
+// the partials of a group of 64 chunks are all loaded before the in-order sum.
+constexpr int kScoreThreads = 64;
+constexpr int kScoreBatch = 64;
+__global__ __launch_bounds__(kScoreThreads) void k_score_reduce(const float* __restrict__ partial,
+                                                               int64_t nchunks, int64_t K,
+                                                               float* __restrict__ score) {
+  const int64_t c = (int64_t)blockIdx.x * kScoreThreads + threadIdx.x;
   if (c >= K) return;
   float s = 0.0f;
-  for (int64_t j0 = 0; j0 < nchunks; j0 += 32) {
-    float v[32];
+  for (int64_t j0 = 0; j0 < nchunks; j0 += kScoreBatch) {
+    float v[kScoreBatch];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) v[j] = (j0 + j < nchunks) ? partial[(j0 + j) * K + c] : 0.0f;
+    for (int j = 0; j < kScoreBatch; ++j)
+      v[j] = (j0 + j < nchunks) ? partial[(j0 + j) * K + c] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
+    for (int j = 0; j < kScoreBatch; ++j)
       if (j0 + j < nchunks) s += v[j];
   }
   score[c] = s;
@@ -486,13 +528,20 @@ __global__ __launch_bounds__(512) void k_resid_partials(const void* __restrict__
   }
 }
 
+// Order-preserving map of fp32 bits to uint32 (larger float -> larger key;
+// -0 and +0 map to the same key, so they tie like equal values).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  const uint32_t u = __float_as_uint(f) == 0x80000000u ? 0u : __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Top-k of K scores by (score desc, index asc) with a bitonic sort of 64-bit
-// keys in LDS; one workgroup.  Kp = padded power of two.
+// keys in LDS; one workgroup.  Kp = padded power of two.  Used for k > 1024.
 __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ score, int K, int Kp,
                                               int k, int32_t* __restrict__ idx_out) {
   extern __shared__ uint64_t keys[];
   for (int i = threadIdx.x; i < Kp; i += 1024)
-    keys[i] = (i < K) ? (((uint64_t)__float_as_uint(score[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i))
+    keys[i] = (i < K) ? (((uint64_t)f32_order_key(score[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i))
                       : 0ull;
   __syncthreads();
   for (int size = 2; size <= Kp; size <<= 1) {
@@ -512,6 +561,110 @@ __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ score, 
   }
   for (int j = threadIdx.x; j < k; j += 1024)
     idx_out[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)(keys[j] & 0xFFFFFFFFull));
+}
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkMaxK = 1024;
+
+// Top-k (k <= 1024) of K scores by (score desc, index asc); one workgroup.
+// Radix select on the order keys, 8 bits per pass from the top: each pass
+// histograms the digit of the keys that match the prefix found so far and
+// picks the digit holding the k-th largest key.  The threshold key T ends up
+// exact; every key above T is taken, and of the keys equal to T the needed
+// number with the lowest indices (an index-ordered scan).  The k winners are
+// then put in rank order by counting, for each, the winners with a larger
+// (key, -index).  All loops are bounded by K and k.
+__global__ __launch_bounds__(kTopkThreads) void k_topk_radix(const float* __restrict__ score, int K,
+                                                            int k, int32_t* __restrict__ idx_out) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_bin;     // chosen digit
+  __shared__ uint32_t s_above;   // keys above the chosen digit (within the prefix)
+  __shared__ uint32_t s_cnt;     // winners placed so far
+  __shared__ uint32_t s_wave[kTopkThreads / 64];
+  __shared__ uint64_t sel[kTopkMaxK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  uint32_t prefix = 0, mask = 0, need = (uint32_t)k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < K; i += kTopkThreads) {
+      const uint32_t key = f32_order_key(score[i]);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns digits 4l..4l+3; suffix sums over lanes from the top
+      const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
+                     h3 = hist[4 * lane + 3];
+      const uint32_t own = h0 + h1 + h2 + h3;
+      uint32_t suf = own;  // inclusive suffix sum over lanes >= lane
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_down((int)suf, d, 64);
+        if (lane + d < 64) suf += o;
+      }
+      const uint32_t above = suf - own;  // keys in digits of higher lanes
+      // the k-th largest lies in this lane's digits iff above < need <= suf
+      if (above < need && need <= suf) {
+        uint32_t a = above, dsel = 4 * lane + 3;
+        if (a + h3 < need) {
+          a += h3;
+          dsel = 4 * lane + 2;
+          if (a + h2 < need) {
+            a += h2;
+            dsel = 4 * lane + 1;
+            if (a + h1 < need) {
+              a += h1;
+              dsel = 4 * lane;
+            }
+          }
+        }
+        s_bin = dsel;
+        s_above = a;
+      }
+    }
+    __syncthreads();
+    prefix |= s_bin << shift;
+    mask |= 255u << shift;
+    need -= s_above;
+    __syncthreads();
+  }
+  // prefix = T, the k-th largest key; take all keys > T and the `need`
+  // lowest-index keys == T.  Thread t scans the index range [t*C, t*C + C).
+  const int C = (K + kTopkThreads - 1) / kTopkThreads;
+  const int i0 = min(K, tid * C), i1 = min(K, i0 + C);
+  uint32_t eq = 0;
+  for (int i = i0; i < i1; ++i) eq += f32_order_key(score[i]) == prefix;
+  // exclusive scan of eq over threads (index order)
+  uint32_t inc = eq;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_up((int)inc, d, 64);
+    if (lane >= d) inc += o;
+  }
+  if (tid == 0) s_cnt = 0;
+  if (lane == 63) s_wave[wave] = inc;
+  __syncthreads();
+  uint32_t base = inc - eq;
+  for (int w = 0; w < wave; ++w) base += s_wave[w];
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = f32_order_key(score[i]);
+    bool take = key > prefix;
+    if (key == prefix) take = (base++ < need);
+    if (take) {
+      const uint32_t slot = atomicAdd(&s_cnt, 1u);
+      if (slot < (uint32_t)kTopkMaxK)
+        sel[slot] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+    }
+  }
+  __syncthreads();
+  if (tid < k) {
+    const uint64_t mine = sel[tid];
+    int rank = 0;
+    for (int j = 0; j < k; ++j) rank += sel[j] > mine;
+    idx_out[rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)(mine & 0xFFFFFFFFull));
+  }
 }
 
 // resid[m, j] = bf16(fl32(x[m, idx[j]] - v[m, idx[j]])).
@@ -605,10 +758,14 @@ QuantLayout quant_layout(void* ws, int64_t batch, int64_t rows, int64_t K, int x
 
 int topk_launch(const float* score, int64_t K, int32_t k, int32_t* idx, hipStream_t s) {
   if (k == 0) return NVQ_OK;
+  if (K > INT32_MAX) return NVQ_EUNSUPPORTED;
+  if (k <= kTopkMaxK) {
+    hipLaunchKernelGGL(k_topk_radix, dim3(1), dim3(kTopkThreads), 0, s, score, (int)K, (int)k, idx);
+    return last_launch();
+  }
   int Kp = 1;
   while (Kp < K) Kp <<= 1;
   if (Kp > 8192) return NVQ_EUNSUPPORTED;  // 64 KB of LDS keys
-  if (Kp < 2) Kp = 2;
   hipLaunchKernelGGL(k_topk, dim3(1), dim3(1024), Kp * sizeof(uint64_t), s, score, (int)K, Kp, (int)k,
                      idx);
   return last_launch();
@@ -670,7 +827,8 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
 #undef NVQ_LAUNCH_Q
   if (int rc = last_launch()) return rc;
   if (score) {
-    hipLaunchKernelGGL(k_score_reduce, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_score_reduce, dim3((unsigned)((K + kScoreThreads - 1) / kScoreThreads)),
+                       dim3(kScoreThreads), 0, s,
                        L.chunk_partial, L.nchunks, K, chan_score);
     return last_launch();
   }
@@ -740,7 +898,8 @@ extern "C" int residual_topk_channels(const void* x, int x_dtype, int64_t rows, 
                            scales, tensor_scale, chunk_partial);
       if (int rc = last_launch()) return rc;
     }
-    hipLaunchKernelGGL(k_score_reduce, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_score_reduce, dim3((unsigned)((K + kScoreThreads - 1) / kScoreThreads)),
+                       dim3(kScoreThreads), 0, s,
                        chunk_partial, nchunks, K, dst);
     if (int rc = last_launch()) return rc;
     score = dst;

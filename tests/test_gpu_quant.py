@@ -86,6 +86,19 @@ def test_golden_blocks_and_near_ties():
     _check_quant(inputs.to_bf16_bits(_near_tie_tensor(9)), what="near-ties bf16")
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_scale_midpoints_under_full_mantissa_tensor_scale(seed):
+    """Block maxima on and one ulp around E4M3 midpoints (times 6 s_t) and
+    elements near E2M1 midpoints, with a tensor scale that has a full mantissa
+    (the fma decisions of the fast path), in fp32 and bf16."""
+    from test_oracle_quant import _scale_tie_tensor
+
+    for amax in (1.2345678e3, 3.0e-3, 7.77e-20):
+        x = _scale_tie_tensor(seed, amax)
+        _check_quant(x, k=8, what=f"scale ties {seed} {amax}")
+        _check_quant(inputs.to_bf16_bits(x), what=f"scale ties bf16 {seed} {amax}")
+
+
 def test_extreme_tensor_scales_and_denormals():
     g = np.random.default_rng(11)
     base = g.standard_normal((64, 128)).astype(np.float32)
@@ -152,3 +165,25 @@ def test_repeat_runs_are_bitwise_identical():
     b = [to_np(t) for t in nvq.nvfp4_quantize(x, score=True)[:4]]
     for u, v in zip(a, b):
         assert_bits_equal(u, v, "repeat")
+
+
+@pytest.mark.parametrize("K,k", [(16, 1), (48, 3), (64, 64), (1008, 17), (7168, 64), (7168, 1024),
+                                 (7168, 1025), (4096, 4096), (20000, 128), (100000, 1000)])
+def test_topk_on_given_scores_ties_and_sizes(K, k):
+    """residual_topk_channels on caller scores: heavy exact ties, negative
+    values and both zeros (ties break to the lower index; -0 equals +0).
+    k <= 1024 runs the radix select, larger k the bitonic sort."""
+    import torch
+
+    nvq = _nvq()
+    g = np.random.default_rng(K * 7 + k)
+    sc = g.integers(-3, 12, K).astype(np.float32) * np.float32(0.25)
+    sc[g.random(K) < 0.1] = np.float32(-0.0)
+    sc[g.random(K) < 0.05] = g.standard_normal(int((g.random(K) < 0.05).sum()) or 1)[0]
+    sc[g.random(K) < 0.01] = np.float32(3.0e38)
+    log(f"[topk] K={K} k={k}")
+    x = torch.empty(0, K, dtype=torch.float32, device="cuda")
+    idx, _, _ = nvq.residual_topk_channels(x, None, None, None, k, scores=to_gpu(sc),
+                                           want_resid=False)
+    torch.cuda.synchronize()
+    assert_bits_equal(to_np(idx), oracle.topk(sc, k), f"topk K={K} k={k}")

@@ -143,9 +143,51 @@ def _near_tie_tensor(seed):
     return x
 
 
+def _e4m3_midpoints():
+    """All 126 midpoints between consecutive finite non-negative E4M3 values."""
+    v = np.array([oracle.e4m3_value(c) for c in range(0x7F)], np.float64)
+    return 0.5 * (v[:-1] + v[1:])
+
+
+def _scale_tie_tensor(seed, s_t_amax=1.2345678e3):
+    """A tensor scale with a full mantissa (amax = s_t_amax), block maxima at
+    fl32(6 mid s_t) and one ulp either side of it for random E4M3 midpoints
+    mid (so amax_b / (6 s_t) sits within an ulp or two of the midpoint), and
+    other elements at fl32(m s_b s_t) -+ 1 ulp for E2M1 midpoints m under the
+    scale the block will get."""
+    g = np.random.default_rng(seed)
+    rows, K = 32, 256
+    x = np.zeros((rows, K), np.float32)
+    x[0, 0] = np.float32(s_t_amax)
+    s_t = np.float64(np.float32(np.float64(np.float32(s_t_amax)) / 2688.0))
+    mids = _e4m3_midpoints()
+    emids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for r in range(rows):
+        for b in range(K // 16):
+            if r == 0 and b == 0:
+                continue
+            mid = mids[g.integers(0, mids.size)]
+            am = np.float32(6.0 * mid * s_t)
+            am = [np.nextafter(am, np.float32(0)), am, np.nextafter(am, np.float32(np.inf))][g.integers(0, 3)]
+            blk = np.zeros(16, np.float32)
+            blk[g.integers(0, 16)] = am
+            # the block scale is one of the two codes around mid; elements sit
+            # near E2M1 midpoints under either
+            s_b = np.float64(oracle.e4m3_value(int(np.searchsorted(mids, mid)) + int(g.integers(0, 2))))
+            for j in range(16):
+                if blk[j] != 0:
+                    continue
+                v = np.float32(emids[g.integers(0, 7)] * s_b * s_t)
+                v = [np.nextafter(v, np.float32(0)), v, np.nextafter(v, np.float32(np.inf))][g.integers(0, 3)]
+                blk[j] = min(v, am) * (-1 if g.random() < 0.5 else 1)
+            x[r, 16 * b:16 * b + 16] = blk
+    return x
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_threshold_form_agrees_with_search(seed):
-    for x in (_random_tensor(seed), _random_tensor(seed, dtype="bf16"), _near_tie_tensor(seed)):
+    for x in (_random_tensor(seed), _random_tensor(seed, dtype="bf16"), _near_tie_tensor(seed),
+              _scale_tie_tensor(seed), _scale_tie_tensor(seed, 3.0e-3)):
         a = oracle.quantize(x)
         b = oracle.quantize(x, threshold_form=True)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
