@@ -345,6 +345,8 @@ def main():
     os.environ.setdefault("ORACLE_THREADS", "16")
     legs = []
     wanted = args.legs.split(",")
+    if "quant" not in wanted:
+        wanted.append("quant")  # the headline value is the quantizer's
     if "quant" in wanted:
         legs.append(QuantLeg())
     if "copy" in wanted:

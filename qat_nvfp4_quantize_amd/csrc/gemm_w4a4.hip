@@ -17,18 +17,26 @@
 // runs as extra bf16 MFMA steps into the same accumulators between the
 // s_tA and s_tW scalings.
 //
-// Tiling: workgroup = 2 waves = 128 rows x 256 columns; wave = 128 x 128
-// (4 x 4 MFMA 32x32 tiles, accumulators in AGPRs); K staged through LDS in
-// 128-element steps, double buffered: FP4 codes and raw E4M3 scale bytes only
-// (4.5 bits/element), never dequantized 16-bit tiles.  A rows are gathered
-// through a_row (token index).  Within a 128-element K step, lane half h owns
-// elements [64h, 64h + 64) and MFMA step s takes elements 64h + 8s .. +8 from
-// each half: any fixed K assignment works because A and B share it and every
-// element carries its own block scale into the fragment.
+// Tiling: workgroup = 4 waves = 128 rows x 256 columns, two workgroups per
+// CU (each wave keeps its 128 x 64 accumulators in VGPRs, at most 256
+// registers, so two waves share a SIMD and one covers the other's barrier
+// and memory waits).  K advances 128 elements per step.  The A tile (128
+// rows, shared by the four waves) is dequantized once per workgroup to exact
+// fp16 into a double-buffered LDS tile (272-byte rows: the 16-byte fragment
+// reads of consecutive rows hit distinct banks).  Each wave's 64 weight rows
+// are used by that wave only, so they skip LDS: they are loaded straight into
+// registers in MFMA fragment order, two steps ahead, and dequantized there.
+// Within a 128-element step, lane half h owns elements [64h, 64h + 64) and
+// MFMA sub-step d takes its elements 64h + 8d .. +8: any fixed K assignment
+// works because A and B share it and every element carries its own block
+// scale into the fragment.  A rows are gathered through a_row (token index).
+// The compensation runs as extra bf16 steps of 128 channels through the same
+// LDS tile (residual columns) and registers (packed weight columns).
 //
-// Workgroups map to tiles XCD-aware: consecutive logical tiles (same expert
-// and column tile, consecutive row tiles) share their weight tile and land on
-// the same XCD, so the second and third readers hit that XCD's L2.
+// Workgroups map to tiles XCD-aware: each XCD walks a contiguous range of
+// logical tiles, ordered by groups of 4 row tiles, then column tile, then row
+// tile within the group, so the workgroups resident on one XCD share a few
+// A and B tiles in that XCD's L2.
 
 #include <hip/hip_runtime.h>
 
@@ -46,12 +54,12 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
+constexpr int NTHR = 256;     // threads per workgroup (4 waves)
 constexpr int BM = 128;       // rows per workgroup
-constexpr int BN = 256;       // columns per workgroup (2 waves x 128)
-constexpr int BK = 128;       // K elements per LDS stage
-constexpr int NTHR = 128;     // threads per workgroup
-constexpr int KQ = BK / 32;   // 16-byte code chunks per row per stage (4)
-constexpr int KB = BK / 16;   // scale bytes per row per stage (8)
+constexpr int BN = 256;       // columns per workgroup (4 waves x 64)
+constexpr int WN = 64;        // columns per wave
+constexpr int SE = 128;       // K elements per step
+constexpr int LROW = 272;     // LDS bytes per A tile row (256 data + 16 pad)
 
 struct GemmParams {
   int64_t rows, K, N, E, a_rows;
@@ -76,10 +84,11 @@ struct GemmParams {
   int max_tiles;
   int n_tiles_n;
   int swiglu;             // 1: gate/up fused weight, epilogue h = silu(gate) * up
+  int bm;                 // row tile of the tile table
 };
 
 // Tile table: expert e's rows [off[e], off[e+1]) split into BM-row tiles.
-__global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__ off, int E,
+__global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__ off, int E, int BM,
                                                     int32_t* __restrict__ tiles,
                                                     int32_t* __restrict__ ntiles, int max_tiles) {
   __shared__ int32_t s_first[1025];
@@ -110,20 +119,28 @@ __device__ __forceinline__ int64_t a_source_row(const GemmParams& p, int64_t pr)
   return p.a_row_div > 0 ? v / p.a_row_div : v;
 }
 
-// Weight row (column n of Y) held at local B row r of a workgroup.  With the
-// SwiGLU epilogue each wave holds 64 gate rows then the 64 matching up rows.
+// Weight row (column n of Y) held at local B row r (0..255) of column tile
+// nt.  With the SwiGLU epilogue each wave's 64 rows are 32 gate rows then the
+// 32 matching up rows, so a lane holds gate and up of the same column.
 __device__ __forceinline__ int64_t b_row_to_n(int r, int nt, int swiglu, int64_t N) {
   if (!swiglu) return (int64_t)nt * BN + r;
-  const int w = r >> 7, q = r & 127;
+  const int w = r >> 6, q = r & 63;
   const int64_t I = N >> 1;
-  const int64_t g0 = (int64_t)nt * (BN / 2) + 64 * w;
-  return (q < 64) ? g0 + q : I + g0 + (q - 64);
+  const int64_t g0 = (int64_t)nt * (BN / 2) + 32 * w;
+  return (q < 32) ? g0 + q : I + g0 + (q - 32);
 }
 
-// 8 FP4 codes (one dword) times one E4M3 scale -> 8 exact fp16 values.
-__device__ __forceinline__ half8_t dequant8(uint32_t w, uint32_t sc2) {
+// E4M3 code byte b (0..3) of a dword -> fp16x2 pattern (code << 7) in both
+// halves, i.e. s_b * 2^-8 twice.
+__device__ __forceinline__ uint32_t scale_pair(uint32_t four, int b) {
+  const uint32_t sel = (uint32_t)b | (0x0Cu << 8) | ((uint32_t)b << 16) | (0x0Cu << 24);
+  return __builtin_amdgcn_perm(0u, four, sel) << 7;
+}
+
+// 8 FP4 codes (one dword) times the fp16x2 scale pattern -> 8 exact fp16 values.
+__device__ __forceinline__ half8_t dequant8(uint32_t w, uint32_t pat) {
   half2_t s;
-  __builtin_memcpy(&s, &sc2, 4);
+  __builtin_memcpy(&s, &pat, 4);
   const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s;
   const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s;
   const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s;
@@ -134,11 +151,9 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, uint32_t sc2) {
   return r;
 }
 
-// E4M3 code byte b (0..3) of a dword -> fp16x2 pattern (code << 7) in both
-// halves, i.e. s_b * 2^-8 twice.
-__device__ __forceinline__ uint32_t scale_pair(uint32_t four, int b) {
-  const uint32_t sel = (uint32_t)b | (0x0Cu << 8) | ((uint32_t)b << 16) | (0x0Cu << 24);
-  return __builtin_amdgcn_perm(0u, four, sel) << 7;
+__device__ __forceinline__ uint32_t dword_of(const uint4 (&c)[2], int d) {
+  const uint4& v = c[d >> 2];
+  return (d & 3) == 0 ? v.x : (d & 3) == 1 ? v.y : (d & 3) == 2 ? v.z : v.w;
 }
 
 // bf16 bits of the exact dequantized weight value G * s_b (<= 6 significant bits).
@@ -167,19 +182,27 @@ __global__ __launch_bounds__(256) void k_gather_wcomp(const uint8_t* __restrict_
 }
 
 template <int kSwiglu>
-__global__ __launch_bounds__(NTHR) void k_moe_gemm_deq16(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][KQ][BM][16];
-  __shared__ __attribute__((aligned(16))) uint8_t sAs[2][BM][KB];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][KQ][BN][16];
-  __shared__ __attribute__((aligned(16))) uint8_t sBs[2][BN][KB];
+__global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM][LROW];
 
-  // XCD-aware tile order (the grid is a multiple of 8 workgroups).
-  const int G = gridDim.x;
-  const int per = G >> 3;
-  const int logical = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  const int mt = logical % p.max_tiles;
-  const int nt = logical / p.max_tiles;
-  if (nt >= p.n_tiles_n || mt >= *p.ntiles) return;
+  // XCD-aware tile order.  The grid is sized for the most row tiles the
+  // offsets allow; the real count comes from the tile table.  Workgroups are
+  // dealt to the 8 XCDs round-robin, so XCD x = blockIdx % 8 takes the
+  // contiguous logical range [x * per, (x + 1) * per) of the real tiles, in
+  // groups of 4 row tiles x all column tiles; the surplus workgroups exit.
+  const int n_mt = min(*p.ntiles, p.max_tiles);
+  const int n_groups = (n_mt + 3) / 4;
+  const int total = n_groups * 4 * p.n_tiles_n;
+  const int per = (total + 7) / 8;
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per) return;
+  const int logical = (blockIdx.x & 7) * per + slot;
+  if (logical >= total) return;
+  const int group_span = 4 * p.n_tiles_n;
+  const int grp = logical / group_span, rem = logical - grp * group_span;
+  const int mt = 4 * grp + (rem & 3);
+  const int nt = rem >> 2;
+  if (mt >= n_mt) return;
   const int e = p.tiles[2 * mt];
   const int64_t row0 = p.tiles[2 * mt + 1];
   const int64_t row_end = p.off[e + 1];
@@ -190,130 +213,102 @@ __global__ __launch_bounds__(NTHR) void k_moe_gemm_deq16(GemmParams p) {
   const int wave = t >> 6, lane = t & 63;
   const int l32 = lane & 31, h = lane >> 5;
 
-  // ---- loader state: each thread stages 4 A chunks, 8 B chunks, 1 A and 2 B scale rows
-  const uint8_t* a_src[4];
-  bool a_ok[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = (t >> 2) + 32 * u;
-    const int64_t pr = row0 + r;
-    a_ok[u] = pr < row_end;
-    const int64_t ar = a_ok[u] ? a_source_row(p, pr) : 0;
-    a_src[u] = p.a_codes + ar * Kh + (t & 3) * 16;
-  }
-  const uint8_t* as_src;
-  bool as_ok;
-  {
-    const int64_t pr = row0 + t;
-    as_ok = pr < row_end;
-    const int64_t ar = as_ok ? a_source_row(p, pr) : 0;
-    as_src = p.a_scales + ar * Kb;
-  }
+  // A loader: row ar = t / 2, lane half ahh = t % 2 (elements [64 ahh, 64 ahh
+  // + 64) of each step).  B: fragment j = local row 64 wave + 32 j + l32, lane
+  // half h.  Rows past the expert's end or past N read a clamped valid row:
+  // FP4 values are always finite and those outputs are never stored, so every
+  // load is issued unconditionally and needs no mask.
+  const int ar = t >> 1, ahh = t & 1;
+  const int64_t a_tok = a_source_row(p, min<int64_t>(row0 + ar, row_end - 1));
+  const uint8_t* a_src = p.a_codes + a_tok * Kh + 32 * ahh;
+  const uint8_t* a_ssrc = p.a_scales + a_tok * Kb + 4 * ahh;
   const uint8_t* wcodes_e = p.w_codes + (int64_t)e * N * Kh;
   const uint8_t* wscales_e = p.w_scales + (int64_t)e * N * Kb;
-  const uint8_t* b_src[8];
-  bool b_ok[8];
+  const uint8_t* b_src[2];
+  const uint8_t* b_ssrc[2];
+  int64_t b_n[2];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int r = (t >> 2) + 32 * u;
-    const int64_t n = b_row_to_n(r, nt, kSwiglu, N);
-    b_ok[u] = n < N;
-    b_src[u] = wcodes_e + (b_ok[u] ? n : 0) * Kh + (t & 3) * 16;
-  }
-  const uint8_t* bs_src[2];
-  bool bs_ok[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int64_t n = b_row_to_n(t + 128 * u, nt, kSwiglu, N);
-    bs_ok[u] = n < N;
-    bs_src[u] = wscales_e + (bs_ok[u] ? n : 0) * Kb;
+  for (int j = 0; j < 2; ++j) {
+    b_n[j] = min<int64_t>(b_row_to_n(WN * wave + 32 * j + l32, nt, kSwiglu, N), N - 1);
+    b_src[j] = wcodes_e + b_n[j] * Kh + 32 * h;
+    b_ssrc[j] = wscales_e + b_n[j] * Kb + 4 * h;
   }
 
-  uint4 ra[4], rb[8];
-  uint2 ras, rbs[2];
-  auto gload = [&](int kstep) {
-    const int64_t kc = (int64_t)kstep * (BK / 2), ks = (int64_t)kstep * KB;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      ra[u] = a_ok[u] ? *reinterpret_cast<const uint4*>(a_src[u] + kc) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      rb[u] = b_ok[u] ? *reinterpret_cast<const uint4*>(b_src[u] + kc) : make_uint4(0, 0, 0, 0);
-    ras = as_ok ? *reinterpret_cast<const uint2*>(as_src + ks) : make_uint2(0, 0);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      rbs[u] = bs_ok[u] ? *reinterpret_cast<const uint2*>(bs_src[u] + ks) : make_uint2(0, 0);
+  struct Stage {
+    uint4 a[2];
+    uint32_t as;
+    uint4 b[2][2];
+    uint32_t bs[2];
   };
-  auto lstore = [&](int buf) {
+  const int nst = (int)(K / SE);
+  auto gload = [&](Stage& S, int step) {
+    const int64_t sc = min(step, nst - 1);  // past the end: a valid step, zero-scaled later
+    S.a[0] = *reinterpret_cast<const uint4*>(a_src + sc * 64);
+    S.a[1] = *reinterpret_cast<const uint4*>(a_src + sc * 64 + 16);
+    S.as = *reinterpret_cast<const uint32_t*>(a_ssrc + sc * 8);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      *reinterpret_cast<uint4*>(&sA[buf][t & 3][(t >> 2) + 32 * u][0]) = ra[u];
+    for (int j = 0; j < 2; ++j) {
+      S.b[j][0] = *reinterpret_cast<const uint4*>(b_src[j] + sc * 64);
+      S.b[j][1] = *reinterpret_cast<const uint4*>(b_src[j] + sc * 64 + 16);
+      S.bs[j] = *reinterpret_cast<const uint32_t*>(b_ssrc[j] + sc * 8);
+    }
+  };
+  // This thread's 64 A elements of a step -> exact fp16 at LDS row ar, bytes
+  // [128 ahh, 128 ahh + 128).  live == false (a step past K) writes zeros.
+  auto a_store = [&](const Stage& S, int buf, bool live) {
+    uint8_t* dst = &lds[buf][ar][128 * ahh];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      *reinterpret_cast<uint4*>(&sB[buf][t & 3][(t >> 2) + 32 * u][0]) = rb[u];
-    *reinterpret_cast<uint2*>(&sAs[buf][t][0]) = ras;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) *reinterpret_cast<uint2*>(&sBs[buf][t + 128 * u][0]) = rbs[u];
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t pat = live ? scale_pair(S.as, d >> 1) : 0u;
+      *reinterpret_cast<half8_t*>(dst + 16 * d) = dequant8(dword_of(S.a, d), pat);
+    }
   };
 
-  floatx16_t acc[4][4];
+  floatx16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int nk = (int)(K / BK);
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) gload(ks + 1);
-    // scale bytes of this lane's 4 blocks (lane half h owns blocks 4h .. 4h+3)
-    uint32_t asc[4], bsc[4];
+  // one step: 8 sub-steps; A fragments from LDS (rows 32 i + l32, bytes
+  // 128 h + 16 d), B fragments dequantized from registers (dword d).
+  auto mfma_step = [&](const Stage& S, int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      asc[i] = *reinterpret_cast<const uint32_t*>(&sAs[buf][32 * i + l32][4 * h]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bsc[j] = *reinterpret_cast<const uint32_t*>(&sBs[buf][128 * wave + 32 * j + l32][4 * h]);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint4 ac[4], bc[4];
+    for (int d = 0; d < 8; ++d) {
+      half8_t af[4], bf[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        ac[i] = *reinterpret_cast<const uint4*>(&sA[buf][2 * h + half][32 * i + l32][0]);
+        af[i] = *reinterpret_cast<const half8_t*>(&lds[buf][32 * i + l32][128 * h + 16 * d]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bc[j] = *reinterpret_cast<const uint4*>(&sB[buf][2 * h + half][128 * wave + 32 * j + l32][0]);
+      for (int j = 0; j < 2; ++j) bf[j] = dequant8(dword_of(S.b[j], d), scale_pair(S.bs[j], d >> 1));
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int sb = 2 * half + (s >> 1);  // block within this lane half's 4
-        half8_t af[4], bf[4];
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = s == 0 ? ac[i].x : s == 1 ? ac[i].y : s == 2 ? ac[i].z : ac[i].w;
-          af[i] = dequant8(w, scale_pair(asc[i], sb));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w = s == 0 ? bc[j].x : s == 1 ? bc[j].y : s == 2 ? bc[j].z : bc[j].w;
-          bf[j] = dequant8(w, scale_pair(bsc[j], sb));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      }
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (ks + 1 < nk) {
-      __syncthreads();  // everyone is done reading buf ^ 1 from the previous step
-      lstore(buf ^ 1);
-      __syncthreads();
-    }
+  };
+
+  // Pipeline: while the waves run the MFMAs of step s from LDS buffer s & 1,
+  // step s + 1 (in registers) is dequantized into the other buffer; each
+  // register stage is loaded two steps before its MFMAs.  The loop covers
+  // step pairs; an odd step count adds one zero-scaled step.
+  Stage X0, X1;
+  gload(X0, 0);
+  gload(X1, 1);
+  a_store(X0, 0, true);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    mfma_step(X0, 0);
+    a_store(X1, 1, st + 1 < nst);
+    __syncthreads();
+    gload(X0, st + 2);
+    mfma_step(X1, 1);
+    a_store(X0, 0, st + 2 < nst);
+    __syncthreads();
+    gload(X1, st + 3);
   }
 
   // ---- s_tA, then the compensation steps, then s_tW
@@ -321,54 +316,52 @@ __global__ __launch_bounds__(NTHR) void k_moe_gemm_deq16(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] *= sta;
 
   if (p.k > 0) {
-    const int nsteps = (p.k + 15) / 16;
-    int64_t arow_i[4];
-    bool arow_ok[4];
+    // residual row of this thread's A row (stride k); packed weight columns
+    // of each B fragment (stride kpad).  Channels past k (kpad) read as zero.
+    const uint16_t* r_src = p.a_resid + a_tok * p.k;
+    const uint16_t* w_src[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t pr = row0 + 32 * i + l32;
-      arow_ok[i] = pr < row_end;
-      arow_i[i] = arow_ok[i] ? a_source_row(p, pr) : 0;
-    }
-    const uint16_t* wrow[4];
-    bool wok[4];
+    for (int j = 0; j < 2; ++j) w_src[j] = p.wcomp + ((int64_t)e * N + b_n[j]) * p.kpad;
+    const int ncs = (p.k + SE - 1) / SE;
+    for (int cs = 0; cs < ncs; ++cs) {
+      const int c0 = SE * cs + 64 * ahh;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = b_row_to_n(128 * wave + 32 * j + l32, nt, kSwiglu, N);
-      wok[j] = n < N;
-      wrow[j] = p.wcomp + ((int64_t)e * N + (wok[j] ? n : 0)) * p.kpad;
-    }
-    for (int st = 0; st < nsteps; ++st) {
-      const int c0 = 16 * st + 8 * h;  // this lane's 8 compensation channels (k % 8 == 0)
-      bf16x8_t af[4], bf[4];
-      const bool cin = c0 < p.k;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (arow_ok[i] && cin) v = *reinterpret_cast<const uint4*>(p.a_resid + arow_i[i] * p.k + c0);
-        __builtin_memcpy(&af[i], &v, 16);
+      for (int q = 0; q < 8; ++q) {
+        const int c = c0 + 8 * q;  // 8 channels (16 bytes); k % 8 == 0
+        const uint4 v = c < p.k ? *reinterpret_cast<const uint4*>(r_src + c) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(&lds[0][ar][128 * ahh + 16 * q]) = v;
       }
+      __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (wok[j]) v = *reinterpret_cast<const uint4*>(wrow[j] + c0);
-        __builtin_memcpy(&bf[j], &v, 16);
+      for (int d = 0; d < 8; ++d) {
+        bf16x8_t af[4], bf[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[i] = *reinterpret_cast<const bf16x8_t*>(&lds[0][32 * i + l32][128 * h + 16 * d]);
+        const int cb = SE * cs + 64 * h + 8 * d;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint4 v = cb < p.kpad ? *reinterpret_cast<const uint4*>(w_src[j] + cb) : make_uint4(0, 0, 0, 0);
+          __builtin_memcpy(&bf[j], &v, 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      __syncthreads();
     }
   }
 
   const float stw = p.w_st[e];
-  // ---- epilogue.  acc[i][j][v]: row 32i + 8(v/4) + 4h + v%4, column 32j + l32 of the wave tile.
+  // ---- epilogue.  acc[i][j][v]: row 32i + 8(v/4) + 4h + v%4, local column
+  // 64 wave + 32 j + l32.
   if (!kSwiglu) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -377,8 +370,8 @@ __global__ __launch_bounds__(NTHR) void k_moe_gemm_deq16(GemmParams p) {
         const int64_t pr = row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
         if (pr >= row_end) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t n = (int64_t)nt * BN + 128 * wave + 32 * j + l32;
+        for (int j = 0; j < 2; ++j) {
+          const int64_t n = (int64_t)nt * BN + WN * wave + 32 * j + l32;
           if (n >= N) continue;
           const float y = acc[i][j][v] * stw;
           if (p.out_f32) p.out_f32[pr * N + n] = y;
@@ -387,18 +380,16 @@ __global__ __launch_bounds__(NTHR) void k_moe_gemm_deq16(GemmParams p) {
       }
   } else {
     const int64_t I = N >> 1;
+    const int64_t ng = (int64_t)nt * (BN / 2) + 32 * wave + l32;
+    if (ng < I) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t pr = row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (pr >= row_end) continue;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t ng = (int64_t)nt * (BN / 2) + 64 * wave + 32 * j + l32;
-          if (ng >= I) continue;
-          const float g = acc[i][j][v] * stw;
-          const float u = acc[i][j + 2][v] * stw;
+        for (int v = 0; v < 16; ++v) {
+          const int64_t pr = row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (pr >= row_end) continue;
+          const float g = acc[i][0][v] * stw;
+          const float u = acc[i][1][v] * stw;
           if (p.out_f32) {
             p.out_f32[pr * N + ng] = g;
             p.out_f32[pr * N + I + ng] = u;
@@ -406,7 +397,7 @@ __global__ __launch_bounds__(NTHR) void k_moe_gemm_deq16(GemmParams p) {
           const float hv = g / (1.0f + __expf(-g)) * u;
           if (p.out_bf16) p.out_bf16[pr * I + ng] = (uint16_t)f32_to_bf16_rne(hv);
         }
-      }
+    }
   }
 }
 
@@ -452,7 +443,7 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
     return NVQ_EINVAL;
   if (a->path == NVQ_GEMM_FP8_BLOCK) return NVQ_EUNSUPPORTED;
   if (a->rows < 0 || a->E < 1 || a->E > 1024 || a->N <= 0 || a->K <= 0) return NVQ_ESHAPE;
-  if (a->K % BK != 0) return NVQ_ESHAPE;  // the FP4 stage is 128 elements of K
+  if (a->K % 128 != 0) return NVQ_ESHAPE;  // K steps of 32 elements; 128 keeps rows 64-byte aligned
   if (a->epilogue == NVQ_EPI_SWIGLU && (a->N % 2 != 0)) return NVQ_ESHAPE;
   if (a->k < 0 || a->k > a->K || (a->k & 7)) return NVQ_ESHAPE;
   if (a->k > 0 && (!a->a_resid || !a->comp_idx)) return NVQ_EINVAL;
@@ -466,7 +457,7 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   if (a->ws_bytes < L.bytes) return NVQ_EWORKSPACE;
   if (a->rows == 0) return NVQ_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, a->expert_offsets, (int)a->E, L.tiles,
+  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, a->expert_offsets, (int)a->E, BM, L.tiles,
                      L.ntiles, L.max_tiles);
   if (int rc = last_launch()) return rc;
   GemmParams p;
@@ -486,8 +477,10 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   p.tiles = L.tiles; p.ntiles = L.ntiles; p.max_tiles = L.max_tiles;
   const bool swiglu = a->epilogue == NVQ_EPI_SWIGLU;
   p.swiglu = swiglu ? 1 : 0;
+  p.bm = BM;
   p.n_tiles_n = swiglu ? (int)((a->N / 2 + BN / 2 - 1) / (BN / 2)) : (int)((a->N + BN - 1) / BN);
-  const int64_t G0 = (int64_t)L.max_tiles * p.n_tiles_n;
+  const int n_groups = (L.max_tiles + 3) / 4;
+  const int64_t G0 = (int64_t)n_groups * 4 * p.n_tiles_n;
   const int64_t G = (G0 + 7) / 8 * 8;
   if (swiglu)
     hipLaunchKernelGGL(k_moe_gemm_deq16<1>, dim3((unsigned)G), dim3(NTHR), 0, s, p);

@@ -565,6 +565,7 @@ __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ score, 
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkMaxK = 1024;
+constexpr int kTopkRegs = 8;  // keys per thread held in registers when K <= 8192
 
 // Top-k (k <= 1024) of K scores by (score desc, index asc); one workgroup.
 // Radix select on the order keys, 8 bits per pass from the top: each pass
@@ -573,7 +574,10 @@ constexpr int kTopkMaxK = 1024;
 // exact; every key above T is taken, and of the keys equal to T the needed
 // number with the lowest indices (an index-ordered scan).  The k winners are
 // then put in rank order by counting, for each, the winners with a larger
-// (key, -index).  All loops are bounded by K and k.
+// (key, -index).  Thread t owns the contiguous index range [t C, t C + C);
+// with kRegs its keys stay in registers (C <= 8), else every pass re-reads
+// the scores.  All loops are bounded by K and k.
+template <bool kRegs>
 __global__ __launch_bounds__(kTopkThreads) void k_topk_radix(const float* __restrict__ score, int K,
                                                             int k, int32_t* __restrict__ idx_out) {
   __shared__ uint32_t hist[256];
@@ -583,14 +587,36 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_radix(const float* __rest
   __shared__ uint32_t s_wave[kTopkThreads / 64];
   __shared__ uint64_t sel[kTopkMaxK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int C = (K + kTopkThreads - 1) / kTopkThreads;
+  const int i0 = min(K, tid * C), i1 = min(K, i0 + C);
+  uint32_t kr[kRegs ? kTopkRegs : 1];
+  if (kRegs) {
+#pragma unroll
+    for (int j = 0; j < kTopkRegs; ++j) kr[j] = (i0 + j < i1) ? f32_order_key(score[i0 + j]) : 0u;
+  }
+  auto key_at = [&](int j) -> uint32_t {  // j-th key of this thread's range
+    if (kRegs) {
+      uint32_t v = kr[0];
+#pragma unroll
+      for (int t = 1; t < kTopkRegs; ++t) v = (j == t) ? kr[t] : v;
+      return v;
+    }
+    return f32_order_key(score[i0 + j]);
+  };
 
   uint32_t prefix = 0, mask = 0, need = (uint32_t)k;
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < K; i += kTopkThreads) {
-      const uint32_t key = f32_order_key(score[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    if (kRegs) {
+#pragma unroll
+      for (int j = 0; j < kTopkRegs; ++j)
+        if (i0 + j < i1 && (kr[j] & mask) == prefix) atomicAdd(&hist[(kr[j] >> shift) & 255u], 1u);
+    } else {
+      for (int j = 0; j < i1 - i0; ++j) {
+        const uint32_t key = key_at(j);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
     if (wave == 0) {
@@ -631,12 +657,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_radix(const float* __rest
     __syncthreads();
   }
   // prefix = T, the k-th largest key; take all keys > T and the `need`
-  // lowest-index keys == T.  Thread t scans the index range [t*C, t*C + C).
-  const int C = (K + kTopkThreads - 1) / kTopkThreads;
-  const int i0 = min(K, tid * C), i1 = min(K, i0 + C);
+  // lowest-index keys == T, by an exclusive scan of the equal counts in
+  // index order.
   uint32_t eq = 0;
-  for (int i = i0; i < i1; ++i) eq += f32_order_key(score[i]) == prefix;
-  // exclusive scan of eq over threads (index order)
+  if (kRegs) {
+#pragma unroll
+    for (int j = 0; j < kTopkRegs; ++j) eq += (i0 + j < i1 && kr[j] == prefix) ? 1u : 0u;
+  } else {
+    for (int j = 0; j < i1 - i0; ++j) eq += key_at(j) == prefix;
+  }
   uint32_t inc = eq;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -648,8 +677,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_radix(const float* __rest
   __syncthreads();
   uint32_t base = inc - eq;
   for (int w = 0; w < wave; ++w) base += s_wave[w];
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = f32_order_key(score[i]);
+  auto place = [&](uint32_t key, int i) {
     bool take = key > prefix;
     if (key == prefix) take = (base++ < need);
     if (take) {
@@ -657,6 +685,13 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_radix(const float* __rest
       if (slot < (uint32_t)kTopkMaxK)
         sel[slot] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
     }
+  };
+  if (kRegs) {
+#pragma unroll
+    for (int j = 0; j < kTopkRegs; ++j)
+      if (i0 + j < i1) place(kr[j], i0 + j);
+  } else {
+    for (int j = 0; j < i1 - i0; ++j) place(key_at(j), i0 + j);
   }
   __syncthreads();
   if (tid < k) {
@@ -760,7 +795,12 @@ int topk_launch(const float* score, int64_t K, int32_t k, int32_t* idx, hipStrea
   if (k == 0) return NVQ_OK;
   if (K > INT32_MAX) return NVQ_EUNSUPPORTED;
   if (k <= kTopkMaxK) {
-    hipLaunchKernelGGL(k_topk_radix, dim3(1), dim3(kTopkThreads), 0, s, score, (int)K, (int)k, idx);
+    if (K <= (int64_t)kTopkThreads * kTopkRegs)
+      hipLaunchKernelGGL(k_topk_radix<true>, dim3(1), dim3(kTopkThreads), 0, s, score, (int)K, (int)k,
+                         idx);
+    else
+      hipLaunchKernelGGL(k_topk_radix<false>, dim3(1), dim3(kTopkThreads), 0, s, score, (int)K, (int)k,
+                         idx);
     return last_launch();
   }
   int Kp = 1;
