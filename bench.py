@@ -179,17 +179,19 @@ class MoeLeg:
         self.flops_dn = 2.0 * P * I * H
         self.flops_comp = 2.0 * P * k * 2 * I + 2.0 * P * k * H
 
-    def gemm(self, proj, a, rows, a_row, resid, idx, out, epi, comp=True):
+    def gemm(self, proj, a, rows, a_row, resid, idx, out, epi, comp=True, path=0):
         nvq = self.nvq
         codes, scales, st = self.qw[proj]
         return nvq.moe_grouped_gemm_w4a4_comp(
             a[0], a[1], a[2], codes, scales, st, self.off, rows=rows, a_row=a_row,
             a_resid=resid if comp else None, comp_idx=idx if comp else None, epilogue=epi,
-            ws=self.ws_g, a_row_div=self.s.topk if a_row is not None else 0, out=out)
+            ws=self.ws_g, a_row_div=self.s.topk if a_row is not None else 0, out=out, path=path)
 
-    def step(self, timer_, comp=True):
+    def step(self, timer_, comp=True, path=0):
+        """path 0: the library's choice (exact fp16 dequantization); 2: the
+        FP8 block-product path, timed separately for the comparison."""
         nvq, s = self.nvq, self.s
-        tag = "" if comp else "_k0"
+        tag = ("" if comp else "_k0") + ("_fp8blk" if path == nvq.NVQ_GEMM_FP8_BLOCK else "")
         timer = lambda label, fn: timer_(self.name + "/" + label, fn)
         r = timer("route", lambda: nvq.nvq_moe_route(self.logits, s.topk))
         self.ids, self.w = r
@@ -198,12 +200,12 @@ class MoeLeg:
         idx1, r1, _ = timer("topk_x", lambda: nvq.residual_topk_channels(
             self.x, self.qx[0], self.qx[1], self.qx[2], s.k, scores=self.qx[3], ws=self.ws_t1))
         timer("gemm_gu" + tag, lambda: self.gemm("gu", self.qx, s.P, self.sp, r1, idx1, (self.h, None),
-                                                  nvq.NVQ_EPI_SWIGLU, comp))
+                                                  nvq.NVQ_EPI_SWIGLU, comp, path))
         timer("quant_h", lambda: nvq.nvfp4_quantize(self.h, score=True, ws=self.ws_q2, out=self.qh))
         idx2, r2, _ = timer("topk_h", lambda: nvq.residual_topk_channels(
             self.h, self.qh[0], self.qh[1], self.qh[2], s.k, scores=self.qh[3], ws=self.ws_t2))
         timer("gemm_dn" + tag, lambda: self.gemm("dn", self.qh, s.P, None, r2, idx2, (self.y2, None),
-                                                  nvq.NVQ_EPI_NONE, comp))
+                                                  nvq.NVQ_EPI_NONE, comp, path))
         timer("combine", lambda: nvq.nvq_moe_combine(self.y2, self.pos, self.w))
 
     def report(self, timer_):
@@ -231,6 +233,13 @@ class MoeLeg:
         if "gemm_gu_k0" in timer.total:
             k0 = timer.avg_ms("gemm_gu_k0") + timer.avg_ms("gemm_dn_k0")
             out["comp_overhead_vs_k0"] = round((gu + dn) / k0 - 1.0, 4)
+        if "gemm_gu_fp8blk" in timer.total:
+            g8, d8 = timer.avg_ms("gemm_gu_fp8blk"), timer.avg_ms("gemm_dn_fp8blk")
+            tf8 = (self.flops_gu + self.flops_dn) / ((g8 + d8) * 1e-3) / 1e12
+            out["path_fp8_block"] = {"gemm_gu_ms": round(g8, 4), "gemm_dn_ms": round(d8, 4),
+                                     "gemm_tflops": round(tf8, 1),
+                                     "frac_fp8_mfma_peak": round(tf8 / FP8_PEAK_TFLOPS, 4),
+                                     "time_vs_chosen_path": round((g8 + d8) / (gu + dn), 3)}
         return out
 
 
@@ -375,10 +384,15 @@ def main():
     ms_step = wall * 1e3 / args.steps
     # k = 0 reference runs of the MoE legs (outside the timed steps): the
     # compensation overhead is the GEMM time at k > 0 over the time at k = 0
+    # and the FP8 block-product path, the evaluated alternative to exact fp16
+    # dequantization, on the same layers
+    from qat_nvfp4_quantize_amd import nvq as _nvq
     for leg in legs:
         if leg.name.startswith("moe"):
             for _ in range(2):
                 leg.step(timer, comp=False)
+            for _ in range(2):
+                leg.step(timer, path=_nvq.NVQ_GEMM_FP8_BLOCK)
     timer.collect()
 
     q = next(l for l in legs if l.name == "quant")

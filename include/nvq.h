@@ -159,9 +159,11 @@ int nvq_moe_combine(const uint16_t* y, const int32_t* pos, const float* weights,
  * Epilogue NVQ_EPI_NONE writes Y (bf16 [rows, N] and/or fp32 [rows, N]);
  * NVQ_EPI_SWIGLU writes h = bf16(silu(Y[:, :N/2]) * Y[:, N/2:]) [rows, N/2]
  * (out_f32, if given, still receives the full pre-activation Y).
- * Path NVQ_GEMM_DEQ16 dequantizes each NVFP4 tile exactly to 16-bit floats and
- * feeds 16-bit MFMA; NVQ_GEMM_FP8_BLOCK runs one FP8 MFMA per 16-block and
- * applies both block scales in fp32 (evaluated alternative). */
+ * Path NVQ_GEMM_DEQ16 (what NVQ_GEMM_AUTO selects) dequantizes each NVFP4 tile
+ * exactly to fp16 and feeds fp16 MFMA; NVQ_GEMM_FP8_BLOCK runs one FP8 MFMA per
+ * 16-element block on the raw E2M1 magnitudes and applies both block scales to
+ * the block product in fp32 (the evaluated alternative; same result to
+ * rounding, slower).  K % 128 == 0; k % 8 == 0. */
 enum { NVQ_EPI_NONE = 0, NVQ_EPI_SWIGLU = 1 };
 enum { NVQ_GEMM_AUTO = 0, NVQ_GEMM_DEQ16 = 1, NVQ_GEMM_FP8_BLOCK = 2 };
 

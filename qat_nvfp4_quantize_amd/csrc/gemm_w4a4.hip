@@ -181,67 +181,194 @@ __global__ __launch_bounds__(256) void k_gather_wcomp(const uint8_t* __restrict_
     wcomp[row * kpad + j] = (uint16_t)((j < k) ? w_comp_bf16(cr, sr, idx[j]) : 0u);
 }
 
-template <int kSwiglu>
-__global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM][LROW];
-
-  // XCD-aware tile order.  The grid is sized for the most row tiles the
-  // offsets allow; the real count comes from the tile table.  Workgroups are
-  // dealt to the 8 XCDs round-robin, so XCD x = blockIdx % 8 takes the
-  // contiguous logical range [x * per, (x + 1) * per) of the real tiles, in
-  // groups of 4 row tiles x all column tiles; the surplus workgroups exit.
+// The tile of this workgroup.  XCD-aware order: the grid is sized for the
+// most row tiles the offsets allow and the real count comes from the tile
+// table.  Workgroups are dealt to the 8 XCDs round-robin, so XCD x =
+// blockIdx % 8 takes the contiguous logical range [x * per, (x + 1) * per)
+// of the real tiles, in groups of 4 row tiles x all column tiles; surplus
+// workgroups get valid == false.
+struct TileCtx {
+  bool valid;
+  int e, nt;
+  int64_t row0, row_end;
+};
+__device__ __forceinline__ TileCtx tile_of_block(const GemmParams& p) {
+  TileCtx c;
+  c.valid = false;
   const int n_mt = min(*p.ntiles, p.max_tiles);
   const int n_groups = (n_mt + 3) / 4;
   const int total = n_groups * 4 * p.n_tiles_n;
   const int per = (total + 7) / 8;
   const int slot = blockIdx.x >> 3;
-  if (slot >= per) return;
+  if (slot >= per) return c;
   const int logical = (blockIdx.x & 7) * per + slot;
-  if (logical >= total) return;
+  if (logical >= total) return c;
   const int group_span = 4 * p.n_tiles_n;
   const int grp = logical / group_span, rem = logical - grp * group_span;
   const int mt = 4 * grp + (rem & 3);
-  const int nt = rem >> 2;
-  if (mt >= n_mt) return;
-  const int e = p.tiles[2 * mt];
-  const int64_t row0 = p.tiles[2 * mt + 1];
-  const int64_t row_end = p.off[e + 1];
+  if (mt >= n_mt) return c;
+  c.valid = true;
+  c.nt = rem >> 2;
+  c.e = p.tiles[2 * mt];
+  c.row0 = p.tiles[2 * mt + 1];
+  c.row_end = p.off[c.e + 1];
+  return c;
+}
+
+// Token row of A loader row ar (clamped to the expert's last row) and the
+// weight rows of this lane's two B fragments (clamped to N - 1): rows past
+// the ends are read but never stored, so every load is unconditional.
+__device__ __forceinline__ int64_t loader_a_token(const GemmParams& p, const TileCtx& c, int ar) {
+  return a_source_row(p, min<int64_t>(c.row0 + ar, c.row_end - 1));
+}
+template <int kSwiglu>
+__device__ __forceinline__ int64_t loader_b_row(const GemmParams& p, const TileCtx& c, int wave, int j,
+                                                int l32) {
+  return min<int64_t>(b_row_to_n(WN * wave + 32 * j + l32, c.nt, kSwiglu, p.N), p.N - 1);
+}
+
+// acc *= s_tA, then the compensation: 128-channel bf16 steps with the
+// residual rows through the LDS tile and the packed weight columns loaded in
+// fragment order.  Channels past k (kpad) read as zero.
+__device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c,
+                                           floatx16_t (&acc)[4][2], uint8_t (*lds)[LROW],
+                                           int64_t a_tok, const int64_t (&b_n)[2]) {
+  const float sta = *p.a_st;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] *= sta;
+  if (p.k <= 0) return;
+  const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, h = lane >> 5;
+  const int ar = t >> 1, ahh = t & 1;
+  const uint16_t* r_src = p.a_resid + a_tok * p.k;
+  const uint16_t* w_src[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) w_src[j] = p.wcomp + ((int64_t)c.e * p.N + b_n[j]) * p.kpad;
+  const int ncs = (p.k + SE - 1) / SE;
+  for (int cs = 0; cs < ncs; ++cs) {
+    const int c0 = SE * cs + 64 * ahh;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int ch = c0 + 8 * q;  // 8 channels (16 bytes); k % 8 == 0
+      const uint4 v = ch < p.k ? *reinterpret_cast<const uint4*>(r_src + ch) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&lds[ar][128 * ahh + 16 * q]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      bf16x8_t af[4], bf[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&lds[32 * i + l32][128 * h + 16 * d]);
+      const int cb = SE * cs + 64 * h + 8 * d;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4 v = cb < p.kpad ? *reinterpret_cast<const uint4*>(w_src[j] + cb) : make_uint4(0, 0, 0, 0);
+        __builtin_memcpy(&bf[j], &v, 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+}
+
+// Scale by s_tW and store.  acc[i][j][v]: row 32i + 8(v/4) + 4h + v%4, local
+// column 64 wave + 32 j + l32; with SwiGLU fragment 0 is the gate and
+// fragment 1 the up column of the same output column.
+template <int kSwiglu>
+__device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c,
+                                         const floatx16_t (&acc)[4][2]) {
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, l32 = lane & 31, h = lane >> 5;
+  const int64_t N = p.N;
+  const float stw = p.w_st[c.e];
+  if (!kSwiglu) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t pr = c.row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (pr >= c.row_end) continue;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int64_t n = (int64_t)c.nt * BN + WN * wave + 32 * j + l32;
+          if (n >= N) continue;
+          const float y = acc[i][j][v] * stw;
+          if (p.out_f32) p.out_f32[pr * N + n] = y;
+          if (p.out_bf16) p.out_bf16[pr * N + n] = (uint16_t)f32_to_bf16_rne(y);
+        }
+      }
+  } else {
+    const int64_t I = N >> 1;
+    const int64_t ng = (int64_t)c.nt * (BN / 2) + 32 * wave + l32;
+    if (ng >= I) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t pr = c.row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (pr >= c.row_end) continue;
+        const float g = acc[i][0][v] * stw;
+        const float u = acc[i][1][v] * stw;
+        if (p.out_f32) {
+          p.out_f32[pr * N + ng] = g;
+          p.out_f32[pr * N + I + ng] = u;
+        }
+        const float hv = g / (1.0f + __expf(-g)) * u;
+        if (p.out_bf16) p.out_bf16[pr * I + ng] = (uint16_t)f32_to_bf16_rne(hv);
+      }
+  }
+}
+
+// Per-thread register stage of one 128-element K step: this thread's A half
+// row (32 code bytes, 4 scale bytes) and, for each of its two B fragments,
+// the lane half (32 + 4 bytes) or, for path FP8_BLOCK, one code dword of
+// each of the 8 blocks (the lane half's 8 elements of the block) and the
+// 8 scale bytes.
+template <bool kFp8>
+struct Stage {
+  uint4 a[2];
+  uint32_t as;
+  uint4 b[2][2];
+  uint32_t bs[2][kFp8 ? 2 : 1];
+};
+
+// ------------------------------------------------------------ path DEQ16 --
+template <int kSwiglu>
+__global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM][LROW];
+  const TileCtx c = tile_of_block(p);
+  if (!c.valid) return;
   const int64_t K = p.K, N = p.N;
   const int64_t Kh = K >> 1, Kb = K >> 4;
-
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int l32 = lane & 31, h = lane >> 5;
 
   // A loader: row ar = t / 2, lane half ahh = t % 2 (elements [64 ahh, 64 ahh
   // + 64) of each step).  B: fragment j = local row 64 wave + 32 j + l32, lane
-  // half h.  Rows past the expert's end or past N read a clamped valid row:
-  // FP4 values are always finite and those outputs are never stored, so every
-  // load is issued unconditionally and needs no mask.
+  // half h.
   const int ar = t >> 1, ahh = t & 1;
-  const int64_t a_tok = a_source_row(p, min<int64_t>(row0 + ar, row_end - 1));
+  const int64_t a_tok = loader_a_token(p, c, ar);
   const uint8_t* a_src = p.a_codes + a_tok * Kh + 32 * ahh;
   const uint8_t* a_ssrc = p.a_scales + a_tok * Kb + 4 * ahh;
-  const uint8_t* wcodes_e = p.w_codes + (int64_t)e * N * Kh;
-  const uint8_t* wscales_e = p.w_scales + (int64_t)e * N * Kb;
   const uint8_t* b_src[2];
   const uint8_t* b_ssrc[2];
   int64_t b_n[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    b_n[j] = min<int64_t>(b_row_to_n(WN * wave + 32 * j + l32, nt, kSwiglu, N), N - 1);
-    b_src[j] = wcodes_e + b_n[j] * Kh + 32 * h;
-    b_ssrc[j] = wscales_e + b_n[j] * Kb + 4 * h;
+    b_n[j] = loader_b_row<kSwiglu>(p, c, wave, j, l32);
+    b_src[j] = p.w_codes + ((int64_t)c.e * N + b_n[j]) * Kh + 32 * h;
+    b_ssrc[j] = p.w_scales + ((int64_t)c.e * N + b_n[j]) * Kb + 4 * h;
   }
-
-  struct Stage {
-    uint4 a[2];
-    uint32_t as;
-    uint4 b[2][2];
-    uint32_t bs[2];
-  };
   const int nst = (int)(K / SE);
-  auto gload = [&](Stage& S, int step) {
+  auto gload = [&](Stage<false>& S, int step) {
     const int64_t sc = min(step, nst - 1);  // past the end: a valid step, zero-scaled later
     S.a[0] = *reinterpret_cast<const uint4*>(a_src + sc * 64);
     S.a[1] = *reinterpret_cast<const uint4*>(a_src + sc * 64 + 16);
@@ -250,12 +377,12 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
     for (int j = 0; j < 2; ++j) {
       S.b[j][0] = *reinterpret_cast<const uint4*>(b_src[j] + sc * 64);
       S.b[j][1] = *reinterpret_cast<const uint4*>(b_src[j] + sc * 64 + 16);
-      S.bs[j] = *reinterpret_cast<const uint32_t*>(b_ssrc[j] + sc * 8);
+      S.bs[j][0] = *reinterpret_cast<const uint32_t*>(b_ssrc[j] + sc * 8);
     }
   };
   // This thread's 64 A elements of a step -> exact fp16 at LDS row ar, bytes
   // [128 ahh, 128 ahh + 128).  live == false (a step past K) writes zeros.
-  auto a_store = [&](const Stage& S, int buf, bool live) {
+  auto a_store = [&](const Stage<false>& S, int buf, bool live) {
     uint8_t* dst = &lds[buf][ar][128 * ahh];
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
@@ -274,7 +401,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
 
   // one step: 8 sub-steps; A fragments from LDS (rows 32 i + l32, bytes
   // 128 h + 16 d), B fragments dequantized from registers (dword d).
-  auto mfma_step = [&](const Stage& S, int buf) {
+  auto mfma_step = [&](const Stage<false>& S, int buf) {
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       half8_t af[4], bf[2];
@@ -282,7 +409,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
       for (int i = 0; i < 4; ++i)
         af[i] = *reinterpret_cast<const half8_t*>(&lds[buf][32 * i + l32][128 * h + 16 * d]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = dequant8(dword_of(S.b[j], d), scale_pair(S.bs[j], d >> 1));
+      for (int j = 0; j < 2; ++j) bf[j] = dequant8(dword_of(S.b[j], d), scale_pair(S.bs[j][0], d >> 1));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -295,7 +422,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
   // step s + 1 (in registers) is dequantized into the other buffer; each
   // register stage is loaded two steps before its MFMAs.  The loop covers
   // step pairs; an odd step count adds one zero-scaled step.
-  Stage X0, X1;
+  Stage<false> X0, X1;
   gload(X0, 0);
   gload(X1, 1);
   a_store(X0, 0, true);
@@ -310,95 +437,175 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
     __syncthreads();
     gload(X1, st + 3);
   }
+  comp_phase(p, c, acc, lds[0], a_tok, b_n);
+  epilogue<kSwiglu>(p, c, acc);
+}
 
-  // ---- s_tA, then the compensation steps, then s_tW
-  const float sta = *p.a_st;
+// -------------------------------------------------------- path FP8_BLOCK --
+// E2M1 magnitude index -> FP8 E4M3 byte (0, 0.5, 1, 1.5, 2, 3, 4, 6), as two
+// byte-select tables for v_perm.
+constexpr uint32_t kFp8TabLo = 0x3C383000u;  // indices 0..3
+constexpr uint32_t kFp8TabHi = 0x4C484440u;  // indices 4..7
+
+// The 4 even (sel_odd = false) or odd nibbles of a code dword -> 4 FP8 bytes.
+__device__ __forceinline__ uint32_t fp4_to_fp8_4(uint32_t w, bool sel_odd) {
+  const uint32_t nib = sel_odd ? (w >> 4) : w;
+  const uint32_t mag = __builtin_amdgcn_perm(kFp8TabHi, kFp8TabLo, nib & 0x07070707u);
+  return mag | ((nib & 0x08080808u) << 4);
+}
+
+// Path FP8_BLOCK: per 16-element block, one v_mfma_f32_32x32x16_fp8_fp8 of
+// the raw E2M1 magnitudes (exact in FP8 E4M3) into a zero accumulator gives
+// the exact block dot products; the fp32 accumulator then adds them times
+// s_bA s_bW.  Within block b, lane half h takes elements 8h .. 8h + 7 (even
+// ones first, then odd), for A and B alike.  The A tile goes through LDS as FP8 with an
+// fp32 table of its block scales; B stays in registers as in path DEQ16.
+template <int kSwiglu>
+__global__ __launch_bounds__(NTHR, 1) void k_moe_gemm_fp8blk(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM][LROW];  // FP8 tile uses 128 bytes a row
+  __shared__ __attribute__((aligned(16))) float s_as[2][8][BM];       // A block scales [block][row]
+  const TileCtx c = tile_of_block(p);
+  if (!c.valid) return;
+  const int64_t K = p.K, N = p.N;
+  const int64_t Kh = K >> 1, Kb = K >> 4;
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int ar = t >> 1, ahh = t & 1;
+  const int64_t a_tok = loader_a_token(p, c, ar);
+  const uint8_t* a_src = p.a_codes + a_tok * Kh + 32 * ahh;
+  const uint8_t* a_ssrc = p.a_scales + a_tok * Kb + 4 * ahh;
+  const uint8_t* b_src[2];
+  const uint8_t* b_ssrc[2];
+  int64_t b_n[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    b_n[j] = loader_b_row<kSwiglu>(p, c, wave, j, l32);
+    b_src[j] = p.w_codes + ((int64_t)c.e * N + b_n[j]) * Kh;
+    b_ssrc[j] = p.w_scales + ((int64_t)c.e * N + b_n[j]) * Kb;
+  }
+  const int nst = (int)(K / SE);
+  auto gload = [&](Stage<true>& S, int step) {
+    const int64_t sc = min(step, nst - 1);
+    S.a[0] = *reinterpret_cast<const uint4*>(a_src + sc * 64);
+    S.a[1] = *reinterpret_cast<const uint4*>(a_src + sc * 64 + 16);
+    S.as = *reinterpret_cast<const uint32_t*>(a_ssrc + sc * 8);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t d[8];
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb)
+        d[bb] = *reinterpret_cast<const uint32_t*>(b_src[j] + sc * 64 + 8 * bb + 4 * h);
+      S.b[j][0] = make_uint4(d[0], d[1], d[2], d[3]);
+      S.b[j][1] = make_uint4(d[4], d[5], d[6], d[7]);
+      const uint2 sv = *reinterpret_cast<const uint2*>(b_ssrc[j] + sc * 8);
+      S.bs[j][0] = sv.x;
+      S.bs[j][1] = sv.y;
+    }
+  };
+  // A blocks 4 ahh .. 4 ahh + 3 of a step -> FP8 at LDS row ar, bytes
+  // [16 b, 16 b + 16): for each lane half h, the 8 elements 16 b + 8 h ..
+  // as (even, odd) nibbles; and the block scales in fp32.
+  auto a_store = [&](const Stage<true>& S, int buf, bool live) {
+    const uint32_t w[8] = {S.a[0].x, S.a[0].y, S.a[0].z, S.a[0].w, S.a[1].x, S.a[1].y, S.a[1].z, S.a[1].w};
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const int b = 4 * ahh + bb;
+      uint4 o;
+      o.x = fp4_to_fp8_4(w[2 * bb], false);
+      o.y = fp4_to_fp8_4(w[2 * bb], true);
+      o.z = fp4_to_fp8_4(w[2 * bb + 1], false);
+      o.w = fp4_to_fp8_4(w[2 * bb + 1], true);
+      *reinterpret_cast<uint4*>(&lds[buf][ar][16 * b]) = o;
+      s_as[buf][b][ar] = live ? e4m3_to_f32((S.as >> (8 * bb)) & 0xFFu) : 0.0f;
+    }
+  };
+
+  floatx16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] *= sta;
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  if (p.k > 0) {
-    // residual row of this thread's A row (stride k); packed weight columns
-    // of each B fragment (stride kpad).  Channels past k (kpad) read as zero.
-    const uint16_t* r_src = p.a_resid + a_tok * p.k;
-    const uint16_t* w_src[2];
+  auto mfma_step = [&](const Stage<true>& S, int buf) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) w_src[j] = p.wcomp + ((int64_t)e * N + b_n[j]) * p.kpad;
-    const int ncs = (p.k + SE - 1) / SE;
-    for (int cs = 0; cs < ncs; ++cs) {
-      const int c0 = SE * cs + 64 * ahh;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int c = c0 + 8 * q;  // 8 channels (16 bytes); k % 8 == 0
-        const uint4 v = c < p.k ? *reinterpret_cast<const uint4*>(r_src + c) : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&lds[0][ar][128 * ahh + 16 * q]) = v;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        bf16x8_t af[4], bf[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const bf16x8_t*>(&lds[0][32 * i + l32][128 * h + 16 * d]);
-        const int cb = SE * cs + 64 * h + 8 * d;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint4 v = cb < p.kpad ? *reinterpret_cast<const uint4*>(w_src[j] + cb) : make_uint4(0, 0, 0, 0);
-          __builtin_memcpy(&bf[j], &v, 16);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      }
-      __syncthreads();
-    }
-  }
-
-  const float stw = p.w_st[e];
-  // ---- epilogue.  acc[i][j][v]: row 32i + 8(v/4) + 4h + v%4, local column
-  // 64 wave + 32 j + l32.
-  if (!kSwiglu) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t pr = row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (pr >= row_end) continue;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t n = (int64_t)nt * BN + WN * wave + 32 * j + l32;
-          if (n >= N) continue;
-          const float y = acc[i][j][v] * stw;
-          if (p.out_f32) p.out_f32[pr * N + n] = y;
-          if (p.out_bf16) p.out_bf16[pr * N + n] = (uint16_t)f32_to_bf16_rne(y);
-        }
-      }
-  } else {
-    const int64_t I = N >> 1;
-    const int64_t ng = (int64_t)nt * (BN / 2) + 32 * wave + l32;
-    if (ng < I) {
+    for (int b = 0; b < 8; ++b) {
+      int64_t af[4], bf[2];
+      float sw[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const int64_t*>(&lds[buf][32 * i + l32][16 * b + 8 * h]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t w = dword_of(S.b[j], b);  // this lane half's 8 elements of block b
+        const uint32_t lo = fp4_to_fp8_4(w, false), hi = fp4_to_fp8_4(w, true);
+        bf[j] = (int64_t)(((uint64_t)hi << 32) | lo);
+        sw[j] = e4m3_to_f32((S.bs[j][b >> 2] >> (8 * (b & 3))) & 0xFFu);
+      }
+      // 8 (i, j) tiles, i-major; the MFMA of tile k + 1 is issued before
+      // tile k's scaled accumulate, and scheduling barriers keep at most two
+      // block products live.
+      float4 sa[4];
+      auto load_sa = [&](int i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sa[r] = *reinterpret_cast<const float4*>(&s_as[buf][b][32 * i + 8 * r + 4 * h]);
+      };
+      // The zero accumulator of each block product passes through an empty
+      // volatile asm after the previous tile's accumulate, so the compiler
+      // cannot hoist all eight products (8 x 16 registers) to the top.
+      auto block_mfma = [&](int k) {
+        floatx16_t z;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) z[v] = 0.0f;
+        asm volatile("" : "+v"(z));
+        return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(af[k >> 1], bf[k & 1], z, 0, 0, 0);
+      };
+      auto accumulate = [&](int k, const floatx16_t& P) {
+        const int i = k >> 1, j = k & 1;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int64_t pr = row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (pr >= row_end) continue;
-          const float g = acc[i][0][v] * stw;
-          const float u = acc[i][1][v] * stw;
-          if (p.out_f32) {
-            p.out_f32[pr * N + ng] = g;
-            p.out_f32[pr * N + I + ng] = u;
-          }
-          const float hv = g / (1.0f + __expf(-g)) * u;
-          if (p.out_bf16) p.out_bf16[pr * I + ng] = (uint16_t)f32_to_bf16_rne(hv);
+          const float4& s4 = sa[v >> 2];
+          const float sav = (v & 3) == 0 ? s4.x : (v & 3) == 1 ? s4.y : (v & 3) == 2 ? s4.z : s4.w;
+          acc[i][j][v] = __builtin_fmaf(P[v], sav * sw[j], acc[i][j][v]);
         }
+        asm volatile("" : "+v"(acc[i][j]));
+      };
+      load_sa(0);
+      floatx16_t P0 = block_mfma(0), P1;
+#define NVQ_FP8_TILE(K)                       \
+  P1 = block_mfma(K);                         \
+  accumulate((K) - 1, P0);                    \
+  if (((K) & 1) == 0) load_sa((K) >> 1);      \
+  __builtin_amdgcn_sched_barrier(0);          \
+  P0 = P1;
+      NVQ_FP8_TILE(1) NVQ_FP8_TILE(2) NVQ_FP8_TILE(3) NVQ_FP8_TILE(4)
+      NVQ_FP8_TILE(5) NVQ_FP8_TILE(6) NVQ_FP8_TILE(7)
+#undef NVQ_FP8_TILE
+      accumulate(7, P0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  Stage<true> X0, X1;
+  gload(X0, 0);
+  gload(X1, 1);
+  a_store(X0, 0, true);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    mfma_step(X0, 0);
+    a_store(X1, 1, st + 1 < nst);
+    __syncthreads();
+    gload(X0, st + 2);
+    mfma_step(X1, 1);
+    a_store(X0, 0, st + 2 < nst);
+    __syncthreads();
+    gload(X1, st + 3);
   }
+  comp_phase(p, c, acc, lds[0], a_tok, b_n);
+  epilogue<kSwiglu>(p, c, acc);
 }
 
 struct MoeLayout {
@@ -441,7 +648,6 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   if (a->epilogue != NVQ_EPI_NONE && a->epilogue != NVQ_EPI_SWIGLU) return NVQ_EINVAL;
   if (a->path != NVQ_GEMM_AUTO && a->path != NVQ_GEMM_DEQ16 && a->path != NVQ_GEMM_FP8_BLOCK)
     return NVQ_EINVAL;
-  if (a->path == NVQ_GEMM_FP8_BLOCK) return NVQ_EUNSUPPORTED;
   if (a->rows < 0 || a->E < 1 || a->E > 1024 || a->N <= 0 || a->K <= 0) return NVQ_ESHAPE;
   if (a->K % 128 != 0) return NVQ_ESHAPE;  // K steps of 32 elements; 128 keeps rows 64-byte aligned
   if (a->epilogue == NVQ_EPI_SWIGLU && (a->N % 2 != 0)) return NVQ_ESHAPE;
@@ -482,9 +688,17 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   const int n_groups = (L.max_tiles + 3) / 4;
   const int64_t G0 = (int64_t)n_groups * 4 * p.n_tiles_n;
   const int64_t G = (G0 + 7) / 8 * 8;
-  if (swiglu)
-    hipLaunchKernelGGL(k_moe_gemm_deq16<1>, dim3((unsigned)G), dim3(NTHR), 0, s, p);
-  else
-    hipLaunchKernelGGL(k_moe_gemm_deq16<0>, dim3((unsigned)G), dim3(NTHR), 0, s, p);
+  const bool fp8 = a->path == NVQ_GEMM_FP8_BLOCK;
+  if (fp8) {
+    if (swiglu)
+      hipLaunchKernelGGL(k_moe_gemm_fp8blk<1>, dim3((unsigned)G), dim3(NTHR), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_moe_gemm_fp8blk<0>, dim3((unsigned)G), dim3(NTHR), 0, s, p);
+  } else {
+    if (swiglu)
+      hipLaunchKernelGGL(k_moe_gemm_deq16<1>, dim3((unsigned)G), dim3(NTHR), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_moe_gemm_deq16<0>, dim3((unsigned)G), dim3(NTHR), 0, s, p);
+  }
   return last_launch();
 }

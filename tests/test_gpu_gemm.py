@@ -35,10 +35,12 @@ def _w_deq(codes, scales, st):
     return oracle.dequantize(codes, scales, st).astype(np.float64)
 
 
-def test_dense_check_workload():
+@pytest.mark.parametrize("path", ["deq16", "fp8_block"])
+def test_dense_check_workload(path):
     import torch
 
     nvq = _nvq()
+    gp = nvq.NVQ_GEMM_DEQ16 if path == "deq16" else nvq.NVQ_GEMM_FP8_BLOCK
     x, w, k = inputs.dense_check()
     xg, wg = to_gpu(x), to_gpu(w)
     qa = nvq.nvfp4_quantize(xg, score=True)
@@ -47,7 +49,7 @@ def test_dense_check_workload():
     off = torch.tensor([0, x.shape[0]], dtype=torch.int32, device="cuda")
     ob, of = nvq.moe_grouped_gemm_w4a4_comp(qa[0], qa[1], qa[2], qw[0], qw[1], qw[2], off,
                                             rows=x.shape[0], a_resid=resid.contiguous(),
-                                            comp_idx=idx, want_f32=True)
+                                            comp_idx=idx, want_f32=True, path=gp)
     torch.cuda.synchronize()
     oqa, oqw = oracle.quantize(x), oracle.quantize(w)
     oidx = oracle.topk(oracle.residual_scores(x, *oqa), k)
@@ -57,7 +59,7 @@ def test_dense_check_workload():
     check_tol(inputs.bf16_bits_to_f32(to_np(ob)), ref, x, _w_deq(*oqw), "dense bf16")
     # k = 0 reproduces the plain W4A4 product
     ob0, of0 = nvq.moe_grouped_gemm_w4a4_comp(qa[0], qa[1], qa[2], qw[0], qw[1], qw[2], off,
-                                              rows=x.shape[0], want_f32=True)
+                                              rows=x.shape[0], want_f32=True, path=gp)
     ref0 = oracle.moe_gemm_w4a4(*oqa, x, None, *oqw, np.arange(64), np.zeros(64))
     check_tol(to_np(of0), ref0, x, _w_deq(*oqw), "dense k=0")
 
@@ -65,10 +67,11 @@ def test_dense_check_workload():
 class MoeRun:
     """Runs a MoE layer stage by stage on the GPU, keeping every intermediate."""
 
-    def __init__(self, s, experts_np=None):
+    def __init__(self, s, path=0):
         import torch
 
         nvq = _nvq()
+        self.path = path
         self.s = s
         self.logits = inputs.logits(s)
         self.x = inputs.activations(s)
@@ -86,17 +89,21 @@ class MoeRun:
         self.h, self.y1 = nvq.moe_grouped_gemm_w4a4_comp(
             self.qx[0], self.qx[1], self.qx[2], self.qgu[0], self.qgu[1], self.qgu[2], self.off,
             rows=s.P, a_row=self.a_row, a_resid=self.r1.contiguous(), comp_idx=self.idx1,
-            epilogue=nvq.NVQ_EPI_SWIGLU, want_f32=True)
+            epilogue=nvq.NVQ_EPI_SWIGLU, want_f32=True, path=path)
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("path", ["deq16", "fp8_block"])
 @pytest.mark.parametrize("shape", ["small", "small_ragged"])
-def test_small_moe_layer_stagewise(shape):
+def test_small_moe_layer_stagewise(shape, path):
+    """Both GEMM paths (exact fp16 dequantization; FP8 block products scaled
+    in fp32) against the same oracle."""
     import torch
 
     nvq = _nvq()
+    gp = nvq.NVQ_GEMM_DEQ16 if path == "deq16" else nvq.NVQ_GEMM_FP8_BLOCK
     s = inputs.small_moe() if shape == "small" else inputs.small_moe(wid=101, T=77, E=5, topk=3, k=24)
-    run = MoeRun(s)
+    run = MoeRun(s, gp)
     x = run.x
     xf = inputs.bf16_bits_to_f32(x)
     oids, ow = oracle.route(run.logits, s.topk)
@@ -140,7 +147,8 @@ def test_small_moe_layer_stagewise(shape):
     dst = np.array([q[2] for q in qdn], np.float32)
     ob, of = nvq.moe_grouped_gemm_w4a4_comp(qh[0], qh[1], qh[2], run.qdn[0], run.qdn[1],
                                             run.qdn[2], run.off, rows=s.P,
-                                            a_resid=r2.contiguous(), comp_idx=idx2, want_f32=True)
+                                            a_resid=r2.contiguous(), comp_idx=idx2, want_f32=True,
+                                            path=gp)
     torch.cuda.synchronize()
     ref_y2 = oracle.moe_gemm_w4a4(*oqh, H, oidx2, dc, dsc, dst, np.arange(s.P), row_e)
     Hf = inputs.bf16_bits_to_f32(H)
