@@ -320,7 +320,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c,
           p.out_f32[pr * N + ng] = g;
           p.out_f32[pr * N + I + ng] = u;
         }
-        const float hv = g / (1.0f + __expf(-g)) * u;
+        // silu(g) u; the result is rounded to bf16, so an rcp suffices
+        const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
         if (p.out_bf16) p.out_bf16[pr * I + ng] = (uint16_t)f32_to_bf16_rne(hv);
       }
   }
