@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import os
 import sys
 import time
@@ -321,6 +322,29 @@ class QatLeg:
         return out
 
 
+def profiled_traffic():
+    """HBM bytes per nvfp4_quantize call on the sweep, from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary (copy-kernel calibrated), when the
+    quantizer sources still hash to the value recorded there; else None."""
+    import hashlib
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "quantize_sweep_8192x7168_bf16.txt")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m_b = re.search(r"^traffic_bytes_per_call: (\d+)", text, re.M)
+    m_h = re.search(r"^source_sha1 \(.*\): ([0-9a-f]{40})", text, re.M)
+    if not (m_b and m_h):
+        return None
+    h = hashlib.sha1()
+    for fn in ("quantize.hip", "nvq_device.h", "nvq_internal.h"):
+        with open(os.path.join(here, "qat_nvfp4_quantize_amd", "csrc", fn), "rb") as fh:
+            h.update(fh.read())
+    return int(m_b.group(1)) if h.hexdigest() == m_h.group(1) else None
+
+
 class CopyLeg:
     """Plain elementwise copy of a known size: calibrates the FETCH_SIZE /
     WRITE_SIZE counters (and measures achievable HBM bandwidth)."""
@@ -418,7 +442,8 @@ def main():
                            "algorithmic_bytes": q.bytes}},
         "roofline": {"kernel": "nvfp4_quantize (amax + quantize + score-reduce kernels)",
                      "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic()},
     }
     for leg in legs:
         if leg.name.startswith("moe") or leg.name == "qat":
