@@ -205,3 +205,64 @@ def test_decode_layer_gate_up_sampled():
     for i, e in enumerate(experts):
         sel = local_e == i
         check_tol(y1[sel], ref[sel], xf[row_tok[sel]], _w_deq(wc[i], wsc[i], wst[i]), f"decode e={e}")
+
+
+@pytest.mark.parametrize("path", ["deq16", "fp8_block"])
+@pytest.mark.parametrize("K,N,k,epi", [(128, 160, 8, "none"), (384, 384, 128, "none"),
+                                       (384, 192, 0, "swiglu"), (128, 208, 128, "swiglu")])
+def test_grouped_gemm_edge_shapes(K, N, k, epi, path):
+    """Direct grouped-GEMM calls on shapes the layer tests do not reach: an odd
+    number of 128-element K steps (K = 384), partial column tiles (N = 160,
+    208, 384; SwiGLU halves of 96 and 104), k = K, k = 0, experts with no
+    rows, one expert with more rows than one row tile, fp32 and bf16 outputs,
+    and rows read through a_row with a divisor."""
+    import torch
+
+    nvq = _nvq()
+    gp = nvq.NVQ_GEMM_DEQ16 if path == "deq16" else nvq.NVQ_GEMM_FP8_BLOCK
+    swiglu = epi == "swiglu"
+    g = np.random.default_rng(K * 1000 + N + k)
+    E, T, topk = 5, 70, 3
+    counts = np.array([0, 150, 3, 0, 57])  # P = 210 sorted rows
+    P = int(counts.sum())
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    pair = g.permutation(T * topk)[:P].astype(np.int32)  # sorted pair ids; token = pair // topk
+    x = (g.standard_normal((T, K)) * np.exp(g.standard_normal((1, K)))).astype(np.float32)
+    w = (g.standard_normal((E, N, K)) * 0.05).astype(np.float32)
+    log(f"[gemm-edge] K={K} N={N} k={k} {epi} {path}")
+    xg = to_gpu(x)
+    qa = nvq.nvfp4_quantize(xg, score=True)
+    qw = nvq.nvfp4_quantize(to_gpu(w))
+    resid, idx = None, None
+    if k > 0:
+        idx, resid, _ = nvq.residual_topk_channels(xg, *qa[:3], k, scores=qa[3])
+        resid = resid.contiguous()
+    ob, of = nvq.moe_grouped_gemm_w4a4_comp(
+        qa[0], qa[1], qa[2], qw[0], qw[1], qw[2], to_gpu(off), rows=P, a_row=to_gpu(pair),
+        a_resid=resid, comp_idx=idx, epilogue=nvq.NVQ_EPI_SWIGLU if swiglu else nvq.NVQ_EPI_NONE,
+        want_f32=True, path=gp, a_row_div=topk)
+    torch.cuda.synchronize()
+    oqa = oracle.quantize(x)
+    oidx = oracle.topk(oracle.residual_scores(x, *oqa), k) if k > 0 else None
+    if k > 0:
+        assert_bits_equal(to_np(idx), oidx, "comp idx")
+    wq = [oracle.quantize(w[e]) for e in range(E)]
+    wc = np.stack([q[0] for q in wq])
+    wsc = np.stack([q[1] for q in wq])
+    wst = np.array([q[2] for q in wq], np.float32)
+    assert_bits_equal(to_np(qw[0]), wc, "weight codes")
+    row_tok = (pair // topk).astype(np.int32)
+    row_e = np.repeat(np.arange(E), counts).astype(np.int32)
+    ref = oracle.moe_gemm_w4a4(*oqa, x, oidx, wc, wsc, wst, row_tok, row_e)
+    y = to_np(of)
+    for e in range(E):
+        rows = slice(off[e], off[e + 1])
+        if off[e + 1] > off[e]:
+            check_tol(y[rows], ref[rows], x[row_tok[rows]], _w_deq(wc[e], wsc[e], wst[e]),
+                      f"edge e={e}")
+    if swiglu:
+        h_ref = oracle.swiglu_bf16(y.astype(np.float64))
+        np.testing.assert_allclose(inputs.bf16_bits_to_f32(to_np(ob)), inputs.bf16_bits_to_f32(h_ref),
+                                   rtol=2 ** -7, atol=1e-6)
+    else:
+        assert_bits_equal(to_np(ob), inputs.to_bf16_bits(y), "bf16 output = rounded fp32 output")
