@@ -423,6 +423,182 @@ __global__ __launch_bounds__(QT) void k_qat_gemm(QatParams p) {
     }
 }
 
+// ------------------------------------------------------ forward, 2 WG/CU --
+// The forward in the grouped-GEMM layout: workgroup = 4 waves = 128 sorted
+// rows x 256 output columns; wave = 128 x 64 with accumulators in VGPRs (two
+// workgroups share a CU).  K advances 128 elements per step.
+//  * A (x rows gathered through a_row, bf16, shared by the four waves) goes
+//    straight from global memory into a double-buffered LDS tile with
+//    global_load_lds_dwordx4 (no registers): LDS slot = base + 16 lane, so
+//    lane l of load instruction I carries row 4 I + l / 16, slot l % 16.  The
+//    slot of 16-byte chunk c of row r is c ^ (r & 15) (256-byte rows, XOR
+//    swizzle: the fragment reads of 16 consecutive rows hit distinct banks).
+//  * B (this wave's 64 weight rows, FP4) is loaded in fragment order two steps
+//    ahead and dequantized exactly to bf16 in registers: G * s_b has <= 6
+//    significant bits.
+// Within a step lane half h owns elements [64h, 64h + 64); sub-step d takes
+// 64h + 8d .. +8 for A and B alike.
+constexpr int FBM = 128, FBN = 256, FWN = 64, FSE = 128;
+
+struct QStage {
+  uint4 b[2][2];
+  uint32_t bs[2];
+};
+
+__device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t w, float s_b) {
+  const uint4 v = fp4x8_to_bf16(w, s_b);
+  bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+__global__ __launch_bounds__(256, 2) void k_qat_fwd2(QatParams p) {
+  __shared__ __attribute__((aligned(16))) uint4 lds[2][FBM * 16];
+  // XCD-aware order over the real tiles (groups of 4 row tiles x all column
+  // tiles, each XCD a contiguous range); surplus workgroups exit.
+  const int n_mt = min(*p.ntiles, p.max_tiles);
+  const int n_groups = (n_mt + 3) / 4;
+  const int total = n_groups * 4 * p.n_tiles_n;
+  const int per = (total + 7) / 8;
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per) return;
+  const int logical = (blockIdx.x & 7) * per + slot;
+  if (logical >= total) return;
+  const int group_span = 4 * p.n_tiles_n;
+  const int grp = logical / group_span, rem = logical - grp * group_span;
+  const int mt = 4 * grp + (rem & 3);
+  const int nt = rem >> 2;
+  if (mt >= n_mt) return;
+  const int e = p.tiles[2 * mt];
+  const int64_t row0 = p.tiles[2 * mt + 1];
+  const int64_t row_end = p.off[e + 1];
+  const int64_t K = p.K, N = p.N;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, l32 = lane & 31, h = lane >> 5;
+
+  // A: this lane's 8 load instructions (I = 4 q + wave) per step; rows past
+  // the expert's end read a clamped valid row (never stored).
+  const uint16_t* a_src[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int I = 4 * q + wave;
+    const int r = 4 * I + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    const int64_t pr = min<int64_t>(row0 + r, row_end - 1);
+    const int64_t tok = p.a_row ? (int64_t)p.a_row[pr] : pr;
+    a_src[q] = p.x + tok * K + 8 * c;
+  }
+  auto a_load = [&](int buf, int step) {
+    const int64_t k0 = (int64_t)min(step, (int)(K / FSE) - 1) * FSE;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int I = 4 * q + wave;
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + k0),
+                                       (__attribute__((address_space(3))) void*)&lds[buf][64 * I], 16, 0, 0);
+    }
+  };
+  // B: fragment j = weight row 64 wave + 32 j + l32 of this column tile
+  const uint8_t* b_src[2];
+  const uint8_t* b_ssrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = min<int64_t>((int64_t)nt * FBN + FWN * wave + 32 * j + l32, N - 1);
+    b_src[j] = p.w_codes + ((int64_t)e * N + n) * (K >> 1) + 32 * h;
+    b_ssrc[j] = p.w_scales + ((int64_t)e * N + n) * (K >> 4) + 4 * h;
+  }
+  const int nst = (int)(K / FSE);
+  auto b_load = [&](QStage& S, int step) {
+    const int64_t sc = min(step, nst - 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      S.b[j][0] = *reinterpret_cast<const uint4*>(b_src[j] + sc * 64);
+      S.b[j][1] = *reinterpret_cast<const uint4*>(b_src[j] + sc * 64 + 16);
+      S.bs[j] = *reinterpret_cast<const uint32_t*>(b_ssrc[j] + sc * 8);
+    }
+  };
+
+  floatx16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  auto mfma_step = [&](const QStage& S, int buf) {
+    float sb[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) sb[j][b] = e4m3_to_f32((S.bs[j] >> (8 * b)) & 0xFFu);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      bf16x8_t af[4], bf[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 32 * i + l32;
+        const int c = 8 * h + d;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&lds[buf][16 * r + (c ^ (r & 15))]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4& v = S.b[j][d >> 2];
+        const uint32_t w = (d & 3) == 0 ? v.x : (d & 3) == 1 ? v.y : (d & 3) == 2 ? v.z : v.w;
+        bf[j] = fp4x8_bf16(w, sb[j][d >> 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Pipeline over step pairs: each step first issues the A tile (into the
+  // other LDS buffer) and the B stage of the next step, runs its MFMAs, then
+  // waits for every load of this thread and meets the other waves at a
+  // barrier, so a load has one step of MFMA work to land.  An odd step count
+  // ends with one more step outside the loop.
+  QStage X0, X1;
+  a_load(0, 0);
+  b_load(X0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  const int npair = nst >> 1;
+  for (int it = 0; it < npair; ++it) {
+    const int st = 2 * it;
+    a_load(1, st + 1);
+    b_load(X1, st + 1);
+    mfma_step(X0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (st + 2 < nst) {
+      a_load(0, st + 2);
+      b_load(X0, st + 2);
+    }
+    mfma_step(X1, 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+  if (nst & 1) mfma_step(X0, 0);
+
+  const float stw = p.w_st[e];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t pr = row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (pr >= row_end) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t n = (int64_t)nt * FBN + FWN * wave + 32 * j + l32;
+        if (n >= N) continue;
+        const float y = acc[i][j][v] * stw;
+        if (p.out_f32) p.out_f32[pr * N + n] = y;
+        if (p.out_bf16) p.out_bf16[pr * N + n] = (uint16_t)f32_to_bf16_rne(y);
+      }
+    }
+}
+
 struct QatLayout {
   int max_tiles;
   int32_t* tiles;
@@ -496,7 +672,11 @@ extern "C" int qat_fakequant_gemm_w4a16(const nvq_qat_gemm_args* a, void* stream
   p.n_tiles_n = (int)((cols + QBN - 1) / QBN);
   const int64_t G0 = (int64_t)L.max_tiles * p.n_tiles_n;
   const int64_t G = (G0 + 7) / 8 * 8;
-  if (a->mode == NVQ_QAT_FWD)
+  if (a->mode == NVQ_QAT_FWD && a->K % FSE == 0 && ((uintptr_t)a->w_scales & 3u) == 0) {
+    p.n_tiles_n = (int)((a->N + FBN - 1) / FBN);
+    const int64_t G2 = ((int64_t)((L.max_tiles + 3) / 4) * 4 * p.n_tiles_n + 7) / 8 * 8;
+    hipLaunchKernelGGL(k_qat_fwd2, dim3((unsigned)G2), dim3(256), 0, s, p);
+  } else if (a->mode == NVQ_QAT_FWD)
     hipLaunchKernelGGL((k_qat_gemm<NVQ_QAT_FWD, LD_ROWS, LD_FP4>), dim3((unsigned)G), dim3(QT), 0, s, p);
   else
     hipLaunchKernelGGL((k_qat_gemm<NVQ_QAT_DGRAD, LD_ROWS, LD_FP4_T>), dim3((unsigned)G), dim3(QT), 0, s,
