@@ -67,11 +67,12 @@ struct QatParams {
 
 __global__ __launch_bounds__(1024) void k_qat_tile_table(const int32_t* __restrict__ off, int E,
                                                         int32_t* __restrict__ tiles,
-                                                        int32_t* __restrict__ ntiles, int max_tiles) {
+                                                        int32_t* __restrict__ ntiles, int max_tiles,
+                                                        int bm) {
   __shared__ int32_t s_first[1025];
   const int e = threadIdx.x;
   int nt = 0;
-  if (e < E) nt = (off[e + 1] - off[e] + QBM - 1) / QBM;
+  if (e < E) nt = (off[e + 1] - off[e] + bm - 1) / bm;
   if (e < E) s_first[e + 1] = nt;
   if (threadIdx.x == 0) s_first[0] = 0;
   __syncthreads();
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(1024) void k_qat_tile_table(const int32_t* __restri
     const int base = s_first[e];
     for (int t = 0; t < nt && base + t < max_tiles; ++t) {
       tiles[2 * (base + t)] = e;
-      tiles[2 * (base + t) + 1] = off[e] + t * QBM;
+      tiles[2 * (base + t) + 1] = off[e] + t * bm;
     }
   }
 }
@@ -452,23 +453,37 @@ __device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t w, float s_b) {
   return r;
 }
 
-__global__ __launch_bounds__(256, 2) void k_qat_fwd2(QatParams p) {
-  __shared__ __attribute__((aligned(16))) uint4 lds[2][FBM * 16];
-  // XCD-aware order over the real tiles (groups of 4 row tiles x all column
-  // tiles, each XCD a contiguous range); surplus workgroups exit.
+// E4M3 code (0..0x7E) -> fp32 without branches: (8 [e > 0] + m) 2^(max(e, 1) - 10),
+// always a normal fp32 (smallest nonzero 2^-9).
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  const uint32_t e = (code >> 3) & 0xFu, m = code & 7u;
+  const uint32_t mant = m | (e != 0u ? 8u : 0u);
+  return __builtin_amdgcn_ldexpf((float)mant, (int)(e != 0u ? e : 1u) - 10);
+}
+
+// XCD-aware order over the real tiles: groups of 4 row tiles x all column
+// tiles, each of the 8 XCDs (blockIdx.x % 8) takes a contiguous range of the
+// order.  False for surplus workgroups.
+__device__ __forceinline__ bool pick_tile(const QatParams& p, int& mt, int& nt) {
   const int n_mt = min(*p.ntiles, p.max_tiles);
   const int n_groups = (n_mt + 3) / 4;
   const int total = n_groups * 4 * p.n_tiles_n;
   const int per = (total + 7) / 8;
   const int slot = blockIdx.x >> 3;
-  if (slot >= per) return;
+  if (slot >= per) return false;
   const int logical = (blockIdx.x & 7) * per + slot;
-  if (logical >= total) return;
+  if (logical >= total) return false;
   const int group_span = 4 * p.n_tiles_n;
   const int grp = logical / group_span, rem = logical - grp * group_span;
-  const int mt = 4 * grp + (rem & 3);
-  const int nt = rem >> 2;
-  if (mt >= n_mt) return;
+  mt = 4 * grp + (rem & 3);
+  nt = rem >> 2;
+  return mt < n_mt;
+}
+
+__global__ __launch_bounds__(256, 2) void k_qat_fwd2(QatParams p) {
+  __shared__ __attribute__((aligned(16))) uint4 lds[2][FBM * 16];
+  int mt, nt;
+  if (!pick_tile(p, mt, nt)) return;
   const int e = p.tiles[2 * mt];
   const int64_t row0 = p.tiles[2 * mt + 1];
   const int64_t row_end = p.off[e + 1];
@@ -529,7 +544,7 @@ __global__ __launch_bounds__(256, 2) void k_qat_fwd2(QatParams p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) sb[j][b] = e4m3_to_f32((S.bs[j] >> (8 * b)) & 0xFFu);
+      for (int b = 0; b < 4; ++b) sb[j][b] = e4m3_value((S.bs[j] >> (8 * b)) & 0xFFu);
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       bf16x8_t af[4], bf[2];
@@ -599,6 +614,194 @@ __global__ __launch_bounds__(256, 2) void k_qat_fwd2(QatParams p) {
     }
 }
 
+// ------------------------------------------------ input gradient, 2 WG/CU --
+// dx[p, c] = sum_n dy[p, n] W^_e[n, c]: the contraction runs over the
+// weight's rows, so an MFMA lane (8 consecutive contraction values of one
+// column) needs a column strip of W.  Workgroup = 4 waves = 256 sorted rows x
+// 128 output columns; wave = 64 rows x 128 columns as 4 x 8 tiles of the
+// 16x16x32 bf16 MFMA (accumulators in VGPRs).
+//  * The weight tile of a step (128 rows n x 128 columns c, FP4) is
+//    dequantized once per workgroup, exactly, and written transposed as bf16
+//    into a double-buffered LDS tile [c][n] (256-byte rows, 16-byte chunk n/8
+//    stored at slot (n/8) ^ (c & 15)).  Thread t takes rows 4 (t & 31) .. +3
+//    and columns 16 (t >> 5) .. +15: one block scale per row.
+//  * dy rows are private to a wave, so lanes keep their fragments in
+//    registers.  In the 16x16x32 layout lane (l16, g) holds row l16 and
+//    contraction values 32 d + 8 g .. +8 of sub-step d, so the four lanes of a
+//    row read 64 contiguous bytes (one load instruction touches 16 rows, not
+//    32 rows x 2 as the 32x32 layout would).  Fragments roll two sub-steps
+//    ahead.
+constexpr int DBM = 256, DBN = 128, DSE = 128;
+
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+struct WStage {
+  uint2 c[4];
+  uint32_t s[4];
+};
+
+template <int kSel>
+__device__ __forceinline__ void fp4_pair_rows(const uint32_t (&w)[4], const float (&sb)[4],
+                                              float (&f)[4][2]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    auto g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[r], 1.0f, kSel);
+    f[r][0] = g[0] * sb[r];
+    f[r][1] = g[1] * sb[r];
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void k_qat_dgrad2(QatParams p) {
+  __shared__ __attribute__((aligned(16))) uint4 wt[2][DBN * 16];
+  int mt, nt;
+  if (!pick_tile(p, mt, nt)) return;
+  const int e = p.tiles[2 * mt];
+  const int64_t row0 = p.tiles[2 * mt + 1];
+  const int64_t row_end = p.off[e + 1];
+  const int64_t Nc = p.N, Ko = p.K;  // contraction length, output columns
+  const int64_t c0 = (int64_t)nt * DBN;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, l16 = lane & 15, g = lane >> 4;
+  const int nst = (int)(Nc / DSE);
+
+  // Addresses are a uniform base plus a 32-bit per-lane byte offset (the
+  // tile's 256 rows of dy; one expert's weight, < 2 GiB by the host check).
+  const char* const dy_t = reinterpret_cast<const char*>(p.dy + row0 * Nc);
+  uint32_t a_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t pr = min<int64_t>(row0 + 64 * wave + 16 * i + l16, row_end - 1);
+    a_off[i] = (uint32_t)(((pr - row0) * Nc + 8 * g) * 2);
+  }
+  auto a_frag = [&](int i, int64_t u) {  // element u of the step sequence
+    return *reinterpret_cast<const bf16x8_t*>(dy_t + 2 * u + a_off[i]);
+  };
+  // weight rows and column block of this thread (columns past K read the last
+  // valid block; their outputs are never stored)
+  const int q = t & 31, cb = t >> 5;
+  const int64_t cw = min<int64_t>(c0 + 16 * cb, Ko - 16);
+  const uint8_t* const w_e = p.w_codes + (int64_t)e * Nc * (Ko >> 1);
+  const uint8_t* const s_e = p.w_scales + (int64_t)e * Nc * (Ko >> 4);
+  const uint32_t w_off = (uint32_t)(4 * q * (Ko >> 1) + (cw >> 1));
+  const uint32_t s_off = (uint32_t)(4 * q * (Ko >> 4) + (cw >> 4));
+  auto w_load = [&](WStage& W, int step) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = (int64_t)step * DSE + r;
+      W.c[r] = *reinterpret_cast<const uint2*>(w_e + row * (Ko >> 1) + w_off);
+      W.s[r] = *(s_e + row * (Ko >> 4) + s_off);
+    }
+  };
+  char* const wt_base = reinterpret_cast<char*>(&wt[0][0]);
+  auto w_store = [&](const WStage& W, int buf) {
+    float sb[4];
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sb[r] = e4m3_value(W.s[r]);
+      lo[r] = W.c[r].x;
+      hi[r] = W.c[r].y;
+    }
+    char* const dst = wt_base + buf * (DBN * 256) + 8 * (q & 1);
+    auto put = [&](const float (&f)[4][2], int u) {  // columns u, u + 1 of the block
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int c = 16 * cb + u + k;
+        uint2 v;
+        v.x = __builtin_amdgcn_perm(__float_as_uint(f[1][k]), __float_as_uint(f[0][k]), 0x07060302u);
+        v.y = __builtin_amdgcn_perm(__float_as_uint(f[3][k]), __float_as_uint(f[2][k]), 0x07060302u);
+        *reinterpret_cast<uint2*>(dst + c * 256 + 16 * ((q >> 1) ^ (c & 15))) = v;
+      }
+    };
+    float f[4][2];
+    fp4_pair_rows<0>(lo, sb, f); put(f, 0);
+    fp4_pair_rows<1>(lo, sb, f); put(f, 2);
+    fp4_pair_rows<2>(lo, sb, f); put(f, 4);
+    fp4_pair_rows<3>(lo, sb, f); put(f, 6);
+    fp4_pair_rows<0>(hi, sb, f); put(f, 8);
+    fp4_pair_rows<1>(hi, sb, f); put(f, 10);
+    fp4_pair_rows<2>(hi, sb, f); put(f, 12);
+    fp4_pair_rows<3>(hi, sb, f); put(f, 14);
+  };
+
+  floatx4_t acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
+
+  // dy fragments of sub-step u = 4 st + d live in slot u % 2
+  bf16x8_t a[2][4];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[s2][i] = a_frag(i, 32 * s2);
+
+  // One step: MFMAs over LDS buffer st % 2; with next the weight tile of step
+  // st + 1 is loaded first and dequantized into the other buffer after the
+  // MFMAs.  Scheduling barriers between sub-steps keep every load where it is
+  // issued (the scheduler otherwise sinks them next to their use).
+  auto step = [&](int st, WStage& W, bool next) {
+    const int buf = st & 1;
+    const char* const src = wt_base + buf * (DBN * 256);
+    if (next) w_load(W, st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int jh = 0; jh < 2; ++jh) {
+        bf16x8_t bfr[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int c = 16 * (4 * jh + jj) + l16;
+          bfr[jj] = *reinterpret_cast<const bf16x8_t*>(src + c * 256 + 16 * ((4 * d + g) ^ (c & 15)));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            acc[i][4 * jh + jj] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[d & 1][i], bfr[jj], acc[i][4 * jh + jj], 0, 0, 0);
+      }
+      if (d < 2 || next) {
+        const int64_t u = (int64_t)st * DSE + 32 * ((d + 2) & 3) + (d < 2 ? 0 : DSE);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[d & 1][i] = a_frag(i, u);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (next) w_store(W, buf ^ 1);
+  };
+
+  WStage W;
+  w_load(W, 0);
+  w_store(W, 0);
+  __syncthreads();
+  for (int st = 0; st + 1 < nst; ++st) {
+    step(st, W, true);
+    __syncthreads();
+  }
+  step(nst - 1, W, false);
+
+  const float stw = p.w_st[e];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t pr = row0 + 64 * wave + 16 * i + 4 * g + v;
+      if (pr >= row_end) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t c = c0 + 16 * j + l16;
+        if (c >= Ko) continue;
+        const float y = acc[i][j][v] * stw;
+        if (p.out_f32) p.out_f32[pr * Ko + c] = y;
+        if (p.out_bf16) p.out_bf16[pr * Ko + c] = (uint16_t)f32_to_bf16_rne(y);
+      }
+    }
+}
+
 struct QatLayout {
   int max_tiles;
   int32_t* tiles;
@@ -664,9 +867,20 @@ extern "C" int qat_fakequant_gemm_w4a16(const nvq_qat_gemm_args* a, void* stream
     return last_launch();
   }
   if (a->rows == 0) return NVQ_OK;
+  // input gradient with 256-row tiles when the contraction (N) splits into
+  // 128-element steps; everything else tiles rows by 128
+  const bool dgrad2 = a->mode == NVQ_QAT_DGRAD && a->N % DSE == 0 && ((uintptr_t)a->w_codes & 7u) == 0 &&
+                      a->N * (a->K / 2) < ((int64_t)1 << 31) && (int64_t)DBM * a->N * 2 < ((int64_t)1 << 31);
   hipLaunchKernelGGL(k_qat_tile_table, dim3(1), dim3(1024), 0, s, a->expert_offsets, (int)a->E,
-                     L.tiles, L.ntiles, L.max_tiles);
+                     L.tiles, L.ntiles, L.max_tiles, dgrad2 ? DBM : QBM);
   if (int rc = last_launch()) return rc;
+  if (dgrad2) {
+    p.n_tiles_n = (int)((a->K + DBN - 1) / DBN);
+    const int64_t mt = (a->rows + DBM - 1) / DBM + a->E;
+    const int64_t G2 = ((mt + 3) / 4 * 4 * p.n_tiles_n + 7) / 8 * 8;
+    hipLaunchKernelGGL(k_qat_dgrad2, dim3((unsigned)G2), dim3(256), 0, s, p);
+    return last_launch();
+  }
   p.n_tiles_m = 0;
   const int64_t cols = (a->mode == NVQ_QAT_FWD) ? a->N : a->K;
   p.n_tiles_n = (int)((cols + QBN - 1) / QBN);

@@ -100,13 +100,16 @@ def test_small_qat_all_modes(proj):
 
 
 @pytest.mark.parametrize("K,N,counts", [
-    (128, 96, (0, 77, 130)),              # one contraction step, partial column tile, empty expert
-    (384, 160, (1, 0, 129, 255, 3)),      # odd step count, ragged row tiles
-    (640, 288, (128, 0, 0, 200)),         # five steps, column tile + 32-column tail
+    (128, 96, (0, 77, 130)),              # one forward step, partial column tile, empty expert
+    (384, 160, (1, 0, 129, 255, 3)),      # odd forward step count, ragged row tiles
+    (640, 288, (128, 0, 0, 200)),         # five forward steps, column tile + 32-column tail
+    (160, 384, (300, 0, 257, 1)),         # three input-gradient steps, 32-column tail
+    (96, 128, (0, 513, 40)),              # one input-gradient step, partial column tile
 ])
-def test_forward_edge_shapes(K, N, counts):
-    """Forward on shapes off the tile grid: row tiles cut by expert ends, empty
-    experts, odd and single contraction-step counts, partial column tiles."""
+def test_fwd_dgrad_edge_shapes(K, N, counts):
+    """Forward and input gradient on shapes off the tile grid: row tiles cut by
+    expert ends, empty experts, odd and single contraction-step counts,
+    partial column tiles (both the 128-step kernels and the 32-step one)."""
     import torch
 
     nvq = _nvq()
@@ -117,27 +120,36 @@ def test_forward_edge_shapes(K, N, counts):
     row_e = np.repeat(np.arange(E), counts).astype(np.int32)
     x_row = g.integers(0, T, P).astype(np.int32)
     x = inputs.to_bf16_bits(g.standard_normal((T, K)).astype(np.float32))
+    dy = inputs.to_bf16_bits(g.standard_normal((P, N)).astype(np.float32))
     wm = inputs.to_bf16_bits((0.02 * g.standard_normal((E, N, K))).astype(np.float32))
     q = nvq.nvfp4_quantize(to_gpu(wm))
-    yb, yf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_FWD, *q[:3], to_gpu(off), P, x=to_gpu(x),
+    offg = to_gpu(off)
+    yb, yf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_FWD, *q[:3], offg, P, x=to_gpu(x),
                                          a_row=to_gpu(x_row), want_f32=True)
+    dxb, dxf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *q[:3], offg, P, dy=to_gpu(dy),
+                                           want_f32=True)
     torch.cuda.synchronize()
     wq = [oracle.quantize(wm[e]) for e in range(E)]
     wc = np.stack([w[0] for w in wq])
     assert_bits_equal(to_np(q[0]), wc, "weight cache codes")
     wsc = np.stack([w[1] for w in wq])
     wst = np.array([w[2] for w in wq], np.float32)
-    ref = oracle.qat_fwd(x, x_row, row_e, wc, wsc, wst)
-    y = to_np(yf)
+    ref_y = oracle.qat_fwd(x, x_row, row_e, wc, wsc, wst)
+    ref_dx = oracle.qat_dgrad(dy, np.arange(P), row_e, wc, wsc, wst)
+    y, dx = to_np(yf), to_np(dxf)
     X = inputs.bf16_bits_to_f32(x).astype(np.float64)
+    DY = inputs.bf16_bits_to_f32(dy).astype(np.float64)
     for e in range(E):
         rows = slice(off[e], off[e + 1])
         if off[e + 1] == off[e]:
             continue
         W = oracle.dequantize(wc[e], wsc[e], wst[e]).astype(np.float64)
-        _norm_err(y[rows], ref[rows], np.linalg.norm(X[x_row[rows]], axis=1),
+        _norm_err(y[rows], ref_y[rows], np.linalg.norm(X[x_row[rows]], axis=1),
                   np.linalg.norm(W, axis=1), f"fwd K={K} N={N} e={e}")
+        _norm_err(dx[rows], ref_dx[rows], np.linalg.norm(DY[rows], axis=1),
+                  np.linalg.norm(W, axis=0), f"dgrad K={K} N={N} e={e}")
     np.testing.assert_array_equal(to_np(yb), inputs.to_bf16_bits(y))
+    np.testing.assert_array_equal(to_np(dxb), inputs.to_bf16_bits(dx))
 
 
 def test_forward_uses_the_cached_rounding():
