@@ -802,6 +802,240 @@ __global__ __launch_bounds__(256, 2) void k_qat_dgrad2(QatParams p) {
     }
 }
 
+// ------------------------------------------------- weight gradient, 2 WG/CU --
+// dW[e, n, c] (+)= sum_{p of e} dy[p, n] x[a_row[p], c]: the contraction runs
+// over the rows of both operands.  Workgroup = 4 waves = 128 n x 256 c of one
+// expert; wave (wn, wc) = 64 n x 128 c as 2 x 4 tiles of the 32x32x16 bf16
+// MFMA.  A step takes 32 contraction rows: dy[32][128] (8 KB) and the gathered
+// x[32][256] (16 KB) stream from global memory into LDS with direct loads,
+// in their natural row layout, three stages deep.  The MFMA operands (8
+// consecutive contraction rows of one column) come out of those row-major
+// tiles through the LDS transpose read ds_read_b64_tr_b16: in each group of
+// 16 lanes, lane i receives element i % 4 of the 8-byte reads of lanes
+// i / 4 + 4 m, m = 0..3, so source lane s points at 4 consecutive columns of
+// contraction row k0 + s / 4.  16-byte chunk c of tile row r is stored at
+// slot c ^ (2 (r & 7)): the 4 rows x 32 bytes of one 16-lane read fall in
+// distinct banks.  Rows past the expert's end are zeroed in LDS by the wave
+// that loaded them.
+// The direct loads are issued from inline assembly and ordered by explicit
+// waits: a compiler-visible one makes the compiler drain every load before
+// any LDS read, which would empty the pipeline.  The x row indices of a step
+// (a_row) are themselves staged into LDS by a direct load one step earlier
+// than the step's tiles, ahead of them in issue order, so the only vector
+// memory operations in the loop are these direct loads.
+constexpr int GBN = 128, GBC = 256, GPS = 32;
+constexpr int G_DY = GPS * GBN * 2, G_X = GPS * GBC * 2, G_TOK = 256;
+constexpr int G_STAGE = G_DY + G_X + G_TOK;
+
+#define NVQ_LDS __attribute__((address_space(3)))
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t tr_pair(const NVQ_LDS char* base, uint32_t off0, uint32_t off1) {
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((NVQ_LDS v4i16_t*)(base + off0));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((NVQ_LDS v4i16_t*)(base + off1));
+  typedef short v8i16_t __attribute__((ext_vector_type(8)));
+  const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Global -> LDS direct loads; lane l lands at LDS byte lds_addr + size * l
+// (lds_addr wave-uniform).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
+}
+
+__global__ __launch_bounds__(256, 2) void k_qat_wgrad2(QatParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[3 * G_STAGE];
+  const int n_tn = p.n_tiles_m, n_tc = p.n_tiles_n;
+  const int per_e = n_tn * n_tc;
+  const int total = (int)p.E * per_e;
+  const int per = (total + 7) / 8;
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per) return;
+  const int logical = (blockIdx.x & 7) * per + slot;  // XCD blockIdx % 8 takes a contiguous range
+  if (logical >= total) return;
+  const int e = logical / per_e, rem = logical - e * per_e;
+  const int tn = rem / n_tc, tc = rem - tn * n_tc;
+  const int64_t N = p.N, K = p.K, rows = p.rows;
+  const int64_t n0 = (int64_t)tn * GBN, c0 = (int64_t)tc * GBC;
+  const int64_t p_beg = p.off[e], p_end = p.off[e + 1];
+  const int nsteps = (int)((p_end - p_beg + GPS - 1) / GPS);
+  const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, h = lane >> 5, s16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wn = wave & 1, wc = wave >> 1;
+
+  floatx16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  if (nsteps > 0) {
+    NVQ_LDS char* const lb = (NVQ_LDS char*)lds;
+    const uint32_t lb_addr = (uint32_t)(uintptr_t)lb;
+    // loads of this lane: dy instructions 2 wave + k (rows 4 I + lane / 16,
+    // 16 slots a row), x instructions 4 wave + k (rows 2 I + lane / 32, 32
+    // slots a row); every row is clamped into [0, rows) and every column
+    // chunk into the matrix (rows past the expert's end are zeroed later,
+    // columns past N or K are never stored)
+    int dy_r[2], x_r[4];
+    int64_t dy_col[2], x_col[4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int I = 2 * wave + k, r = 4 * I + (lane >> 4);
+      dy_r[k] = r;
+      dy_col[k] = min<int64_t>(n0 + 8 * ((lane & 15) ^ (2 * (r & 7))), N - 8);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int I = 4 * wave + k, r = 2 * I + (lane >> 5);
+      x_r[k] = r;
+      x_col[k] = min<int64_t>(c0 + 8 * ((lane & 31) ^ (2 * (r & 7))), K - 8);
+    }
+    auto prow = [&](int st, int r) { return min<int64_t>(p_beg + (int64_t)st * GPS + r, rows - 1); };
+    auto stage_of = [](int st) { return st % 3; };
+    // x row indices of step st -> the tok area of its stage (wave 0; lanes
+    // 32..63 repeat rows 0..31)
+    auto issue_tok = [&](int st) {
+      if (wave == 0 && p.a_row)
+        dma4(p.a_row + prow(st, l32), lb_addr + stage_of(st) * G_STAGE + G_DY + G_X);
+    };
+    auto issue = [&](int st) {
+      const int sg = stage_of(st);
+      const uint32_t base = lb_addr + sg * G_STAGE;
+      const NVQ_LDS int32_t* tok_lds = (const NVQ_LDS int32_t*)(lb + sg * G_STAGE + G_DY + G_X);
+      int64_t tok[4];  // read before the first load is issued (the loads order all memory)
+      if (p.a_row) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tok[k] = tok_lds[x_r[k]];
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tok[k] = prow(st, x_r[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        dma16(p.dy + prow(st, dy_r[k]) * N + dy_col[k], base + 1024 * (2 * wave + k));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dma16(p.x + tok[k] * K + x_col[k], base + G_DY + 1024 * (4 * wave + k));
+    };
+    // rows of step st past the expert's end -> zero (this lane's own slots)
+    auto zero_tail = [&](int st) {
+      const int64_t nvalid = p_end - p_beg - (int64_t)st * GPS;
+      if (nvalid >= GPS) return;
+      NVQ_LDS char* const base = lb + stage_of(st) * G_STAGE;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (dy_r[k] >= nvalid)
+          *(NVQ_LDS u32x4_t*)(base + 1024 * (2 * wave + k) + 16 * lane) = u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (x_r[k] >= nvalid)
+          *(NVQ_LDS u32x4_t*)(base + G_DY + 1024 * (4 * wave + k) + 16 * lane) = u32x4_t{0, 0, 0, 0};
+    };
+
+    // transpose-read offsets: operand row (n or c) base of this lane's group,
+    // 4 columns per source lane; contraction row k0 + s16 / 4
+    uint32_t a_off[2][2], b_off[4][2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int r = 8 * h + 4 * hf + (s16 >> 2);  // contraction row within a 16-row sub-step
+      const int f = 2 * (r & 7);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int col = 64 * wn + 32 * i + 16 * (l32 >> 4) + 4 * (s16 & 3);
+        a_off[i][hf] = (uint32_t)(r * (GBN * 2) + 16 * ((col >> 3) ^ f) + 8 * ((col >> 2) & 1));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = 128 * wc + 32 * j + 16 * (l32 >> 4) + 4 * (s16 & 3);
+        b_off[j][hf] = (uint32_t)(G_DY + r * (GBC * 2) + 16 * ((col >> 3) ^ f) + 8 * ((col >> 2) & 1));
+      }
+    }
+    auto compute = [&](int st) {
+      const NVQ_LDS char* const base = lb + stage_of(st) * G_STAGE;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        bf16x8_t af[2], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          af[i] = tr_pair(base + sub * 16 * (GBN * 2), a_off[i][0], a_off[i][1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bfr[j] = tr_pair(base + sub * 16 * (GBC * 2), b_off[j][0], b_off[j][1]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    };
+    auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+    // prologue: row indices of steps 0..2, then the tiles of steps 0 and 1
+    issue_tok(0);
+    if (nsteps > 1) issue_tok(1);
+    if (nsteps > 2) issue_tok(2);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier();
+    issue(0);
+    if (nsteps > 1) {
+      issue(1);
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");  // step 0 landed
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      zero_tail(0);
+    }
+    barrier();
+
+    // step st: [row indices of st + 3][tiles of st + 2] are issued, step st
+    // is computed, then the tiles of st + 1 (and every older load) must have
+    // landed while the 6 tile loads of st + 2 may still be in flight
+    for (int st = 0; st < nsteps; ++st) {
+      const bool ahead = st + 2 < nsteps;
+      if (ahead) {
+        if (st + 3 < nsteps) issue_tok(st + 3);
+        issue(st + 2);
+      }
+      compute(st);
+      if (st + 1 < nsteps) {
+        if (ahead)
+          asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (st + 1 == nsteps - 1) zero_tail(st + 1);
+        barrier();
+      }
+    }
+  } else if (p.accumulate) {
+    return;  // no rows: dW unchanged
+  }
+
+  // one 32 x 32 tile at a time: with accumulate its 16 old values are loaded
+  // together, then added and stored
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = c0 + 128 * wc + 32 * j + l32;
+      const int64_t nb = n0 + 64 * wn + 32 * i + 4 * h;
+      float* const d = p.dw + ((int64_t)e * N + nb) * K + c;
+      auto idx = [&](int v) { return (int64_t)(8 * (v >> 2) + (v & 3)); };
+      auto ok = [&](int v) { return c < K && nb + idx(v) < N; };
+      float old[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) old[v] = (p.accumulate && ok(v)) ? d[idx(v) * K] : 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (ok(v)) d[idx(v) * K] = old[v] + acc[i][j][v];
+    }
+}
+
 struct QatLayout {
   int max_tiles;
   int32_t* tiles;
@@ -862,8 +1096,11 @@ extern "C" int qat_fakequant_gemm_w4a16(const nvq_qat_gemm_args* a, void* stream
     p.n_tiles_n = (int)((a->K + QBN - 1) / QBN);
     const int64_t G0 = a->E * p.n_tiles_m * p.n_tiles_n;
     const int64_t G = (G0 + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_qat_gemm<NVQ_QAT_WGRAD, LD_ROWS_T, LD_ROWS_T>), dim3((unsigned)G), dim3(QT), 0,
-                       s, p);
+    if (a->rows > 0)  // transpose-read kernel (its tiles equal the 32-step kernel's)
+      hipLaunchKernelGGL(k_qat_wgrad2, dim3((unsigned)G), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((k_qat_gemm<NVQ_QAT_WGRAD, LD_ROWS_T, LD_ROWS_T>), dim3((unsigned)G), dim3(QT), 0,
+                         s, p);
     return last_launch();
   }
   if (a->rows == 0) return NVQ_OK;

@@ -107,9 +107,11 @@ def test_small_qat_all_modes(proj):
     (96, 128, (0, 513, 40)),              # one input-gradient step, partial column tile
 ])
 def test_fwd_dgrad_edge_shapes(K, N, counts):
-    """Forward and input gradient on shapes off the tile grid: row tiles cut by
-    expert ends, empty experts, odd and single contraction-step counts,
-    partial column tiles (both the 128-step kernels and the 32-step one)."""
+    """Forward, input and weight gradient on shapes off the tile grid: row
+    tiles cut by expert ends, empty experts, odd and single contraction-step
+    counts, partial column tiles (both the 128-step kernels and the 32-step
+    one), expert segments of 1 and 3 rows and ragged 32-row weight-gradient
+    steps, weight gradient accumulated."""
     import torch
 
     nvq = _nvq()
@@ -128,6 +130,11 @@ def test_fwd_dgrad_edge_shapes(K, N, counts):
                                          a_row=to_gpu(x_row), want_f32=True)
     dxb, dxf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *q[:3], offg, P, dy=to_gpu(dy),
                                            want_f32=True)
+    dw = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *q[:3], offg, P, x=to_gpu(x),
+                                      dy=to_gpu(dy), a_row=to_gpu(x_row))
+    dw2 = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *q[:3], offg, P, x=to_gpu(x),
+                                       dy=to_gpu(dy), a_row=to_gpu(x_row), dw=dw.clone(),
+                                       accumulate=True)
     torch.cuda.synchronize()
     wq = [oracle.quantize(wm[e]) for e in range(E)]
     wc = np.stack([w[0] for w in wq])
@@ -148,6 +155,17 @@ def test_fwd_dgrad_edge_shapes(K, N, counts):
                   np.linalg.norm(W, axis=1), f"fwd K={K} N={N} e={e}")
         _norm_err(dx[rows], ref_dx[rows], np.linalg.norm(DY[rows], axis=1),
                   np.linalg.norm(W, axis=0), f"dgrad K={K} N={N} e={e}")
+    dwn = to_np(dw)
+    nn, cc = np.meshgrid(np.arange(N), np.arange(K), indexing="ij")
+    for e in range(E):
+        rows = slice(off[e], off[e + 1])
+        if off[e + 1] == off[e]:  # no rows: the gradient is zero
+            assert not dwn[e].any(), f"wgrad of empty expert {e} not zero"
+            continue
+        ref_w = oracle.qat_wgrad(dy, x, x_row, off[e], off[e + 1], nn.ravel(), cc.ravel())
+        _norm_err(dwn[e], ref_w.reshape(N, K), np.linalg.norm(DY[rows], axis=0),
+                  np.linalg.norm(X[x_row[rows]], axis=0), f"wgrad K={K} N={N} e={e}")
+    np.testing.assert_allclose(to_np(dw2), 2 * dwn, rtol=1e-6, atol=1e-6)
     np.testing.assert_array_equal(to_np(yb), inputs.to_bf16_bits(y))
     np.testing.assert_array_equal(to_np(dxb), inputs.to_bf16_bits(dx))
 
