@@ -137,7 +137,8 @@ class MoeLeg:
     """One W4A4 MoE layer with residual compensation: route, permute, quantize X
     (+ residual scores), top-k channels + residual columns, gate/up grouped GEMM
     with SwiGLU epilogue, quantize H (+ scores), top-k + residuals, down grouped
-    GEMM, combine.  Expert weights are quantized once outside the timed step
+    GEMM, combine.  Expert weights are quantized (and their channel-major copy
+    made) once outside the timed step
     (they are static during a rollout)."""
 
     def __init__(self, shape):
@@ -152,11 +153,13 @@ class MoeLeg:
         log(f"[bench] {self.name}: generating inputs")
         self.logits = torch.from_numpy(inputs.logits(s)).to(dev)
         self.x = torch.from_numpy(inputs.activations(s).view(np.int16)).view(torch.bfloat16).to(dev)
-        self.qw = {}
+        self.qw, self.wcm = {}, {}
         for proj in ("gu", "dn"):
             w = inputs.weights_device(s, proj, dev)
             codes, scales, st, _, _ = nvq.nvfp4_quantize(w)
             self.qw[proj] = (codes, scales, st)
+            # channel-major copy for the compensation gather, made with the record
+            self.wcm[proj] = nvq.nvfp4_channel_major(codes, scales)
             del w
         torch.cuda.synchronize()
         P, H, I, k = s.P, s.H, s.I, s.k
@@ -186,7 +189,8 @@ class MoeLeg:
         return nvq.moe_grouped_gemm_w4a4_comp(
             a[0], a[1], a[2], codes, scales, st, self.off, rows=rows, a_row=a_row,
             a_resid=resid if comp else None, comp_idx=idx if comp else None, epilogue=epi,
-            ws=self.ws_g, a_row_div=self.s.topk if a_row is not None else 0, out=out, path=path)
+            ws=self.ws_g, a_row_div=self.s.topk if a_row is not None else 0, out=out, path=path,
+            w_cm=self.wcm[proj])
 
     def step(self, timer_, comp=True, path=0):
         """path 0: the library's choice (exact fp16 dequantization); 2: the

@@ -191,7 +191,29 @@ typedef struct nvq_moe_gemm_args {
   size_t ws_bytes;
   int32_t a_row_div;             /* > 0: A row of sorted row p is a_row[p] / a_row_div
                                     (pass sorted pair ids with topk); 0: a_row[p] */
+  /* Optional, read only when struct_size covers them: the channel-major copy of
+   * the weight record made by nvfp4_channel_major.  When both are set the
+   * compensation columns are gathered from it (the k selected channels are k
+   * contiguous rows there) instead of from every row of w_codes. */
+  const uint8_t* w_codes_cm;     /* [E, K, N/2] or NULL */
+  const uint8_t* w_scales_cm;    /* [E, K/16, N] or NULL */
 } nvq_moe_gemm_args;
+
+/* Channel-major copy of an NVFP4 weight record (same codes and scales, other
+ * layout), for the compensation gather of moe_grouped_gemm_w4a4_comp: the
+ * correction multiplies the residual by the weight columns of the selected
+ * channels (QUADS §2.2-B), and in the row-major record one column touches
+ * every weight row.  Built once per weight version (the rollout's weights are
+ * static between syncs).
+ *   codes  [batch, N, K/2] (even element in the low nibble) -> codes_cm [batch, K, N/2]
+ *          (row n even in the low nibble)
+ *   scales [batch, N, K/16]                                -> scales_cm [batch, K/16, N]
+ * N % 16 == 0, K % 16 == 0, 1 <= batch <= 65535; codes and codes_cm 8-byte
+ * aligned.  Device pointers, caller-owned, no overlap; asynchronous on stream.
+ * Errors: NVQ_EINVAL (null pointer), NVQ_ESHAPE, NVQ_EALIGN; nothing is
+ * launched then. */
+int nvfp4_channel_major(const uint8_t* codes, const uint8_t* scales, int64_t batch, int64_t N,
+                        int64_t K, uint8_t* codes_cm, uint8_t* scales_cm, void* stream);
 
 /* Workspace: tile table plus the packed compensation weights [E, N, k16] bf16. */
 size_t moe_gemm_workspace_bytes(int64_t rows, int64_t E, int64_t N, int32_t k);

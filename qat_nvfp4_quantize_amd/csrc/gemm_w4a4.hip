@@ -181,6 +181,103 @@ __global__ __launch_bounds__(256) void k_gather_wcomp(const uint8_t* __restrict_
     wcomp[row * kpad + j] = (uint16_t)((j < k) ? w_comp_bf16(cr, sr, idx[j]) : 0u);
 }
 
+// Channel-major copy of a weight record.  Codes: a 64 x 64 (rows n x
+// columns c) tile through LDS; output byte (c, m) packs rows 2m (low nibble)
+// and 2m + 1.  N and K are multiples of 16, so every 16-row or 16-column
+// group is wholly inside or outside the matrix.
+__global__ __launch_bounds__(256) void k_codes_cm(const uint8_t* __restrict__ codes, int64_t N, int64_t K,
+                                                 uint8_t* __restrict__ codes_cm) {
+  __shared__ uint32_t tile[64][9];  // row n: 32 code bytes (64 columns) + pad
+  const int64_t b = blockIdx.z, n0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int t = threadIdx.x;
+  {
+    const int r = t >> 2, q = t & 3;  // row n0 + r, code bytes 8q .. 8q + 7 (columns c0 + 16q ..)
+    uint2 v = make_uint2(0u, 0u);
+    if (n0 + r < N && c0 + 16 * q < K)
+      v = *reinterpret_cast<const uint2*>(codes + (b * N + n0 + r) * (K >> 1) + (c0 >> 1) + 8 * q);
+    tile[r][2 * q] = v.x;
+    tile[r][2 * q + 1] = v.y;
+  }
+  __syncthreads();
+  const int c = t >> 2, q = t & 3;  // column c0 + c, output bytes 8q .. 8q + 7 (rows n0 + 16q ..)
+  if (c0 + c >= K || n0 + 16 * q >= N) return;
+  const int sh = 4 * (c & 7);  // nibble of column c in its word
+  uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int n = 16 * q + 2 * m;
+    const uint32_t lo = (tile[n][c >> 3] >> sh) & 15u, hi = (tile[n + 1][c >> 3] >> sh) & 15u;
+    const uint32_t byte = (lo | (hi << 4)) << (8 * (m & 3));
+    if (m < 4) w0 |= byte; else w1 |= byte;
+  }
+  *reinterpret_cast<uint2*>(codes_cm + (b * K + c0 + c) * (N >> 1) + (n0 >> 1) + 8 * q) = make_uint2(w0, w1);
+}
+
+// Scales [b, N, K/16] -> [b, K/16, N]: a 64 x 64 byte transpose through LDS.
+__global__ __launch_bounds__(256) void k_scales_cm(const uint8_t* __restrict__ scales, int64_t N, int64_t KB,
+                                                  uint8_t* __restrict__ scales_cm) {
+  __shared__ uint8_t tile[64][65];
+  const int64_t b = blockIdx.z, n0 = (int64_t)blockIdx.y * 64, s0 = (int64_t)blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i >> 6, cc = i & 63;
+    tile[r][cc] = (n0 + r < N && s0 + cc < KB) ? scales[(b * N + n0 + r) * KB + s0 + cc] : (uint8_t)0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i >> 6, r = i & 63;
+    if (s0 + cc < KB && n0 + r < N) scales_cm[(b * KB + s0 + cc) * N + n0 + r] = tile[r][cc];
+  }
+}
+
+// bf16 bits of G * s_b for code nibble nib and E4M3 scale byte sc (exact).
+__device__ __forceinline__ uint32_t wq_bf16(uint32_t nib, uint32_t sc) {
+  const float v = e2m1_mag(nib & 7u) * e4m3_to_f32(sc);
+  return (__float_as_uint(v) >> 16) | ((nib & 8u) << 12);
+}
+
+// The compensation weights from the channel-major record: wcomp[e, n, j] =
+// bf16 of G * s_b at channel idx[j] (0 for j >= k).  Thread = rows n, n + 1
+// of one expert and channels 8 q .. 8 q + 7 (blockIdx.y = q): eight
+// independent (code byte, two scale bytes) loads from those channels'
+// contiguous rows, then one 16-byte store per row.  Lanes run along n, so
+// every load instruction reads consecutive bytes.
+__global__ __launch_bounds__(256) void k_gather_wcomp_cm(const uint8_t* __restrict__ codes_cm,
+                                                        const uint8_t* __restrict__ scales_cm, int64_t N,
+                                                        int64_t K, const int32_t* __restrict__ idx, int k,
+                                                        int kpad, uint16_t* __restrict__ wcomp) {
+  const int64_t e = blockIdx.z;
+  const int j0 = 8 * (int)blockIdx.y;
+  const int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+  if (n >= N || j0 >= kpad) return;
+  const uint8_t* cb = codes_cm + e * K * (N >> 1) + (n >> 1);
+  const uint8_t* sb = scales_cm + e * (K >> 4) * N + n;
+  uint32_t byte[8], sc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    byte[u] = 0u;
+    sc[u] = 0u;
+    if (j0 + u < k) {
+      const int64_t ch = idx[j0 + u];
+      byte[u] = cb[ch * (N >> 1)];
+      sc[u] = *reinterpret_cast<const uint16_t*>(sb + (ch >> 4) * N);
+    }
+  }
+  uint32_t r0[4], r1[4];
+#pragma unroll
+  for (int u = 0; u < 8; u += 2) {
+    const bool v0 = j0 + u < k, v1 = j0 + u + 1 < k;
+    const uint32_t a0 = v0 ? wq_bf16(byte[u] & 15u, sc[u] & 0xFFu) : 0u;
+    const uint32_t b0 = v0 ? wq_bf16(byte[u] >> 4, sc[u] >> 8) : 0u;
+    const uint32_t a1 = v1 ? wq_bf16(byte[u + 1] & 15u, sc[u + 1] & 0xFFu) : 0u;
+    const uint32_t b1 = v1 ? wq_bf16(byte[u + 1] >> 4, sc[u + 1] >> 8) : 0u;
+    r0[u >> 1] = a0 | (a1 << 16);
+    r1[u >> 1] = b0 | (b1 << 16);
+  }
+  uint16_t* o0 = wcomp + (e * N + n) * kpad + j0;
+  *reinterpret_cast<uint4*>(o0) = make_uint4(r0[0], r0[1], r0[2], r0[3]);
+  *reinterpret_cast<uint4*>(o0 + kpad) = make_uint4(r1[0], r1[1], r1[2], r1[3]);
+}
+
 // The tile of this workgroup.  XCD-aware order: the grid is sized for the
 // most row tiles the offsets allow and the real count comes from the tile
 // table.  Workgroups are dealt to the 8 XCDs round-robin, so XCD x =
@@ -641,7 +738,8 @@ extern "C" size_t moe_gemm_workspace_bytes(int64_t rows, int64_t E, int64_t N, i
 }
 
 extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stream) {
-  if (!a || a->struct_size < sizeof(nvq_moe_gemm_args)) return NVQ_EINVAL;
+  if (!a || a->struct_size < offsetof(nvq_moe_gemm_args, w_codes_cm)) return NVQ_EINVAL;
+  const bool has_cm = a->struct_size >= sizeof(nvq_moe_gemm_args) && a->w_codes_cm && a->w_scales_cm;
   if (!a->expert_offsets || !a->a_codes || !a->a_scales || !a->a_tensor_scale || !a->w_codes ||
       !a->w_scales || !a->w_tensor_scale || !a->ws)
     return NVQ_EINVAL;
@@ -673,7 +771,12 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   p.a_codes = a->a_codes; p.a_scales = a->a_scales; p.a_st = a->a_tensor_scale;
   p.a_resid = a->a_resid; p.comp_idx = a->comp_idx; p.k = a->k;
   p.kpad = L.kpad; p.wcomp = L.wcomp;
-  if (a->k > 0) {
+  if (a->k > 0 && has_cm) {
+    hipLaunchKernelGGL(k_gather_wcomp_cm, dim3((unsigned)((a->N + 511) / 512), (unsigned)(L.kpad / 8), (unsigned)a->E),
+                       dim3(256), 0, s, a->w_codes_cm, a->w_scales_cm, a->N, a->K, a->comp_idx, (int)a->k, L.kpad,
+                       L.wcomp);
+    if (int rc = last_launch()) return rc;
+  } else if (a->k > 0) {
     const int64_t wrows = a->E * a->N;
     hipLaunchKernelGGL(k_gather_wcomp, dim3((unsigned)((wrows + 3) / 4)), dim3(256), 0, s, a->w_codes,
                        a->w_scales, wrows, a->K, a->comp_idx, (int)a->k, L.kpad, L.wcomp);
@@ -701,5 +804,21 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
     else
       hipLaunchKernelGGL(k_moe_gemm_deq16<0>, dim3((unsigned)G), dim3(NTHR), 0, s, p);
   }
+  return last_launch();
+}
+
+extern "C" int nvfp4_channel_major(const uint8_t* codes, const uint8_t* scales, int64_t batch, int64_t N,
+                                   int64_t K, uint8_t* codes_cm, uint8_t* scales_cm, void* stream) {
+  if (!codes || !scales || !codes_cm || !scales_cm) return NVQ_EINVAL;
+  if (batch < 1 || N <= 0 || K <= 0 || (N % 16) || (K % 16)) return NVQ_ESHAPE;
+  if (((uintptr_t)codes & 7u) || ((uintptr_t)codes_cm & 7u)) return NVQ_EALIGN;
+  if (batch > 65535 || (N + 63) / 64 > 65535) return NVQ_ESHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(k_codes_cm, dim3((unsigned)((K + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)batch),
+                     dim3(256), 0, s, codes, N, K, codes_cm);
+  if (int rc = last_launch()) return rc;
+  const int64_t KB = K / 16;
+  hipLaunchKernelGGL(k_scales_cm, dim3((unsigned)((KB + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)batch),
+                     dim3(256), 0, s, scales, N, KB, scales_cm);
   return last_launch();
 }

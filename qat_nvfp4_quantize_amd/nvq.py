@@ -43,7 +43,8 @@ class MoeGemmArgs(ctypes.Structure):
         ("a_scales", _P), ("a_tensor_scale", _P), ("a_resid", _P), ("comp_idx", _P),
         ("k", _I32), ("w_codes", _P), ("w_scales", _P), ("w_tensor_scale", _P),
         ("epilogue", _I32), ("path", _I32), ("out_bf16", _P), ("out_f32", _P),
-        ("ws", _P), ("ws_bytes", _SZ), ("a_row_div", _I32),
+        ("ws", _P), ("ws_bytes", _SZ), ("a_row_div", _I32), ("w_codes_cm", _P),
+        ("w_scales_cm", _P),
     ]
 
 
@@ -71,6 +72,7 @@ _SIGS = [
     ("nvq_moe_permute_workspace_bytes", _SZ, [_I64, _I64, _I64]),
     ("nvq_moe_permute", ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     ("nvq_moe_combine", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    ("nvfp4_channel_major", ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P]),
     ("moe_gemm_workspace_bytes", _SZ, [_I64, _I64, _I64, _I32]),
     ("moe_grouped_gemm_w4a4_comp", ctypes.c_int, [ctypes.POINTER(MoeGemmArgs), _P]),
     ("qat_gemm_workspace_bytes", _SZ, [_I64, _I64]),
@@ -238,11 +240,31 @@ def nvq_moe_combine(y, pos, weights):
 
 
 # ------------------------------------------------------------------- GEMMs --
+def nvfp4_channel_major(codes, scales, out=None):
+    """Channel-major copy of a weight record: codes [B, N, K/2] -> [B, K, N/2],
+    scales [B, N, K/16] -> [B, K/16, N].  Returns (codes_cm, scales_cm)."""
+    _dev(codes, "codes")
+    L = load()
+    if codes.dim() == 2:
+        codes, scales = codes.unsqueeze(0), scales.unsqueeze(0)
+    B, N, Kh = codes.shape
+    K = Kh * 2
+    if out is None:
+        out = (torch.empty(B, K, N // 2, dtype=torch.uint8, device=codes.device),
+               torch.empty(B, K // 16, N, dtype=torch.uint8, device=codes.device))
+    _check("nvfp4_channel_major",
+           L.nvfp4_channel_major(_ptr(codes), _ptr(scales), B, N, K, _ptr(out[0]), _ptr(out[1]),
+                                 _stream()))
+    return out
+
+
 def moe_grouped_gemm_w4a4_comp(a_codes, a_scales, a_tensor_scale, w_codes, w_scales,
                                w_tensor_scale, expert_offsets, rows, a_row=None, a_resid=None,
                                comp_idx=None, epilogue=NVQ_EPI_NONE, path=NVQ_GEMM_AUTO,
-                               want_bf16=True, want_f32=False, ws=None, a_row_div=0, out=None):
-    """Returns (out_bf16 or None, out_f32 or None)."""
+                               want_bf16=True, want_f32=False, ws=None, a_row_div=0, out=None,
+                               w_cm=None):
+    """Returns (out_bf16 or None, out_f32 or None).  w_cm: optional
+    (codes_cm, scales_cm) from nvfp4_channel_major for the compensation gather."""
     L = load()
     E, N, Kh = w_codes.shape
     K = Kh * 2
@@ -271,6 +293,8 @@ def moe_grouped_gemm_w4a4_comp(a_codes, a_scales, a_tensor_scale, w_codes, w_sca
     a.out_bf16, a.out_f32 = _ptr(ob), _ptr(of)
     a.ws, a.ws_bytes = _ptr(ws), ws.numel()
     a.a_row_div = int(a_row_div)
+    if w_cm is not None:
+        a.w_codes_cm, a.w_scales_cm = _ptr(w_cm[0]), _ptr(w_cm[1])
     _check("moe_grouped_gemm_w4a4_comp", L.moe_grouped_gemm_w4a4_comp(ctypes.byref(a), _stream()))
     return ob, of
 

@@ -49,6 +49,10 @@ def test_host_side_validation_launches_nothing():
     L = _lib()
     P = ctypes.c_void_p
     fake = P(0x1000)  # never dereferenced: every call below fails validation first
+    # channel-major relayout: null pointer, N not a multiple of 16, misaligned codes
+    assert L.nvfp4_channel_major(None, fake, 1, 32, 32, fake, fake, None) == -1
+    assert L.nvfp4_channel_major(fake, fake, 1, 24, 32, fake, fake, None) == -2
+    assert L.nvfp4_channel_major(P(0x1004), fake, 1, 32, 32, fake, fake, None) == -3
     # null x
     assert L.nvfp4_quantize(None, 1, 1, 4, 32, None, fake, fake, fake, None, fake, 1 << 20, None) == -1
     # K not a multiple of 16

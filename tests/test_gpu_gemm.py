@@ -242,6 +242,17 @@ def test_grouped_gemm_edge_shapes(K, N, k, epi, path):
         a_resid=resid, comp_idx=idx, epilogue=nvq.NVQ_EPI_SWIGLU if swiglu else nvq.NVQ_EPI_NONE,
         want_f32=True, path=gp, a_row_div=topk)
     torch.cuda.synchronize()
+    if k > 0:
+        # the compensation gathered from the channel-major record: same outputs, bit for bit
+        wcm = nvq.nvfp4_channel_major(qw[0], qw[1])
+        ob2, of2 = nvq.moe_grouped_gemm_w4a4_comp(
+            qa[0], qa[1], qa[2], qw[0], qw[1], qw[2], to_gpu(off), rows=P, a_row=to_gpu(pair),
+            a_resid=resid, comp_idx=idx,
+            epilogue=nvq.NVQ_EPI_SWIGLU if swiglu else nvq.NVQ_EPI_NONE, want_f32=True, path=gp,
+            a_row_div=topk, w_cm=wcm)
+        torch.cuda.synchronize()
+        assert_bits_equal(to_np(of2), to_np(of), "fp32 output with the channel-major record")
+        assert_bits_equal(to_np(ob2), to_np(ob), "bf16 output with the channel-major record")
     oqa = oracle.quantize(x)
     oidx = oracle.topk(oracle.residual_scores(x, *oqa), k) if k > 0 else None
     if k > 0:
@@ -266,3 +277,25 @@ def test_grouped_gemm_edge_shapes(K, N, k, epi, path):
                                    rtol=2 ** -7, atol=1e-6)
     else:
         assert_bits_equal(to_np(ob), inputs.to_bf16_bits(y), "bf16 output = rounded fp32 output")
+
+
+@pytest.mark.parametrize("B,N,K", [(2, 96, 160), (1, 208, 48), (3, 64, 64), (1, 16, 1040)])
+def test_channel_major_record_layout(B, N, K):
+    """nvfp4_channel_major is a pure relayout: random code and scale bytes,
+    compared byte for byte with the same relayout in numpy (partial 64-wide
+    tiles in both directions)."""
+    import torch
+
+    nvq = _nvq()
+    g = np.random.default_rng(B * 7 + N * 3 + K)
+    codes = g.integers(0, 256, (B, N, K // 2), dtype=np.uint8)
+    scales = g.integers(0, 127, (B, N, K // 16), dtype=np.uint8)
+    ccm, scm = nvq.nvfp4_channel_major(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
+    torch.cuda.synchronize()
+    nib = np.empty((B, N, K), np.uint8)
+    nib[..., 0::2] = codes & 15
+    nib[..., 1::2] = codes >> 4
+    t = nib.transpose(0, 2, 1)  # [B, K, N]
+    want_codes = (t[..., 0::2] | (t[..., 1::2] << 4)).astype(np.uint8)
+    assert_bits_equal(to_np(ccm), want_codes, "channel-major codes")
+    assert_bits_equal(to_np(scm), np.ascontiguousarray(scales.transpose(0, 2, 1)), "channel-major scales")
