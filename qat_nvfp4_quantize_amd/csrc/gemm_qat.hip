@@ -804,11 +804,14 @@ __global__ __launch_bounds__(256, 2) void k_qat_dgrad2(QatParams p) {
 
 // ------------------------------------------------- weight gradient, 2 WG/CU --
 // dW[e, n, c] (+)= sum_{p of e} dy[p, n] x[a_row[p], c]: the contraction runs
-// over the rows of both operands.  Workgroup = 4 waves = 128 n x 256 c of one
-// expert; wave (wn, wc) = 64 n x 128 c as 2 x 4 tiles of the 32x32x16 bf16
-// MFMA.  A step takes 32 contraction rows: dy[32][128] (8 KB) and the gathered
-// x[32][256] (16 KB) stream from global memory into LDS with direct loads,
-// in their natural row layout, three stages deep.  The MFMA operands (8
+// over the rows of both operands.  Workgroup = 8 waves = 256 n x 256 c of one
+// expert (one workgroup per CU); wave (wn, wc) = 64 n x 128 c as 2 x 4 tiles
+// of the 32x32x16 bf16 MFMA.  The square tile halves the re-reads of x
+// against 128 x 256 (every n tile reads the whole x panel of its columns),
+// and the operand re-reads are what bounds this kernel.  A step takes 32
+// contraction rows: dy[32][256] and the gathered x[32][256] (16 KB each)
+// stream from global memory into LDS with direct loads, in their natural row
+// layout, three stages deep.  The MFMA operands (8
 // consecutive contraction rows of one column) come out of those row-major
 // tiles through the LDS transpose read ds_read_b64_tr_b16: in each group of
 // 16 lanes, lane i receives element i % 4 of the 8-byte reads of lanes
@@ -823,7 +826,7 @@ __global__ __launch_bounds__(256, 2) void k_qat_dgrad2(QatParams p) {
 // (a_row) are themselves staged into LDS by a direct load one step earlier
 // than the step's tiles, ahead of them in issue order, so the only vector
 // memory operations in the loop are these direct loads.
-constexpr int GBN = 128, GBC = 256, GPS = 32;
+constexpr int GBN = 256, GBC = 256, GPS = 32;
 constexpr int G_DY = GPS * GBN * 2, G_X = GPS * GBC * 2, G_TOK = 256;
 constexpr int G_STAGE = G_DY + G_X + G_TOK;
 
@@ -848,7 +851,7 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
 }
 
-__global__ __launch_bounds__(256, 2) void k_qat_wgrad2(QatParams p) {
+__global__ __launch_bounds__(512, 1) void k_qat_wgrad2(QatParams p) {
   __shared__ __attribute__((aligned(16))) char lds[3 * G_STAGE];
   const int n_tn = p.n_tiles_m, n_tc = p.n_tiles_n;
   const int per_e = n_tn * n_tc;
@@ -866,7 +869,7 @@ __global__ __launch_bounds__(256, 2) void k_qat_wgrad2(QatParams p) {
   const int nsteps = (int)((p_end - p_beg + GPS - 1) / GPS);
   const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, h = lane >> 5, s16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wn = wave & 1, wc = wave >> 1;
+  const int wn = wave & 3, wc = wave >> 2;
 
   floatx16_t acc[2][4];
 #pragma unroll
@@ -879,23 +882,19 @@ __global__ __launch_bounds__(256, 2) void k_qat_wgrad2(QatParams p) {
   if (nsteps > 0) {
     NVQ_LDS char* const lb = (NVQ_LDS char*)lds;
     const uint32_t lb_addr = (uint32_t)(uintptr_t)lb;
-    // loads of this lane: dy instructions 2 wave + k (rows 4 I + lane / 16,
-    // 16 slots a row), x instructions 4 wave + k (rows 2 I + lane / 32, 32
-    // slots a row); every row is clamped into [0, rows) and every column
-    // chunk into the matrix (rows past the expert's end are zeroed later,
-    // columns past N or K are never stored)
-    int dy_r[2], x_r[4];
-    int64_t dy_col[2], x_col[4];
+    // loads of this lane: instructions I = 2 wave + k of each tile (rows
+    // 2 I + lane / 32, 32 slots of 16 bytes a row), so wave w loads rows
+    // 4 w .. 4 w + 3 of both tiles; every row is clamped into [0, rows) and
+    // every column chunk into the matrix (rows past the expert's end are
+    // zeroed later, columns past N or K are never stored)
+    int dy_r[2], x_r[2];
+    int64_t dy_col[2], x_col[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int I = 2 * wave + k, r = 4 * I + (lane >> 4);
+      const int I = 2 * wave + k, r = 2 * I + (lane >> 5);
       dy_r[k] = r;
-      dy_col[k] = min<int64_t>(n0 + 8 * ((lane & 15) ^ (2 * (r & 7))), N - 8);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int I = 4 * wave + k, r = 2 * I + (lane >> 5);
       x_r[k] = r;
+      dy_col[k] = min<int64_t>(n0 + 8 * ((lane & 31) ^ (2 * (r & 7))), N - 8);
       x_col[k] = min<int64_t>(c0 + 8 * ((lane & 31) ^ (2 * (r & 7))), K - 8);
     }
     auto prow = [&](int st, int r) { return min<int64_t>(p_beg + (int64_t)st * GPS + r, rows - 1); };
@@ -910,19 +909,19 @@ __global__ __launch_bounds__(256, 2) void k_qat_wgrad2(QatParams p) {
       const int sg = stage_of(st);
       const uint32_t base = lb_addr + sg * G_STAGE;
       const NVQ_LDS int32_t* tok_lds = (const NVQ_LDS int32_t*)(lb + sg * G_STAGE + G_DY + G_X);
-      int64_t tok[4];  // read before the first load is issued (the loads order all memory)
+      int64_t tok[2];  // read before the first load is issued (the loads order all memory)
       if (p.a_row) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) tok[k] = tok_lds[x_r[k]];
+        for (int k = 0; k < 2; ++k) tok[k] = tok_lds[x_r[k]];
       } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) tok[k] = prow(st, x_r[k]);
+        for (int k = 0; k < 2; ++k) tok[k] = prow(st, x_r[k]);
       }
 #pragma unroll
       for (int k = 0; k < 2; ++k)
         dma16(p.dy + prow(st, dy_r[k]) * N + dy_col[k], base + 1024 * (2 * wave + k));
 #pragma unroll
-      for (int k = 0; k < 4; ++k) dma16(p.x + tok[k] * K + x_col[k], base + G_DY + 1024 * (4 * wave + k));
+      for (int k = 0; k < 2; ++k) dma16(p.x + tok[k] * K + x_col[k], base + G_DY + 1024 * (2 * wave + k));
     };
     // rows of step st past the expert's end -> zero (this lane's own slots)
     auto zero_tail = [&](int st) {
@@ -931,12 +930,10 @@ __global__ __launch_bounds__(256, 2) void k_qat_wgrad2(QatParams p) {
       NVQ_LDS char* const base = lb + stage_of(st) * G_STAGE;
 #pragma unroll
       for (int k = 0; k < 2; ++k)
-        if (dy_r[k] >= nvalid)
+        if (dy_r[k] >= nvalid) {
           *(NVQ_LDS u32x4_t*)(base + 1024 * (2 * wave + k) + 16 * lane) = u32x4_t{0, 0, 0, 0};
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (x_r[k] >= nvalid)
-          *(NVQ_LDS u32x4_t*)(base + G_DY + 1024 * (4 * wave + k) + 16 * lane) = u32x4_t{0, 0, 0, 0};
+          *(NVQ_LDS u32x4_t*)(base + G_DY + 1024 * (2 * wave + k) + 16 * lane) = u32x4_t{0, 0, 0, 0};
+        }
     };
 
     // transpose-read offsets: operand row (n or c) base of this lane's group,
@@ -986,7 +983,7 @@ __global__ __launch_bounds__(256, 2) void k_qat_wgrad2(QatParams p) {
     issue(0);
     if (nsteps > 1) {
       issue(1);
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");  // step 0 landed
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // step 0 landed
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       zero_tail(0);
@@ -995,7 +992,7 @@ __global__ __launch_bounds__(256, 2) void k_qat_wgrad2(QatParams p) {
 
     // step st: [row indices of st + 3][tiles of st + 2] are issued, step st
     // is computed, then the tiles of st + 1 (and every older load) must have
-    // landed while the 6 tile loads of st + 2 may still be in flight
+    // landed while the 4 tile loads of st + 2 may still be in flight
     for (int st = 0; st < nsteps; ++st) {
       const bool ahead = st + 2 < nsteps;
       if (ahead) {
@@ -1005,7 +1002,7 @@ __global__ __launch_bounds__(256, 2) void k_qat_wgrad2(QatParams p) {
       compute(st);
       if (st + 1 < nsteps) {
         if (ahead)
-          asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+          asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
         else
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (st + 1 == nsteps - 1) zero_tail(st + 1);
@@ -1096,9 +1093,12 @@ extern "C" int qat_fakequant_gemm_w4a16(const nvq_qat_gemm_args* a, void* stream
     p.n_tiles_n = (int)((a->K + QBN - 1) / QBN);
     const int64_t G0 = a->E * p.n_tiles_m * p.n_tiles_n;
     const int64_t G = (G0 + 7) / 8 * 8;
-    if (a->rows > 0)  // transpose-read kernel (its tiles equal the 32-step kernel's)
-      hipLaunchKernelGGL(k_qat_wgrad2, dim3((unsigned)G), dim3(256), 0, s, p);
-    else
+    if (a->rows > 0) {  // transpose-read kernel, 256 x 256 tiles
+      p.n_tiles_m = (int)((a->N + GBN - 1) / GBN);
+      p.n_tiles_n = (int)((a->K + GBC - 1) / GBC);
+      const int64_t G2 = (a->E * p.n_tiles_m * p.n_tiles_n + 7) / 8 * 8;
+      hipLaunchKernelGGL(k_qat_wgrad2, dim3((unsigned)G2), dim3(512), 0, s, p);
+    } else
       hipLaunchKernelGGL((k_qat_gemm<NVQ_QAT_WGRAD, LD_ROWS_T, LD_ROWS_T>), dim3((unsigned)G), dim3(QT), 0,
                          s, p);
     return last_launch();
