@@ -36,6 +36,13 @@
  *  - Conditions only the device sees set bits of a status word kept in the
  *    workspace (NVQ_STATUS_*), read with nvq_device_status().
  *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - Empty inputs: a tensor whose row (or token) count is 0 may be passed as
+ *    NULL.  The outputs that are not empty are still written as the
+ *    definitions give them: nvfp4_quantize with rows == 0 writes
+ *    s_t = fl32(amax / 2688) with the amax of nothing taken as 0 (or
+ *    amax_in) and chan_score = 0; nvq_moe_permute with T == 0 writes all-zero
+ *    expert offsets; the WGRAD mode of qat_fakequant_gemm_w4a16 writes dw = 0
+ *    (leaves it with accumulate) for experts without rows.
  */
 #ifndef NVQ_H
 #define NVQ_H

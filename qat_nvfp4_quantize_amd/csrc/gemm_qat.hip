@@ -1068,10 +1068,11 @@ extern "C" int qat_fakequant_gemm_w4a16(const nvq_qat_gemm_args* a, void* stream
   if (a->rows < 0 || a->E < 1 || a->E > 1024 || a->N <= 0 || a->K <= 0) return NVQ_ESHAPE;
   if (a->K % QBK != 0 || a->N % QBK != 0) return NVQ_ESHAPE;  // 32-element contraction stages
   const bool wgrad = a->mode == NVQ_QAT_WGRAD;
-  if (a->mode != NVQ_QAT_DGRAD && !a->x) return NVQ_EINVAL;
-  if (a->mode != NVQ_QAT_FWD && !a->dy) return NVQ_EINVAL;
+  // the row buffers (x, dy, outputs of FWD and DGRAD) may be NULL when there are no rows
+  if (a->rows != 0 && a->mode != NVQ_QAT_DGRAD && !a->x) return NVQ_EINVAL;
+  if (a->rows != 0 && a->mode != NVQ_QAT_FWD && !a->dy) return NVQ_EINVAL;
   if (!wgrad && (!a->w_codes || !a->w_scales || !a->w_tensor_scale)) return NVQ_EINVAL;
-  if (!wgrad && !a->out_bf16 && !a->out_f32) return NVQ_EINVAL;
+  if (!wgrad && a->rows != 0 && !a->out_bf16 && !a->out_f32) return NVQ_EINVAL;
   if (wgrad && !a->dw) return NVQ_EINVAL;
   if ((a->x && !aligned16(a->x)) || (a->dy && !aligned16(a->dy)) ||
       (a->w_codes && ((uintptr_t)a->w_codes & 15u)))
@@ -1089,18 +1090,12 @@ extern "C" int qat_fakequant_gemm_w4a16(const nvq_qat_gemm_args* a, void* stream
   p.out_bf16 = a->out_bf16; p.out_f32 = a->out_f32; p.dw = a->dw;
   p.tiles = L.tiles; p.ntiles = L.ntiles; p.max_tiles = L.max_tiles;
   if (wgrad) {
-    p.n_tiles_m = (int)((a->N + QBM - 1) / QBM);
-    p.n_tiles_n = (int)((a->K + QBN - 1) / QBN);
-    const int64_t G0 = a->E * p.n_tiles_m * p.n_tiles_n;
-    const int64_t G = (G0 + 7) / 8 * 8;
-    if (a->rows > 0) {  // transpose-read kernel, 256 x 256 tiles
-      p.n_tiles_m = (int)((a->N + GBN - 1) / GBN);
-      p.n_tiles_n = (int)((a->K + GBC - 1) / GBC);
-      const int64_t G2 = (a->E * p.n_tiles_m * p.n_tiles_n + 7) / 8 * 8;
-      hipLaunchKernelGGL(k_qat_wgrad2, dim3((unsigned)G2), dim3(512), 0, s, p);
-    } else
-      hipLaunchKernelGGL((k_qat_gemm<NVQ_QAT_WGRAD, LD_ROWS_T, LD_ROWS_T>), dim3((unsigned)G), dim3(QT), 0,
-                         s, p);
+    // transpose-read kernel, 256 x 256 tiles (no rows: every expert has no
+    // contraction steps, so it only writes zeros, or leaves dW with accumulate)
+    p.n_tiles_m = (int)((a->N + GBN - 1) / GBN);
+    p.n_tiles_n = (int)((a->K + GBC - 1) / GBC);
+    const int64_t G2 = (a->E * p.n_tiles_m * p.n_tiles_n + 7) / 8 * 8;
+    hipLaunchKernelGGL(k_qat_wgrad2, dim3((unsigned)G2), dim3(512), 0, s, p);
     return last_launch();
   }
   if (a->rows == 0) return NVQ_OK;

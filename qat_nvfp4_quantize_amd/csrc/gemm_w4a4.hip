@@ -740,10 +740,10 @@ extern "C" size_t moe_gemm_workspace_bytes(int64_t rows, int64_t E, int64_t N, i
 extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stream) {
   if (!a || a->struct_size < offsetof(nvq_moe_gemm_args, w_codes_cm)) return NVQ_EINVAL;
   const bool has_cm = a->struct_size >= sizeof(nvq_moe_gemm_args) && a->w_codes_cm && a->w_scales_cm;
-  if (!a->expert_offsets || !a->a_codes || !a->a_scales || !a->a_tensor_scale || !a->w_codes ||
-      !a->w_scales || !a->w_tensor_scale || !a->ws)
-    return NVQ_EINVAL;
-  if (!a->out_bf16 && !a->out_f32) return NVQ_EINVAL;
+  if (!a->expert_offsets || !a->w_codes || !a->w_scales || !a->w_tensor_scale || !a->ws) return NVQ_EINVAL;
+  // the row buffers may be NULL when there are no rows
+  if (a->rows != 0 && (!a->a_codes || !a->a_scales || !a->a_tensor_scale)) return NVQ_EINVAL;
+  if (a->rows != 0 && !a->out_bf16 && !a->out_f32) return NVQ_EINVAL;
   if (a->epilogue != NVQ_EPI_NONE && a->epilogue != NVQ_EPI_SWIGLU) return NVQ_EINVAL;
   if (a->path != NVQ_GEMM_AUTO && a->path != NVQ_GEMM_DEQ16 && a->path != NVQ_GEMM_FP8_BLOCK)
     return NVQ_EINVAL;
@@ -751,7 +751,7 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   if (a->K % 128 != 0) return NVQ_ESHAPE;  // K steps of 32 elements; 128 keeps rows 64-byte aligned
   if (a->epilogue == NVQ_EPI_SWIGLU && (a->N % 2 != 0)) return NVQ_ESHAPE;
   if (a->k < 0 || a->k > a->K || (a->k & 7)) return NVQ_ESHAPE;
-  if (a->k > 0 && (!a->a_resid || !a->comp_idx)) return NVQ_EINVAL;
+  if (a->rows != 0 && a->k > 0 && (!a->a_resid || !a->comp_idx)) return NVQ_EINVAL;
   if (a->a_row_div < 0) return NVQ_EINVAL;
   if (((uintptr_t)a->a_codes & 15u) || ((uintptr_t)a->w_codes & 15u) ||
       (a->k > 0 && ((uintptr_t)a->a_resid & 15u)) ||

@@ -216,7 +216,7 @@ using namespace nvq;
 
 extern "C" int nvq_moe_route(const float* logits, int64_t T, int64_t E, int64_t topk, int32_t* ids,
                              float* weights, void* stream) {
-  if (!logits || !ids || !weights) return NVQ_EINVAL;
+  if (T != 0 && (!logits || !ids || !weights)) return NVQ_EINVAL;
   if (T < 0 || E < 1 || E > 1024 || topk < 1 || topk > E) return NVQ_ESHAPE;
   if (T == 0) return NVQ_OK;
   hipLaunchKernelGGL(k_route, dim3((unsigned)((T + 3) / 4)), dim3(256), 0,
@@ -235,7 +235,7 @@ extern "C" size_t nvq_moe_permute_workspace_bytes(int64_t T, int64_t topk, int64
 extern "C" int nvq_moe_permute(const int32_t* ids, int64_t T, int64_t topk, int64_t E,
                                int32_t* sorted_pair, int32_t* expert_offsets, int32_t* pos,
                                void* ws, size_t ws_bytes, void* stream) {
-  if (!ids || !sorted_pair || !expert_offsets || !pos || !ws) return NVQ_EINVAL;
+  if (!expert_offsets || !ws || (T != 0 && (!ids || !sorted_pair || !pos))) return NVQ_EINVAL;
   if (T < 0 || topk < 1 || E < 1 || E > 1024) return NVQ_ESHAPE;
   if (!aligned256(ws)) return NVQ_EALIGN;
   const int64_t P = T * topk;
@@ -259,7 +259,7 @@ extern "C" int nvq_moe_permute(const int32_t* ids, int64_t T, int64_t topk, int6
 
 extern "C" int nvq_moe_combine(const uint16_t* y, const int32_t* pos, const float* weights,
                                int64_t T, int64_t topk, int64_t N, uint16_t* out, void* stream) {
-  if (!y || !pos || !weights || !out) return NVQ_EINVAL;
+  if (T != 0 && (!y || !pos || !weights || !out)) return NVQ_EINVAL;
   if (T < 0 || topk < 1 || N <= 0 || (N & 7)) return NVQ_ESHAPE;
   if (!aligned16(y) || !aligned16(out)) return NVQ_EALIGN;
   const int64_t n = T * (N / 8);

@@ -94,6 +94,16 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4* __restrict__
 
 __global__ void k_clear_status(uint32_t* status) { *status = 0; }
 
+// No rows: the amax over nothing is 0 (or amax_in), so s_t = fl32(amax / 2688)
+// as in pass 2, and every channel's residual sum is the empty sum 0.
+__global__ void k_quant_empty(const float* __restrict__ amax_in, int64_t batch, float* __restrict__ tensor_scale,
+                              float* __restrict__ chan_score, int64_t K, uint32_t* __restrict__ status) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) *status = 0;
+  if (i < batch) tensor_scale[i] = amax_in ? (float)((double)amax_in[i] / 2688.0) : 0.0f;
+  if (chan_score && i < K) chan_score[i] = 0.0f;
+}
+
 // ---------------------------------------------------------------- pass 2 --
 // E4M3 code (0..0x7E) -> fp32.
 __device__ __forceinline__ float e4m3_value_f32(uint32_t sc) {
@@ -826,7 +836,7 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
                               const float* amax_in, uint8_t* codes, uint8_t* scales,
                               float* tensor_scale, float* chan_score, void* ws, size_t ws_bytes,
                               void* stream) {
-  if (!x || !codes || !scales || !tensor_scale || !ws) return NVQ_EINVAL;
+  if (!tensor_scale || !ws || (rows != 0 && (!x || !codes || !scales))) return NVQ_EINVAL;
   if (x_dtype != NVQ_F32 && x_dtype != NVQ_BF16) return NVQ_EINVAL;
   if (batch <= 0 || rows < 0 || K <= 0 || (K & 15)) return NVQ_ESHAPE;
   if (chan_score && batch != 1) return NVQ_ESHAPE;
@@ -837,7 +847,9 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = x_dtype == NVQ_BF16;
   if (rows == 0) {
-    hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, s, L.status);
+    const int64_t n = std::max<int64_t>(batch, chan_score ? K : 0);
+    hipLaunchKernelGGL(k_quant_empty, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, amax_in, batch,
+                       tensor_scale, chan_score, K, L.status);
     return last_launch();
   }
   if (!amax_in) {

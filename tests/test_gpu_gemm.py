@@ -299,3 +299,22 @@ def test_channel_major_record_layout(B, N, K):
     want_codes = (t[..., 0::2] | (t[..., 1::2] << 4)).astype(np.uint8)
     assert_bits_equal(to_np(ccm), want_codes, "channel-major codes")
     assert_bits_equal(to_np(scm), np.ascontiguousarray(scales.transpose(0, 2, 1)), "channel-major scales")
+
+
+def test_grouped_gemm_no_rows():
+    """rows = 0 with k > 0: the call succeeds and launches nothing harmful; the
+    empty outputs stay empty."""
+    import torch
+
+    nvq = _nvq()
+    E, N, K, k = 4, 256, 256, 8
+    g = np.random.default_rng(9)
+    qw = nvq.nvfp4_quantize(to_gpu((g.standard_normal((E, N, K)) * 0.05).astype(np.float32)))
+    qa = nvq.nvfp4_quantize(torch.empty(0, K, dtype=torch.float32, device="cuda"))
+    off = to_gpu(np.zeros(E + 1, np.int32))
+    idx = to_gpu(np.arange(k, dtype=np.int32))
+    resid = torch.empty(0, k, dtype=torch.bfloat16, device="cuda")
+    ob, of = nvq.moe_grouped_gemm_w4a4_comp(qa[0], qa[1], qa[2], qw[0], qw[1], qw[2], off, rows=0,
+                                            a_resid=resid, comp_idx=idx, want_f32=True)
+    torch.cuda.synchronize()
+    assert ob.shape == (0, N) and of.shape == (0, N)

@@ -78,3 +78,18 @@ def test_combine_matches_oracle():
     ref = oracle.combine_bf16(inputs.bf16_bits_to_f32(y), opos, ow)
     got = inputs.bf16_bits_to_f32(to_np(out))
     np.testing.assert_allclose(got, inputs.bf16_bits_to_f32(ref), rtol=2 ** -7, atol=1e-6)
+
+
+def test_no_tokens():
+    """T = 0: routing and combine do nothing, the permutation writes all-zero
+    expert offsets."""
+    import torch
+
+    nvq = _nvq()
+    E, topk, H = 16, 4, 64
+    ids, w = nvq.nvq_moe_route(torch.empty(0, E, dtype=torch.float32, device="cuda"), topk)
+    sp, off, pos, _ = nvq.nvq_moe_permute(ids, E)
+    out = nvq.nvq_moe_combine(torch.empty(0, H, dtype=torch.bfloat16, device="cuda"), pos, w)
+    torch.cuda.synchronize()
+    assert ids.shape == (0, topk) and sp.numel() == 0 and out.shape[0] == 0
+    assert_bits_equal(to_np(off), np.zeros(E + 1, np.int32), "offsets of no tokens")

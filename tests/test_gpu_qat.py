@@ -250,3 +250,28 @@ def test_qat_layer_full_size_sampled():
         _norm_err(to_np(dw[e])[np.ix_(ns, cs)], refw.reshape(ns.size, cs.size),
                   np.linalg.norm(DYe[:, ns], axis=0), np.linalg.norm(Xe[:, cs], axis=0),
                   f"full wgrad e={e}")
+
+
+def test_qat_no_rows():
+    """No rows: forward and input gradient succeed with empty outputs; the
+    weight gradient is zero, or unchanged with accumulate."""
+    import torch
+
+    nvq = _nvq()
+    E, N, K = 3, 64, 128
+    g = np.random.default_rng(5)
+    wm = inputs.to_bf16_bits((0.02 * g.standard_normal((E, N, K))).astype(np.float32))
+    q = nvq.nvfp4_quantize(to_gpu(wm))
+    off = to_gpu(np.zeros(E + 1, np.int32))
+    x = torch.empty(0, K, dtype=torch.bfloat16, device="cuda")
+    dy = torch.empty(0, N, dtype=torch.bfloat16, device="cuda")
+    yb, yf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_FWD, *q[:3], off, 0, x=x, want_f32=True)
+    dxb, dxf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *q[:3], off, 0, dy=dy, want_f32=True)
+    dw = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *q[:3], off, 0, x=x, dy=dy,
+                                      dw=torch.full((E, N, K), 7.0, device="cuda"))
+    dw2 = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *q[:3], off, 0, x=x, dy=dy,
+                                       dw=torch.full((E, N, K), 7.0, device="cuda"), accumulate=True)
+    torch.cuda.synchronize()
+    assert yf.shape == (0, N) and dxf.shape == (0, K)
+    assert not to_np(dw).any(), "weight gradient of no rows not zero"
+    assert (to_np(dw2) == 7.0).all(), "accumulated weight gradient of no rows changed"

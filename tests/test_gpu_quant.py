@@ -187,3 +187,24 @@ def test_topk_on_given_scores_ties_and_sizes(K, k):
                                            want_resid=False)
     torch.cuda.synchronize()
     assert_bits_equal(to_np(idx), oracle.topk(sc, k), f"topk K={K} k={k}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_no_rows(dtype):
+    """Zero rows: no codes, s_t = fl32(amax / 2688) with the amax of nothing 0
+    (or the given amax), every channel score the empty sum 0 -- as the oracle."""
+    import torch
+
+    nvq = _nvq()
+    K = 64
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    x = torch.empty(0, K, dtype=tdt, device="cuda")
+    for amax in (None, 3.5):
+        amax_t = None if amax is None else torch.tensor([amax], dtype=torch.float32, device="cuda")
+        codes, scales, st, score, _ = nvq.nvfp4_quantize(x, amax_in=amax_t, score=True)
+        torch.cuda.synchronize()
+        oc, osc, ost = oracle.quantize(np.zeros((0, K), np.float32), amax_in=amax)
+        assert codes.shape == (0, K // 2) and scales.shape == (0, K // 16)
+        assert_bits_equal(to_np(st), np.array([ost], np.float32), f"s_t of no rows (amax {amax})")
+        assert_bits_equal(to_np(score), oracle.residual_scores(np.zeros((0, K), np.float32), oc, osc, ost),
+                          "scores of no rows")
