@@ -842,13 +842,16 @@ __device__ __forceinline__ bf16x8_t tr_pair(const NVQ_LDS char* base, uint32_t o
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Global -> LDS direct loads; lane l lands at LDS byte lds_addr + size * l
-// (lds_addr wave-uniform).
+// Global -> LDS direct loads; lane l lands at LDS byte lds_addr + size * l.
+// lds_addr must be wave-uniform; it is read from the first lane so that it
+// is in a scalar register even where the compiler cannot prove uniformity.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
 }
 
 __global__ __launch_bounds__(512, 1) void k_qat_wgrad2(QatParams p) {
