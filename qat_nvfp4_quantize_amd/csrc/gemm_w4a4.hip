@@ -282,8 +282,10 @@ __global__ __launch_bounds__(256) void k_gather_wcomp_cm(const uint8_t* __restri
 // most row tiles the offsets allow and the real count comes from the tile
 // table.  Workgroups are dealt to the 8 XCDs round-robin, so XCD x =
 // blockIdx % 8 takes the contiguous logical range [x * per, (x + 1) * per)
-// of the real tiles, in groups of 4 row tiles x all column tiles; surplus
-// workgroups get valid == false.
+// of the real tiles, in groups of kGroupM row tiles x all column tiles (the
+// row tiles of a group, consecutive in the order, read the same weight tile
+// at about the same time); surplus workgroups get valid == false.
+constexpr int kGroupM = 8;
 struct TileCtx {
   bool valid;
   int e, nt;
@@ -293,19 +295,19 @@ __device__ __forceinline__ TileCtx tile_of_block(const GemmParams& p) {
   TileCtx c;
   c.valid = false;
   const int n_mt = min(*p.ntiles, p.max_tiles);
-  const int n_groups = (n_mt + 3) / 4;
-  const int total = n_groups * 4 * p.n_tiles_n;
+  const int n_groups = (n_mt + kGroupM - 1) / kGroupM;
+  const int total = n_groups * kGroupM * p.n_tiles_n;
   const int per = (total + 7) / 8;
   const int slot = blockIdx.x >> 3;
   if (slot >= per) return c;
   const int logical = (blockIdx.x & 7) * per + slot;
   if (logical >= total) return c;
-  const int group_span = 4 * p.n_tiles_n;
+  const int group_span = kGroupM * p.n_tiles_n;
   const int grp = logical / group_span, rem = logical - grp * group_span;
-  const int mt = 4 * grp + (rem & 3);
+  const int mt = kGroupM * grp + (rem % kGroupM);
   if (mt >= n_mt) return c;
   c.valid = true;
-  c.nt = rem >> 2;
+  c.nt = rem / kGroupM;
   c.e = p.tiles[2 * mt];
   c.row0 = p.tiles[2 * mt + 1];
   c.row_end = p.off[c.e + 1];
@@ -789,8 +791,8 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   p.swiglu = swiglu ? 1 : 0;
   p.bm = BM;
   p.n_tiles_n = swiglu ? (int)((a->N / 2 + BN / 2 - 1) / (BN / 2)) : (int)((a->N + BN - 1) / BN);
-  const int n_groups = (L.max_tiles + 3) / 4;
-  const int64_t G0 = (int64_t)n_groups * 4 * p.n_tiles_n;
+  const int n_groups = (L.max_tiles + kGroupM - 1) / kGroupM;
+  const int64_t G0 = (int64_t)n_groups * kGroupM * p.n_tiles_n;
   const int64_t G = (G0 + 7) / 8 * 8;
   const bool fp8 = a->path == NVQ_GEMM_FP8_BLOCK;
   if (fp8) {
