@@ -67,7 +67,7 @@ PREFILL = MoEShape(wid=4, T=32768, H=4096, E=128, I=1536, topk=8, k=128)
 QAT = MoEShape(wid=5, T=16384, H=4096, E=128, I=1536, topk=8, k=0)
 
 # tensor ids within a workload
-_X, _W, _OUTLIER, _LOGITS, _WGU, _WDN, _DYGU, _DYDN, _WOUT = range(9)
+_X, _W, _OUTLIER, _LOGITS, _WGU, _WDN, _DYGU, _DYDN, _WOUT, _HID = range(10)
 
 
 # ------------------------------------------------------------- workload 1 --
@@ -138,6 +138,17 @@ def grad_out(s: MoEShape, proj: str) -> np.ndarray:
     return to_bf16_bits(rng(s.wid, tid).standard_normal((s.P, N), dtype=np.float32))
 
 
+def hidden(s: MoEShape) -> np.ndarray:
+    """bf16 bits [P, I]: a stand-in for the down projection's input (the SwiGLU
+    output), drawn independently of the gate/up path: N(0,1) with 1% of the
+    channels x8."""
+    g = rng(s.wid, _HID)
+    h = g.standard_normal((s.P, s.I), dtype=np.float32)
+    cols = g.permutation(s.I)[: max(1, int(round(0.01 * s.I)))]
+    h[:, cols] *= np.float32(8.0)
+    return to_bf16_bits(h)
+
+
 def small_moe(wid=100, T=96, H=256, E=8, I=128, topk=2, k=16) -> MoEShape:
     """A reduced MoE shape for fast parity tests (several tiles plus ragged tails)."""
     return MoEShape(wid=wid, T=T, H=H, E=E, I=I, topk=topk, k=k)
@@ -146,8 +157,8 @@ def small_moe(wid=100, T=96, H=256, E=8, I=128, topk=2, k=16) -> MoEShape:
 def weights_device(s: MoEShape, proj: str, device="cuda"):
     """bf16 [E, N, K] expert weights drawn on the GPU (torch Philox generator,
     seeded per workload and tensor): same recipe as expert_weight_f32, another
-    random stream.  Used where the full-size weights are only timed, never
-    compared with the oracle."""
+    random stream, for the full-size layers (the parity tests copy the sampled
+    experts to the host for the oracle)."""
     import torch
 
     tid = _WGU if proj == "gu" else _WDN

@@ -318,3 +318,98 @@ def test_grouped_gemm_no_rows():
                                             a_resid=resid, comp_idx=idx, want_f32=True)
     torch.cuda.synchronize()
     assert ob.shape == (0, N) and of.shape == (0, N)
+
+
+def _prefill_weights(nvq, s, proj):
+    """The benchmark's weights: drawn on the device, quantized there, with the
+    channel-major copy the benchmark passes for the compensation gather."""
+    w = inputs.weights_device(s, proj)
+    q = nvq.nvfp4_quantize(w)
+    cm = nvq.nvfp4_channel_major(q[0], q[1])
+    return w, q, cm
+
+
+def _check_sampled(nvq, s, y, rows, row_tok, row_e, oq, x_hi, oidx, w, q, what):
+    """Oracle rows of the W4A4 + compensation GEMM for the sampled rows; the
+    sampled experts' weights are quantized by the oracle from the same draw and
+    checked bit-exact against the device record first."""
+    experts = sorted(set(row_e.tolist()))
+    wq = {}
+    for e in experts:
+        wb = to_np(w[e])
+        wq[e] = oracle.quantize(wb)
+        assert_bits_equal(to_np(q[0][e]), wq[e][0], f"{what} weight codes e={e}")
+        assert_bits_equal(to_np(q[1][e]), wq[e][1], f"{what} weight scales e={e}")
+    wc = np.stack([wq[e][0] for e in experts])
+    wsc = np.stack([wq[e][1] for e in experts])
+    wst = np.array([wq[e][2] for e in experts], np.float32)
+    local_e = np.array([experts.index(e) for e in row_e], np.int32)
+    log(f"[prefill] {what}: oracle on {len(rows)} sampled rows x {wc.shape[1]} cols, {len(experts)} experts")
+    ref = oracle.moe_gemm_w4a4(*oq, x_hi, oidx, wc, wsc, wst, row_tok, local_e)
+    xf = inputs.bf16_bits_to_f32(x_hi)
+    for i, e in enumerate(experts):
+        sel = local_e == i
+        check_tol(y[sel], ref[sel], xf[row_tok[sel]], _w_deq(wc[i], wsc[i], wst[i]), f"{what} e={e}")
+
+
+def test_prefill_gate_up_full_size_sampled():
+    """Full-size prefill layer (T=32768, H=4096, E=128, I=1536, top-8, k=128)
+    in the benchmark's launch configuration (sorted pair ids with a divisor,
+    channel-major record for the compensation): routing and permutation from
+    the oracle checked bit-exact, then the gate/up GEMM on sampled rows."""
+    import torch
+
+    nvq = _nvq()
+    s = inputs.PREFILL
+    logits, x = inputs.logits(s), inputs.activations(s)
+    ids, _ = nvq.nvq_moe_route(to_gpu(logits), s.topk)
+    sp, off, _, _ = nvq.nvq_moe_permute(ids, s.E)
+    oids, _ = oracle.route(logits, s.topk)
+    osp, ooff, _ = oracle.permute(oids, s.E)
+    assert_bits_equal(to_np(sp), osp, "sorted pairs")
+    assert_bits_equal(to_np(off), ooff, "expert offsets")
+    xg = to_gpu(x)
+    qx = nvq.nvfp4_quantize(xg, score=True)
+    idx1, r1, _ = nvq.residual_topk_channels(xg, *qx[:3], s.k, scores=qx[3])
+    w, q, cm = _prefill_weights(nvq, s, "gu")
+    _, y1 = nvq.moe_grouped_gemm_w4a4_comp(qx[0], qx[1], qx[2], q[0], q[1], q[2], off, rows=s.P, a_row=sp,
+                                           a_resid=r1.contiguous(), comp_idx=idx1,
+                                           epilogue=nvq.NVQ_EPI_SWIGLU, want_f32=True, a_row_div=s.topk,
+                                           w_cm=cm)
+    torch.cuda.synchronize()
+    oqx = oracle.quantize(x)
+    assert_bits_equal(to_np(qx[0]), oqx[0], "X codes")
+    oidx1 = oracle.topk(oracle.residual_scores(x, *oqx), s.k)
+    assert_bits_equal(to_np(idx1), oidx1, "X channels")
+    rows = _sample_rows(ooff, every=1499)
+    row_e = np.searchsorted(ooff, rows, side="right") - 1
+    _check_sampled(nvq, s, to_np(y1)[rows], rows, (osp[rows] // s.topk).astype(np.int32), row_e, oqx, x,
+                   oidx1, w, q, "gate/up")
+
+
+def test_prefill_down_full_size_sampled():
+    """Full-size prefill down projection (K=1536, N=4096, k=128, P=262144 rows)
+    in the benchmark's launch configuration, on an independently drawn H of the
+    layer's shape: H's record checked bit-exact, then sampled rows."""
+    import torch
+
+    nvq = _nvq()
+    s = inputs.PREFILL
+    logits = inputs.logits(s)
+    oids, _ = oracle.route(logits, s.topk)
+    _, ooff, _ = oracle.permute(oids, s.E)
+    hb = inputs.hidden(s)
+    hg = to_gpu(hb)
+    qh = nvq.nvfp4_quantize(hg, score=True)
+    idx2, r2, _ = nvq.residual_topk_channels(hg, *qh[:3], s.k, scores=qh[3])
+    w, q, cm = _prefill_weights(nvq, s, "dn")
+    _, y2 = nvq.moe_grouped_gemm_w4a4_comp(qh[0], qh[1], qh[2], q[0], q[1], q[2], to_gpu(ooff), rows=s.P,
+                                           a_resid=r2.contiguous(), comp_idx=idx2, want_f32=True, w_cm=cm)
+    torch.cuda.synchronize()
+    oqh = oracle.quantize(hb)
+    assert_bits_equal(to_np(qh[0]), oqh[0], "H codes")
+    oidx2 = oracle.topk(oracle.residual_scores(hb, *oqh), s.k)
+    assert_bits_equal(to_np(idx2), oidx2, "H channels")
+    rows = _sample_rows(ooff, every=1499)
+    row_e = np.searchsorted(ooff, rows, side="right") - 1
+    _check_sampled(nvq, s, to_np(y2)[rows], rows, rows.astype(np.int32), row_e, oqh, hb, oidx2, w, q, "down")
