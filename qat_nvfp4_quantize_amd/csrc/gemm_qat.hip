@@ -465,8 +465,10 @@ __device__ __forceinline__ float e4m3_value(uint32_t code) {
 // tiles (the row tiles of a group read the same weight tile at about the same
 // time), each of the 8 XCDs (blockIdx.x % 8) takes a contiguous range of the
 // order.  False for surplus workgroups.  Measured: 8 for the forward's
-// 128-row tiles, 4 for the input gradient's 256-row tiles.
-constexpr int kFwdGroupM = 8, kDgradGroupM = 4;
+// 128-row tiles; 1 for the input gradient, whose 1.5 MB dy row block (read by
+// every column tile) is eight times its weight slice, so consecutive
+// workgroups should share the rows, not the weight.
+constexpr int kFwdGroupM = 8, kDgradGroupM = 1;
 template <int kGm>
 __device__ __forceinline__ bool pick_tile(const QatParams& p, int& mt, int& nt) {
   const int n_mt = min(*p.ntiles, p.max_tiles);
