@@ -1026,24 +1026,50 @@ __global__ __launch_bounds__(512, 1) void k_qat_wgrad2(QatParams p) {
     return;  // no rows: dW unchanged
   }
 
-  // one 32 x 32 tile at a time: with accumulate its 16 old values are loaded
-  // together, then added and stored
+  // Tiles wholly inside dW (every tile when N and K are multiples of 256) take
+  // branch-free stores; with accumulate the 16 old values of a 32 x 32 tile
+  // are loaded together, then added and stored.  Partial tiles check each
+  // element.
+  auto idx = [](int v) { return (int64_t)(8 * (v >> 2) + (v & 3)); };
+  const bool full = n0 + GBN <= N && c0 + GBC <= K;
+  if (full && !p.accumulate) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t c = c0 + 128 * wc + 32 * j + l32;
-      const int64_t nb = n0 + 64 * wn + 32 * i + 4 * h;
-      float* const d = p.dw + ((int64_t)e * N + nb) * K + c;
-      auto idx = [&](int v) { return (int64_t)(8 * (v >> 2) + (v & 3)); };
-      auto ok = [&](int v) { return c < K && nb + idx(v) < N; };
-      float old[16];
+      for (int j = 0; j < 4; ++j) {
+        float* const d = p.dw + ((int64_t)e * N + n0 + 64 * wn + 32 * i + 4 * h) * K + c0 + 128 * wc + 32 * j + l32;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) old[v] = (p.accumulate && ok(v)) ? d[idx(v) * K] : 0.0f;
+        for (int v = 0; v < 16; ++v) d[idx(v) * K] = acc[i][j][v];
+      }
+  } else if (full) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (ok(v)) d[idx(v) * K] = old[v] + acc[i][j][v];
-    }
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float* const d = p.dw + ((int64_t)e * N + n0 + 64 * wn + 32 * i + 4 * h) * K + c0 + 128 * wc + 32 * j + l32;
+        float old[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) old[v] = d[idx(v) * K];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) d[idx(v) * K] = old[v] + acc[i][j][v];
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t c = c0 + 128 * wc + 32 * j + l32;
+        const int64_t nb = n0 + 64 * wn + 32 * i + 4 * h;
+        float* const d = p.dw + ((int64_t)e * N + nb) * K + c;
+        auto ok = [&](int v) { return c < K && nb + idx(v) < N; };
+        float old[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) old[v] = (p.accumulate && ok(v)) ? d[idx(v) * K] : 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (ok(v)) d[idx(v) * K] = old[v] + acc[i][j][v];
+      }
+  }
 }
 
 struct QatLayout {
