@@ -607,21 +607,33 @@ __global__ __launch_bounds__(256, 2) void k_qat_fwd2(QatParams p) {
   if (nst & 1) mfma_step(X0, 0);
 
   const float stw = p.w_st[e];
+  // A wave whose rows and columns are all inside the output stores without
+  // per-element checks (wave-uniform branches on which outputs are wanted).
+  auto emit = [&](auto&& store, bool check) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t pr = row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-      if (pr >= row_end) continue;
+      for (int v = 0; v < 16; ++v) {
+        const int64_t pr = row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (check && pr >= row_end) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t n = (int64_t)nt * FBN + FWN * wave + 32 * j + l32;
-        if (n >= N) continue;
-        const float y = acc[i][j][v] * stw;
-        if (p.out_f32) p.out_f32[pr * N + n] = y;
-        if (p.out_bf16) p.out_bf16[pr * N + n] = (uint16_t)f32_to_bf16_rne(y);
+        for (int j = 0; j < 2; ++j) {
+          const int64_t n = (int64_t)nt * FBN + FWN * wave + 32 * j + l32;
+          if (check && n >= N) continue;
+          store(pr * N + n, acc[i][j][v] * stw);
+        }
       }
-    }
+  };
+  auto st_f32 = [&](int64_t o, float y) { p.out_f32[o] = y; };
+  auto st_bf16 = [&](int64_t o, float y) { p.out_bf16[o] = (uint16_t)f32_to_bf16_rne(y); };
+  auto st_both = [&](int64_t o, float y) { st_f32(o, y); st_bf16(o, y); };
+  const bool full = row0 + FBM <= row_end && (int64_t)nt * FBN + FWN * (wave + 1) <= N;
+  if (p.out_f32 && p.out_bf16)
+    full ? emit(st_both, false) : emit(st_both, true);
+  else if (p.out_f32)
+    full ? emit(st_f32, false) : emit(st_f32, true);
+  else
+    full ? emit(st_bf16, false) : emit(st_bf16, true);
 }
 
 // ------------------------------------------------ input gradient, 2 WG/CU --
@@ -795,21 +807,33 @@ __global__ __launch_bounds__(256, 2) void k_qat_dgrad2(QatParams p) {
   step(nst - 1, W, false);
 
   const float stw = p.w_st[e];
+  // A wave whose rows and columns are all inside the output stores without
+  // per-element checks (wave-uniform branches on which outputs are wanted).
+  auto emit = [&](auto&& store, bool check) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t pr = row0 + 64 * wave + 16 * i + 4 * g + v;
-      if (pr >= row_end) continue;
+      for (int v = 0; v < 4; ++v) {
+        const int64_t pr = row0 + 64 * wave + 16 * i + 4 * g + v;
+        if (check && pr >= row_end) continue;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t c = c0 + 16 * j + l16;
-        if (c >= Ko) continue;
-        const float y = acc[i][j][v] * stw;
-        if (p.out_f32) p.out_f32[pr * Ko + c] = y;
-        if (p.out_bf16) p.out_bf16[pr * Ko + c] = (uint16_t)f32_to_bf16_rne(y);
+        for (int j = 0; j < 8; ++j) {
+          const int64_t c = c0 + 16 * j + l16;
+          if (check && c >= Ko) continue;
+          store(pr * Ko + c, acc[i][j][v] * stw);
+        }
       }
-    }
+  };
+  auto st_f32 = [&](int64_t o, float y) { p.out_f32[o] = y; };
+  auto st_bf16 = [&](int64_t o, float y) { p.out_bf16[o] = (uint16_t)f32_to_bf16_rne(y); };
+  auto st_both = [&](int64_t o, float y) { st_f32(o, y); st_bf16(o, y); };
+  const bool full = row0 + 64 * (wave + 1) <= row_end && c0 + DBN <= Ko;
+  if (p.out_f32 && p.out_bf16)
+    full ? emit(st_both, false) : emit(st_both, true);
+  else if (p.out_f32)
+    full ? emit(st_f32, false) : emit(st_f32, true);
+  else
+    full ? emit(st_bf16, false) : emit(st_bf16, true);
 }
 
 // ------------------------------------------------- weight gradient, 2 WG/CU --
