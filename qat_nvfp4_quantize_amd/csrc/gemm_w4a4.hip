@@ -387,42 +387,56 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c,
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, l32 = lane & 31, h = lane >> 5;
   const int64_t N = p.N;
   const float stw = p.w_st[c.e];
+  // Tiles wholly inside the output take the unguarded store path: per-element
+  // guards become exec-mask branches whose waits serialize the stores.
+  const bool rows_full = c.row0 + BM <= c.row_end;
   if (!kSwiglu) {
+    auto emit = [&](bool check) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t pr = c.row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (pr >= c.row_end) continue;
+        for (int v = 0; v < 16; ++v) {
+          const int64_t pr = c.row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (check && pr >= c.row_end) continue;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t n = (int64_t)c.nt * BN + WN * wave + 32 * j + l32;
-          if (n >= N) continue;
-          const float y = acc[i][j][v] * stw;
-          if (p.out_f32) p.out_f32[pr * N + n] = y;
-          if (p.out_bf16) p.out_bf16[pr * N + n] = (uint16_t)f32_to_bf16_rne(y);
+          for (int j = 0; j < 2; ++j) {
+            const int64_t n = (int64_t)c.nt * BN + WN * wave + 32 * j + l32;
+            if (check && n >= N) continue;
+            const float y = acc[i][j][v] * stw;
+            if (p.out_f32) p.out_f32[pr * N + n] = y;
+            if (p.out_bf16) p.out_bf16[pr * N + n] = (uint16_t)f32_to_bf16_rne(y);
+          }
         }
-      }
+    };
+    if (rows_full && (int64_t)c.nt * BN + WN * (wave + 1) <= N)
+      emit(false);
+    else
+      emit(true);
   } else {
     const int64_t I = N >> 1;
     const int64_t ng = (int64_t)c.nt * (BN / 2) + 32 * wave + l32;
-    if (ng >= I) return;
+    auto emit = [&](bool check) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t pr = c.row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (pr >= c.row_end) continue;
-        const float g = acc[i][0][v] * stw;
-        const float u = acc[i][1][v] * stw;
-        if (p.out_f32) {
-          p.out_f32[pr * N + ng] = g;
-          p.out_f32[pr * N + I + ng] = u;
+        for (int v = 0; v < 16; ++v) {
+          const int64_t pr = c.row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (check && (pr >= c.row_end || ng >= I)) continue;
+          const float g = acc[i][0][v] * stw;
+          const float u = acc[i][1][v] * stw;
+          if (p.out_f32) {
+            p.out_f32[pr * N + ng] = g;
+            p.out_f32[pr * N + I + ng] = u;
+          }
+          // silu(g) u; the result is rounded to bf16, so an rcp suffices
+          const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+          if (p.out_bf16) p.out_bf16[pr * I + ng] = (uint16_t)f32_to_bf16_rne(hv);
         }
-        // silu(g) u; the result is rounded to bf16, so an rcp suffices
-        const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-        if (p.out_bf16) p.out_bf16[pr * I + ng] = (uint16_t)f32_to_bf16_rne(hv);
-      }
+    };
+    if (rows_full && (int64_t)c.nt * (BN / 2) + 32 * (wave + 1) <= I)
+      emit(false);
+    else
+      emit(true);
   }
 }
 
