@@ -347,25 +347,45 @@ __device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c
 #pragma unroll
   for (int j = 0; j < 2; ++j) w_src[j] = p.wcomp + ((int64_t)c.e * p.N + b_n[j]) * p.kpad;
   const int ncs = (p.k + SE - 1) / SE;
+  // Sub-step d of a 128-channel step covers channels 16 d .. 16 d + 15 (lane
+  // half h: 16 d + 8 h ..), so the sub-steps past k are skipped wave-uniformly
+  // (k = 64 runs half the MFMAs of a step).  Every load of a step is issued
+  // before the first wait: addresses are clamped into the row (k and kpad are
+  // multiples of 8) and channels past k are zeroed by a select afterwards.  A
+  // load under a per-lane condition would be followed by its own wait, one
+  // memory round trip each.
+  auto keep = [](bool live, uint4 v) {
+    const uint32_t m = live ? 0xFFFFFFFFu : 0u;
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+  };
   for (int cs = 0; cs < ncs; ++cs) {
-    const int c0 = SE * cs + 64 * ahh;
+    const int rem = p.k - SE * cs;  // channels left, uniform
+    uint4 rv[8], wv[2][8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int ch = c0 + 8 * q;  // 8 channels (16 bytes); k % 8 == 0
-      const uint4 v = ch < p.k ? *reinterpret_cast<const uint4*>(r_src + ch) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&lds[ar][128 * ahh + 16 * q]) = v;
-    }
+    for (int q = 0; q < 8; ++q)  // residual channels 16 q + 8 ahh .. + 7
+      if (16 * q < rem) rv[q] = *reinterpret_cast<const uint4*>(r_src + min(SE * cs + 16 * q + 8 * ahh, p.k - 8));
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (16 * d < rem)
+          wv[j][d] = *reinterpret_cast<const uint4*>(w_src[j] + min(SE * cs + 16 * d + 8 * h, p.kpad - 8));
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (16 * q < rem)
+        *reinterpret_cast<uint4*>(&lds[ar][32 * q + 16 * ahh]) = keep(16 * q + 8 * ahh < rem, rv[q]);
     __syncthreads();
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
+      if (16 * d >= rem) break;
       bf16x8_t af[4], bf[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&lds[32 * i + l32][128 * h + 16 * d]);
-      const int cb = SE * cs + 64 * h + 8 * d;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&lds[32 * i + l32][32 * d + 16 * h]);
+      const bool live = 16 * d + 8 * h < rem;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint4 v = cb < p.kpad ? *reinterpret_cast<const uint4*>(w_src[j] + cb) : make_uint4(0, 0, 0, 0);
+        const uint4 v = keep(live, wv[j][d]);
         __builtin_memcpy(&bf[j], &v, 16);
       }
 #pragma unroll
