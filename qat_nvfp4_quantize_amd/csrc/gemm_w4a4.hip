@@ -240,7 +240,11 @@ __device__ __forceinline__ uint32_t wq_bf16(uint32_t nib, uint32_t sc) {
 // of one expert and channels 8 q .. 8 q + 7 (blockIdx.y = q): eight
 // independent (code byte, two scale bytes) loads from those channels'
 // contiguous rows, then one 16-byte store per row.  Lanes run along n, so
-// every load instruction reads consecutive bytes.
+// every load instruction reads consecutive bytes.  k is a multiple of 8, so
+// a group of 8 channels is either wholly below k or wholly past it; all
+// loads are unconditional and issued before the first wait, and the decode
+// is branch-free (the hardware FP4 conversion gives both rows' G, signed;
+// G * s_b has at most 6 significant bits, so its bf16 is exact).
 __global__ __launch_bounds__(256) void k_gather_wcomp_cm(const uint8_t* __restrict__ codes_cm,
                                                         const uint8_t* __restrict__ scales_cm, int64_t N,
                                                         int64_t K, const int32_t* __restrict__ idx, int k,
@@ -249,31 +253,41 @@ __global__ __launch_bounds__(256) void k_gather_wcomp_cm(const uint8_t* __restri
   const int j0 = 8 * (int)blockIdx.y;
   const int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
   if (n >= N || j0 >= kpad) return;
+  uint16_t* o0 = wcomp + (e * N + n) * kpad + j0;
+  if (j0 >= k) {
+    *reinterpret_cast<uint4*>(o0) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(o0 + kpad) = make_uint4(0, 0, 0, 0);
+    return;
+  }
   const uint8_t* cb = codes_cm + e * K * (N >> 1) + (n >> 1);
   const uint8_t* sb = scales_cm + e * (K >> 4) * N + n;
+  int64_t ch[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) ch[u] = idx[j0 + u];
   uint32_t byte[8], sc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    byte[u] = 0u;
-    sc[u] = 0u;
-    if (j0 + u < k) {
-      const int64_t ch = idx[j0 + u];
-      byte[u] = cb[ch * (N >> 1)];
-      sc[u] = *reinterpret_cast<const uint16_t*>(sb + (ch >> 4) * N);
-    }
+    byte[u] = cb[ch[u] * (N >> 1)];
+    sc[u] = *reinterpret_cast<const uint16_t*>(sb + (ch[u] >> 4) * N);
   }
+  auto e4m3 = [](uint32_t c) {  // c <= 0x7E
+    const float nrm = __uint_as_float(((c & 0x7Fu) << 20) + (120u << 23));
+    const float sub = (float)(c & 7u) * 0x1p-9f;
+    return (c & 0x78u) ? nrm : sub;
+  };
   uint32_t r0[4], r1[4];
 #pragma unroll
   for (int u = 0; u < 8; u += 2) {
-    const bool v0 = j0 + u < k, v1 = j0 + u + 1 < k;
-    const uint32_t a0 = v0 ? wq_bf16(byte[u] & 15u, sc[u] & 0xFFu) : 0u;
-    const uint32_t b0 = v0 ? wq_bf16(byte[u] >> 4, sc[u] >> 8) : 0u;
-    const uint32_t a1 = v1 ? wq_bf16(byte[u + 1] & 15u, sc[u + 1] & 0xFFu) : 0u;
-    const uint32_t b1 = v1 ? wq_bf16(byte[u + 1] >> 4, sc[u + 1] >> 8) : 0u;
-    r0[u >> 1] = a0 | (a1 << 16);
-    r1[u >> 1] = b0 | (b1 << 16);
+    uint32_t lo[2], hi[2];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const auto g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte[u + v], 1.0f, 0);
+      lo[v] = __float_as_uint(g[0] * e4m3(sc[u + v] & 0xFFu)) >> 16;
+      hi[v] = __float_as_uint(g[1] * e4m3(sc[u + v] >> 8)) >> 16;
+    }
+    r0[u >> 1] = lo[0] | (lo[1] << 16);
+    r1[u >> 1] = hi[0] | (hi[1] << 16);
   }
-  uint16_t* o0 = wcomp + (e * N + n) * kpad + j0;
   *reinterpret_cast<uint4*>(o0) = make_uint4(r0[0], r0[1], r0[2], r0[3]);
   *reinterpret_cast<uint4*>(o0 + kpad) = make_uint4(r1[0], r1[1], r1[2], r1[3]);
 }
