@@ -469,24 +469,61 @@ __global__ __launch_bounds__(512, 2) void k_quantize(
 // score[c] = sum over chunks j ascending of P[j][c] (fp32, sequential).  One
 // column per thread, 64-thread workgroups so the columns spread over many CUs;
 // the partials of a group of 64 chunks are all loaded before the in-order sum.
-constexpr int kScoreThreads = 64;
-constexpr int kScoreBatch = 64;
-__global__ __launch_bounds__(kScoreThreads) void k_score_reduce(const float* __restrict__ partial,
-                                                               int64_t nchunks, int64_t K,
-                                                               float* __restrict__ score) {
-  const int64_t c = (int64_t)blockIdx.x * kScoreThreads + threadIdx.x;
-  if (c >= K) return;
-  float s = 0.0f;
-  for (int64_t j0 = 0; j0 < nchunks; j0 += kScoreBatch) {
-    float v[kScoreBatch];
-#pragma unroll
-    for (int j = 0; j < kScoreBatch; ++j)
-      v[j] = (j0 + j < nchunks) ? partial[(j0 + j) * K + c] : 0.0f;
-#pragma unroll
-    for (int j = 0; j < kScoreBatch; ++j)
-      if (j0 + j < nchunks) s += v[j];
+// score[c] = sum over chunks j = 0, 1, ... of partial[j][c], strictly in
+// chunk order (one fp32 add per chunk).  The add chain is inherently serial,
+// so the loads are spread over a whole workgroup: a workgroup owns 32
+// columns; all four waves stream blocks of 256 chunks into a transposed,
+// double-buffered LDS tile (32 loads in flight per thread), while lanes
+// 0..31 of wave 0 add the previous block in order, four chunks per LDS read.
+constexpr int kScoreCols = 32, kScoreBlock = 256, kScorePitch = kScoreBlock + 4;
+__global__ __launch_bounds__(256) void k_score_reduce(const float* __restrict__ partial,
+                                                     int64_t nchunks, int64_t K,
+                                                     float* __restrict__ score) {
+  __shared__ __attribute__((aligned(16))) float tile[2][kScoreCols * kScorePitch];
+  const int t = threadIdx.x, col = t & 31, r0 = t >> 5;  // chunk rows r0 + 8 i
+  const int64_t c = (int64_t)blockIdx.x * kScoreCols + col;
+  const int64_t cl = min<int64_t>(c, K - 1);  // columns past K load a valid one, never stored
+  if (nchunks <= 0) {  // no rows: every sum is empty
+    if (t < 32 && c < K) score[c] = 0.0f;
+    return;
   }
-  score[c] = s;
+  const int nb = (int)((nchunks + kScoreBlock - 1) / kScoreBlock);
+  float v[kScoreBlock / 8];
+  auto load = [&](int b) {
+    const int64_t j0 = (int64_t)b * kScoreBlock;
+#pragma unroll
+    for (int i = 0; i < kScoreBlock / 8; ++i) {
+      const int64_t j = min<int64_t>(j0 + r0 + 8 * i, nchunks - 1);
+      v[i] = partial[j * K + cl];
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kScoreBlock / 8; ++i) tile[buf][col * kScorePitch + r0 + 8 * i] = v[i];
+  };
+  float acc = 0.0f;
+  load(0);
+  put(0);
+  __syncthreads();
+  for (int b = 0; b < nb; ++b) {
+    if (b + 1 < nb) load(b + 1);
+    if (t < 32) {
+      const int n = (int)min<int64_t>(kScoreBlock, nchunks - (int64_t)b * kScoreBlock);
+      const float* src = &tile[b & 1][col * kScorePitch];
+      int j = 0;
+      for (; j + 4 <= n; j += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(src + j);
+        acc += q.x;
+        acc += q.y;
+        acc += q.z;
+        acc += q.w;
+      }
+      for (; j < n; ++j) acc += src[j];
+    }
+    if (b + 1 < nb) put((b + 1) & 1);
+    __syncthreads();
+  }
+  if (t < 32 && c < K) score[c] = acc;
 }
 
 // Recomputes the residual sub-chunk/chunk partials from an existing NVFP4
@@ -879,8 +916,7 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
 #undef NVQ_LAUNCH_Q
   if (int rc = last_launch()) return rc;
   if (score) {
-    hipLaunchKernelGGL(k_score_reduce, dim3((unsigned)((K + kScoreThreads - 1) / kScoreThreads)),
-                       dim3(kScoreThreads), 0, s,
+    hipLaunchKernelGGL(k_score_reduce, dim3((unsigned)((K + kScoreCols - 1) / kScoreCols)), dim3(256), 0, s,
                        L.chunk_partial, L.nchunks, K, chan_score);
     return last_launch();
   }
@@ -950,8 +986,7 @@ extern "C" int residual_topk_channels(const void* x, int x_dtype, int64_t rows, 
                            scales, tensor_scale, chunk_partial);
       if (int rc = last_launch()) return rc;
     }
-    hipLaunchKernelGGL(k_score_reduce, dim3((unsigned)((K + kScoreThreads - 1) / kScoreThreads)),
-                       dim3(kScoreThreads), 0, s,
+    hipLaunchKernelGGL(k_score_reduce, dim3((unsigned)((K + kScoreCols - 1) / kScoreCols)), dim3(256), 0, s,
                        chunk_partial, nchunks, K, dst);
     if (int rc = last_launch()) return rc;
     score = dst;
