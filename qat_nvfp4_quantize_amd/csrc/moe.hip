@@ -54,7 +54,6 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   }
   double lmax = 0.0, den = 0.0;
   float chosen[8];
-  int32_t chosen_id[8];
   for (int j = 0; j < topk; ++j) {
     uint64_t best = 0;
 #pragma unroll
@@ -64,19 +63,20 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (key[i] == best) key[i] = 0ull;
-    const float lv = l[e];
+    // the logit from its key (no dependent reload); -0 comes back as +0,
+    // which gives the same exp
+    const uint32_t kb = (uint32_t)(best >> 32);
+    const float lv = __uint_as_float((kb & 0x80000000u) ? (kb & 0x7FFFFFFFu) : ~kb);
     if (j == 0) lmax = (double)lv;
     den += exp((double)lv - lmax);
     if (j < 8) {
       chosen[j] = lv;
-      chosen_id[j] = (int32_t)e;
     }
     if (lane == 0) ids[t * topk + j] = (int32_t)e;
   }
   if (lane == 0) {
     for (int j = 0; j < topk; ++j) {
       const float lv = j < 8 ? chosen[j] : l[ids[t * topk + j]];
-      (void)chosen_id;
       weights[t * topk + j] = (float)(exp((double)lv - lmax) / den);
     }
   }
@@ -104,37 +104,56 @@ __global__ __launch_bounds__(256) void k_perm_hist(const int32_t* __restrict__ i
   if (bad) atomicOr(status, (uint32_t)NVQ_STATUS_BAD_EXPERT);
 }
 
-// One workgroup: per-expert running sums over chunks, then the exclusive scan
-// over experts.  base[c][e] = offset of expert e + pairs of e in chunks < c.
+// One workgroup: base[c][e] = offset of expert e + pairs of e in chunks < c.
+// Each expert's chunk column is split over 1024 / E threads (8 for E = 128):
+// a thread sums its contiguous range of chunks, the partial sums give each
+// range's start, an inclusive scan over the expert totals (Hillis-Steele in
+// LDS) gives the expert offsets, and each thread then rewrites its range in
+// batches of 16 (loads first, then stores, so the loads overlap).
 __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts, int64_t nchunks,
                                                    int E, int32_t* __restrict__ offsets) {
-  __shared__ int32_t tot[1024];
-  __shared__ int32_t off[1025];
-  const int e = threadIdx.x;
-  int32_t run = 0;
-  if (e < E) {
-    for (int64_t c = 0; c < nchunks; ++c) {
-      const int32_t n = counts[c * E + e];
-      counts[c * E + e] = run;
-      run += n;
-    }
-    tot[e] = run;
-  }
+  __shared__ int32_t part_sum[1024];
+  __shared__ int32_t scan[1024];
+  const int t = threadIdx.x;
+  const int tpe = max(1, 1024 / E);
+  const int e = t / tpe, part = t - e * tpe;
+  const bool live = e < E;
+  const int64_t len = (nchunks + tpe - 1) / tpe;
+  const int64_t cb = min<int64_t>(part * len, nchunks), ce = min<int64_t>(cb + len, nchunks);
+  int32_t sum = 0;
+  if (live)
+    for (int64_t c = cb; c < ce; ++c) sum += counts[c * E + e];
+  part_sum[t] = sum;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t s = 0;
-    for (int i = 0; i < E; ++i) {
-      off[i] = s;
-      s += tot[i];
-    }
-    off[E] = s;
-  }
+  int32_t tot = 0;
+  if (t < E)
+    for (int k = 0; k < tpe; ++k) tot += part_sum[t * tpe + k];
+  scan[t] = tot;
   __syncthreads();
-  if (e < E) {
-    for (int64_t c = 0; c < nchunks; ++c) counts[c * E + e] += off[e];
-    offsets[e] = off[e];
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int32_t v = t >= d ? scan[t - d] : 0;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
   }
-  if (e == 0) offsets[E] = off[E];
+  if (live) {
+    const int32_t off_e = e > 0 ? scan[e - 1] : 0;
+    int32_t run = off_e;
+    for (int k = 0; k < part; ++k) run += part_sum[e * tpe + k];
+    for (int64_t c = cb; c < ce; c += 16) {
+      int32_t n[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) n[u] = counts[min<int64_t>(c + u, ce - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (c + u < ce) {
+          counts[(c + u) * E + e] = run;
+          run += n[u];
+        }
+    }
+    if (part == 0) offsets[e] = off_e;
+  }
+  if (t == 0) offsets[E] = scan[E - 1];
 }
 
 // Stable scatter: one wave per chunk walks its pairs in order 64 at a time;
