@@ -36,7 +36,9 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-// One wave per token: topk rounds of a 64-bit (key, ~id) wave max.
+// One wave per token: topk rounds of a 64-bit (key, ~id) wave max.  Each
+// lane holds kPer = ceil(E / 64) keys (E <= 64 * kPer).
+template <int kPer>
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int64_t T, int E,
                                               int topk, int32_t* __restrict__ ids,
                                               float* __restrict__ weights) {
@@ -44,7 +46,6 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
   const float* l = logits + t * E;
-  constexpr int kPer = 16;  // E <= 1024
   uint64_t key[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
                      : 0ull;
   }
   double lmax = 0.0, den = 0.0;
-  float chosen[8];
+  double ex[8];
   for (int j = 0; j < topk; ++j) {
     uint64_t best = 0;
 #pragma unroll
@@ -68,16 +69,15 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
     const uint32_t kb = (uint32_t)(best >> 32);
     const float lv = __uint_as_float((kb & 0x80000000u) ? (kb & 0x7FFFFFFFu) : ~kb);
     if (j == 0) lmax = (double)lv;
-    den += exp((double)lv - lmax);
-    if (j < 8) {
-      chosen[j] = lv;
-    }
+    const double x = exp((double)lv - lmax);
+    den += x;
+    if (j < 8) ex[j] = x;
     if (lane == 0) ids[t * topk + j] = (int32_t)e;
   }
   if (lane == 0) {
     for (int j = 0; j < topk; ++j) {
-      const float lv = j < 8 ? chosen[j] : l[ids[t * topk + j]];
-      weights[t * topk + j] = (float)(exp((double)lv - lmax) / den);
+      const double x = j < 8 ? ex[j] : exp((double)l[ids[t * topk + j]] - lmax);
+      weights[t * topk + j] = (float)(x / den);
     }
   }
 }
@@ -238,8 +238,16 @@ extern "C" int nvq_moe_route(const float* logits, int64_t T, int64_t E, int64_t 
   if (T != 0 && (!logits || !ids || !weights)) return NVQ_EINVAL;
   if (T < 0 || E < 1 || E > 1024 || topk < 1 || topk > E) return NVQ_ESHAPE;
   if (T == 0) return NVQ_OK;
-  hipLaunchKernelGGL(k_route, dim3((unsigned)((T + 3) / 4)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), logits, T, (int)E, (int)topk, ids, weights);
+  const dim3 grid((unsigned)((T + 3) / 4));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (E <= 64)
+    hipLaunchKernelGGL(k_route<1>, grid, dim3(256), 0, s, logits, T, (int)E, (int)topk, ids, weights);
+  else if (E <= 128)
+    hipLaunchKernelGGL(k_route<2>, grid, dim3(256), 0, s, logits, T, (int)E, (int)topk, ids, weights);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_route<4>, grid, dim3(256), 0, s, logits, T, (int)E, (int)topk, ids, weights);
+  else
+    hipLaunchKernelGGL(k_route<16>, grid, dim3(256), 0, s, logits, T, (int)E, (int)topk, ids, weights);
   return last_launch();
 }
 
