@@ -653,13 +653,44 @@ __global__ __launch_bounds__(256, 2) void k_qat_fwd2(QatParams p) {
 //    row read 64 contiguous bytes (one load instruction touches 16 rows, not
 //    32 rows x 2 as the 32x32 layout would).  Fragments roll two sub-steps
 //    ahead.
+#define NVQ_LDS __attribute__((address_space(3)))
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Two LDS transpose reads (ds_read_b64_tr_b16) -> one 8-element bf16 MFMA
+// operand: in each group of 16 lanes, lane i receives element i % 4 of the
+// 8-byte reads of lanes i / 4 + 4 m, m = 0..3 (measured), so a source lane
+// that points at 4 consecutive columns of contraction row k0 + s / 4 hands
+// lane i the values of column 4 (s % 4) + i % 4 at rows k0 .. k0 + 3.
+__device__ __forceinline__ bf16x8_t tr_pair(const NVQ_LDS char* base, uint32_t off0, uint32_t off1) {
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((NVQ_LDS v4i16_t*)(base + off0));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((NVQ_LDS v4i16_t*)(base + off1));
+  typedef short v8i16_t __attribute__((ext_vector_type(8)));
+  const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 constexpr int DBM = 256, DBN = 128, DSE = 128;
+// Output widths that are multiples of DBN take the wide weight path: thread t
+// loads contraction row t / 2 of the step, 64 columns (two 16-byte code loads
+// and one scale dword, 3 load instructions against 8), and writes it
+// dequantized in its natural [n][c] layout (rows of DBN bf16 at a 288-byte
+// pitch, so the 4 rows x 32 bytes of one transpose read fall in distinct
+// banks); the MFMA B operands come out through tr_pair.  The input gradient
+// is bound by the vector memory address path, so load instructions count.
+constexpr int DW_PITCH = 2 * DBN + 32, DW_BUF = DSE * DW_PITCH;
 
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
+template <bool kWide>
 struct WStage {
   uint2 c[4];
   uint32_t s[4];
+};
+template <>
+struct WStage<true> {
+  uint4 c[2];
+  uint32_t s;
 };
 
 template <int kSel>
@@ -673,8 +704,9 @@ __device__ __forceinline__ void fp4_pair_rows(const uint32_t (&w)[4], const floa
   }
 }
 
+template <bool kWide>
 __global__ __launch_bounds__(256, 2) void k_qat_dgrad2(QatParams p) {
-  __shared__ __attribute__((aligned(16))) uint4 wt[2][DBN * 16];
+  __shared__ __attribute__((aligned(16))) char wt[kWide ? 2 * DW_BUF : 2 * DBN * 256];
   int mt, nt;
   if (!pick_tile<kDgradGroupM>(p, mt, nt)) return;
   const int e = p.tiles[2 * mt];
@@ -705,44 +737,63 @@ __global__ __launch_bounds__(256, 2) void k_qat_dgrad2(QatParams p) {
   const uint8_t* const s_e = p.w_scales + (int64_t)e * Nc * (Ko >> 4);
   const uint32_t w_off = (uint32_t)(4 * q * (Ko >> 1) + (cw >> 1));
   const uint32_t s_off = (uint32_t)(4 * q * (Ko >> 4) + (cw >> 4));
-  auto w_load = [&](WStage& W, int step) {
+  // wide path: contraction row wr of the step, columns c0 + 64 wh .. +63
+  const int wr = t >> 1, wh = t & 1;
+  const uint32_t ww_off = (uint32_t)(wr * (Ko >> 1) + ((c0 + 64 * wh) >> 1));
+  const uint32_t ws_off = (uint32_t)(wr * (Ko >> 4) + ((c0 + 64 * wh) >> 4));
+  auto w_load = [&](WStage<kWide>& W, int step) {
+    if constexpr (kWide) {
+      const uint8_t* const cr = w_e + (int64_t)step * DSE * (Ko >> 1) + ww_off;
+      W.c[0] = *reinterpret_cast<const uint4*>(cr);
+      W.c[1] = *reinterpret_cast<const uint4*>(cr + 16);
+      W.s = *reinterpret_cast<const uint32_t*>(s_e + (int64_t)step * DSE * (Ko >> 4) + ws_off);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = (int64_t)step * DSE + r;
-      W.c[r] = *reinterpret_cast<const uint2*>(w_e + row * (Ko >> 1) + w_off);
-      W.s[r] = *(s_e + row * (Ko >> 4) + s_off);
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = (int64_t)step * DSE + r;
+        W.c[r] = *reinterpret_cast<const uint2*>(w_e + row * (Ko >> 1) + w_off);
+        W.s[r] = *(s_e + row * (Ko >> 4) + s_off);
+      }
     }
   };
-  char* const wt_base = reinterpret_cast<char*>(&wt[0][0]);
-  auto w_store = [&](const WStage& W, int buf) {
-    float sb[4];
-    uint32_t lo[4], hi[4];
+  char* const wt_base = &wt[0];
+  auto w_store = [&](const WStage<kWide>& W, int buf) {
+    if constexpr (kWide) {
+      char* const dst = wt_base + buf * DW_BUF + wr * DW_PITCH + 128 * wh;
+      const uint32_t w[8] = {W.c[0].x, W.c[0].y, W.c[0].z, W.c[0].w, W.c[1].x, W.c[1].y, W.c[1].z, W.c[1].w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sb[r] = e4m3_value(W.s[r]);
-      lo[r] = W.c[r].x;
-      hi[r] = W.c[r].y;
-    }
-    char* const dst = wt_base + buf * (DBN * 256) + 8 * (q & 1);
-    auto put = [&](const float (&f)[4][2], int u) {  // columns u, u + 1 of the block
+      for (int u = 0; u < 8; ++u)
+        *reinterpret_cast<uint4*>(dst + 16 * u) = fp4x8_to_bf16(w[u], e4m3_value((W.s >> (8 * (u >> 1))) & 0xFFu));
+    } else {
+      float sb[4];
+      uint32_t lo[4], hi[4];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int c = 16 * cb + u + k;
-        uint2 v;
-        v.x = __builtin_amdgcn_perm(__float_as_uint(f[1][k]), __float_as_uint(f[0][k]), 0x07060302u);
-        v.y = __builtin_amdgcn_perm(__float_as_uint(f[3][k]), __float_as_uint(f[2][k]), 0x07060302u);
-        *reinterpret_cast<uint2*>(dst + c * 256 + 16 * ((q >> 1) ^ (c & 15))) = v;
+      for (int r = 0; r < 4; ++r) {
+        sb[r] = e4m3_value(W.s[r]);
+        lo[r] = W.c[r].x;
+        hi[r] = W.c[r].y;
       }
-    };
-    float f[4][2];
-    fp4_pair_rows<0>(lo, sb, f); put(f, 0);
-    fp4_pair_rows<1>(lo, sb, f); put(f, 2);
-    fp4_pair_rows<2>(lo, sb, f); put(f, 4);
-    fp4_pair_rows<3>(lo, sb, f); put(f, 6);
-    fp4_pair_rows<0>(hi, sb, f); put(f, 8);
-    fp4_pair_rows<1>(hi, sb, f); put(f, 10);
-    fp4_pair_rows<2>(hi, sb, f); put(f, 12);
-    fp4_pair_rows<3>(hi, sb, f); put(f, 14);
+      char* const dst = wt_base + buf * (DBN * 256) + 8 * (q & 1);
+      auto put = [&](const float (&f)[4][2], int u) {  // columns u, u + 1 of the block
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int c = 16 * cb + u + k;
+          uint2 v;
+          v.x = __builtin_amdgcn_perm(__float_as_uint(f[1][k]), __float_as_uint(f[0][k]), 0x07060302u);
+          v.y = __builtin_amdgcn_perm(__float_as_uint(f[3][k]), __float_as_uint(f[2][k]), 0x07060302u);
+          *reinterpret_cast<uint2*>(dst + c * 256 + 16 * ((q >> 1) ^ (c & 15))) = v;
+        }
+      };
+      float f[4][2];
+      fp4_pair_rows<0>(lo, sb, f); put(f, 0);
+      fp4_pair_rows<1>(lo, sb, f); put(f, 2);
+      fp4_pair_rows<2>(lo, sb, f); put(f, 4);
+      fp4_pair_rows<3>(lo, sb, f); put(f, 6);
+      fp4_pair_rows<0>(hi, sb, f); put(f, 8);
+      fp4_pair_rows<1>(hi, sb, f); put(f, 10);
+      fp4_pair_rows<2>(hi, sb, f); put(f, 12);
+      fp4_pair_rows<3>(hi, sb, f); put(f, 14);
+    }
   };
 
   floatx4_t acc[4][8];
@@ -764,7 +815,13 @@ __global__ __launch_bounds__(256, 2) void k_qat_dgrad2(QatParams p) {
   // st + 1 is loaded first and dequantized into the other buffer after the
   // MFMAs.  Scheduling barriers between sub-steps keep every load where it is
   // issued (the scheduler otherwise sinks them next to their use).
-  auto step = [&](int st, WStage& W, bool next) {
+  // wide path transpose-read offsets: source lane s = l16 points at columns
+  // 4 (s & 3) .. +3 of contraction row 32 d + 8 g + 4 hf + s / 4
+  const NVQ_LDS char* const wt_lds = (const NVQ_LDS char*)wt;
+  uint32_t tr_off[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) tr_off[hf] = (uint32_t)((8 * g + 4 * hf + (l16 >> 2)) * DW_PITCH + 8 * (l16 & 3));
+  auto step = [&](int st, WStage<kWide>& W, bool next) {
     const int buf = st & 1;
     const char* const src = wt_base + buf * (DBN * 256);
     if (next) w_load(W, st + 1);
@@ -776,8 +833,13 @@ __global__ __launch_bounds__(256, 2) void k_qat_dgrad2(QatParams p) {
         bf16x8_t bfr[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int c = 16 * (4 * jh + jj) + l16;
-          bfr[jj] = *reinterpret_cast<const bf16x8_t*>(src + c * 256 + 16 * ((4 * d + g) ^ (c & 15)));
+          if constexpr (kWide) {
+            const uint32_t o = buf * DW_BUF + 32 * d * DW_PITCH + 32 * (4 * jh + jj);
+            bfr[jj] = tr_pair(wt_lds, tr_off[0] + o, tr_off[1] + o);
+          } else {
+            const int c = 16 * (4 * jh + jj) + l16;
+            bfr[jj] = *reinterpret_cast<const bf16x8_t*>(src + c * 256 + 16 * ((4 * d + g) ^ (c & 15)));
+          }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -796,7 +858,7 @@ __global__ __launch_bounds__(256, 2) void k_qat_dgrad2(QatParams p) {
     if (next) w_store(W, buf ^ 1);
   };
 
-  WStage W;
+  WStage<kWide> W;
   w_load(W, 0);
   w_store(W, 0);
   __syncthreads();
@@ -863,18 +925,6 @@ __global__ __launch_bounds__(256, 2) void k_qat_dgrad2(QatParams p) {
 constexpr int GBN = 256, GBC = 256, GPS = 32;
 constexpr int G_DY = GPS * GBN * 2, G_X = GPS * GBC * 2, G_TOK = 256;
 constexpr int G_STAGE = G_DY + G_X + G_TOK;
-
-#define NVQ_LDS __attribute__((address_space(3)))
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8_t tr_pair(const NVQ_LDS char* base, uint32_t off0, uint32_t off1) {
-  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((NVQ_LDS v4i16_t*)(base + off0));
-  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((NVQ_LDS v4i16_t*)(base + off1));
-  typedef short v8i16_t __attribute__((ext_vector_type(8)));
-  const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8_t, v);
-}
 
 // Global -> LDS direct loads; lane l lands at LDS byte lds_addr + size * l.
 // lds_addr must be wave-uniform; it is read from the first lane so that it
@@ -1173,7 +1223,11 @@ extern "C" int qat_fakequant_gemm_w4a16(const nvq_qat_gemm_args* a, void* stream
     p.n_tiles_n = (int)((a->K + DBN - 1) / DBN);
     const int64_t mt = (a->rows + DBM - 1) / DBM + a->E;
     const int64_t G2 = pick_grid(mt, kDgradGroupM, p.n_tiles_n);
-    hipLaunchKernelGGL(k_qat_dgrad2, dim3((unsigned)G2), dim3(256), 0, s, p);
+    // wide weight path: whole 128-column tiles, 16-byte code and 4-byte scale loads
+    if (a->K % DBN == 0 && ((uintptr_t)a->w_codes & 15u) == 0 && ((uintptr_t)a->w_scales & 3u) == 0)
+      hipLaunchKernelGGL(k_qat_dgrad2<true>, dim3((unsigned)G2), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_qat_dgrad2<false>, dim3((unsigned)G2), dim3(256), 0, s, p);
     return last_launch();
   }
   p.n_tiles_m = 0;

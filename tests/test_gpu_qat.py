@@ -105,6 +105,8 @@ def test_small_qat_all_modes(proj):
     (640, 288, (128, 0, 0, 200)),         # five forward steps, column tile + 32-column tail
     (160, 384, (300, 0, 257, 1)),         # three input-gradient steps, 32-column tail
     (96, 128, (0, 513, 40)),              # one input-gradient step, partial column tile
+    (256, 256, (0, 300, 5, 129)),         # input gradient, wide weight path: 2 column tiles, 2 steps
+    (384, 128, (77, 0, 260)),             # wide weight path: 3 column tiles, one step
 ])
 def test_fwd_dgrad_edge_shapes(K, N, counts):
     """Forward, input and weight gradient on shapes off the tile grid: row
