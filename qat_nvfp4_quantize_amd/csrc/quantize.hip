@@ -158,8 +158,10 @@ template <bool kBF16>
 struct RowBlock {
   uint4 q[kBF16 ? 2 : 4];
   __device__ __forceinline__ void load(const void* xv, int64_t row, int64_t K, int64_t blk) {
-    const uint4* p = reinterpret_cast<const uint4*>(
-        static_cast<const char*>(xv) + (row * K + blk * 16) * (kBF16 ? 2 : 4));
+    load_at(static_cast<const char*>(xv) + (row * K + blk * 16) * (kBF16 ? 2 : 4));
+  }
+  __device__ __forceinline__ void load_at(const char* at) {
+    const uint4* p = reinterpret_cast<const uint4*>(at);
 #pragma unroll
     for (int i = 0; i < (kBF16 ? 2 : 4); ++i) q[i] = p[i];
   }
@@ -422,13 +424,21 @@ __global__ __launch_bounds__(512, 2) void k_quantize(
     for (int j = 0; j < 16; ++j) acc[j] = res.acc[j];
     bad = res.bad;
   } else if (active && nrows > 0) {
-    auto process = [&](const RowBlock<kBF16>& rb, int64_t row) {
+    // Row addresses advance by adds (no 64-bit multiply per row); refills
+    // past the sub-chunk's last row are clamped to it.
+    const int64_t xrow = K * (kBF16 ? 2 : 4), crow = K >> 1;
+    const char* xp = static_cast<const char*>(xv) + (row0 * K + blk * 16) * (kBF16 ? 2 : 4);
+    const char* const xlast = xp + (last - row0) * xrow;
+    uint8_t* cp = codes + row0 * crow + blk * 8;
+    uint8_t* sp = scales + row0 * nblk + blk;
+    auto process = [&](const RowBlock<kBF16>& rb, uint8_t* c_at, uint8_t* s_at) {
       uint32_t sc;
       uint2 cw;
       encode_block_fast<kBF16, kScore>(rb, s_t, g, inv_st, sc, cw, acc, bad, slot);
-      *reinterpret_cast<uint2*>(codes + row * (K >> 1) + blk * 8) = cw;
-      scales[row * nblk + blk] = (uint8_t)sc;
+      *reinterpret_cast<uint2*>(c_at) = cw;
+      *s_at = (uint8_t)sc;
     };
+    auto clamp = [&](const char* a) { return a < xlast ? a : xlast; };
     // Three rotating row buffers: row rr + 3 is loaded into a buffer right
     // after that buffer's row is processed.  Refill addresses are clamped to
     // the last row instead of branching, so no load sits under a branch and
@@ -436,16 +446,18 @@ __global__ __launch_bounds__(512, 2) void k_quantize(
     // (clamped) but never processed.
 #pragma unroll 1
     for (int rr = 0; rr < nrows; rr += 3) {
-      const int64_t row = row0 + rr;
-      process(b0, row);
-      b0.load(xv, min(row + 3, last), K, blk);
+      process(b0, cp, sp);
+      b0.load_at(clamp(xp + 3 * xrow));
       __builtin_amdgcn_sched_barrier(0);
-      if (rr + 1 < nrows) process(b1, row + 1);
-      b1.load(xv, min(row + 4, last), K, blk);
+      if (rr + 1 < nrows) process(b1, cp + crow, sp + nblk);
+      b1.load_at(clamp(xp + 4 * xrow));
       __builtin_amdgcn_sched_barrier(0);
-      if (rr + 2 < nrows) process(b2, row + 2);
-      b2.load(xv, min(row + 5, last), K, blk);
+      if (rr + 2 < nrows) process(b2, cp + 2 * crow, sp + 2 * nblk);
+      b2.load_at(clamp(xp + 5 * xrow));
       __builtin_amdgcn_sched_barrier(0);
+      xp += 3 * xrow;
+      cp += 3 * crow;
+      sp += 3 * nblk;
     }
   }
 
