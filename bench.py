@@ -384,13 +384,17 @@ def main():
     wanted = args.legs.split(",")
     if "quant" not in wanted:
         wanted.append("quant")  # the headline value is the quantizer's
+    # Step order: the decode layer, then the quantizer (as in the rollout
+    # loop, where the next layer's activations are quantized right after a
+    # decode layer), then the rest.  Right after the QAT leg's 9.7 GB of
+    # writes the quantizer's first pass pays for evicting them.
+    from qat_nvfp4_quantize_amd import inputs as _inputs
+    if "moe" in wanted or "decode" in wanted:
+        legs.append(MoeLeg(_inputs.DECODE))
     if "quant" in wanted:
         legs.append(QuantLeg())
     if "copy" in wanted:
         legs.append(CopyLeg())
-    from qat_nvfp4_quantize_amd import inputs as _inputs
-    if "moe" in wanted or "decode" in wanted:
-        legs.append(MoeLeg(_inputs.DECODE))
     if "moe" in wanted or "prefill" in wanted:
         legs.append(MoeLeg(_inputs.PREFILL))
     if "qat" in wanted:
