@@ -66,6 +66,12 @@ def lib():
                 f.restype = ctypes.c_int
                 f.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P]
             L.orc_dequantize_f32.argtypes = [_P, _P, _F, _I64, _I64, _P]
+            L.orc_guidance_record.restype = ctypes.c_int
+            L.orc_guidance_record.argtypes = [_P, ctypes.c_int, _I64, _I64, _P, _P, _F,
+                                              ctypes.c_int, _P]
+            L.orc_guided_quantize.restype = ctypes.c_int
+            L.orc_guided_quantize.argtypes = [_P, ctypes.c_int, _I64, _I64, _P, _P, _F,
+                                              ctypes.c_int, _P]
             L.orc_dequantize_bf16.argtypes = [_P, _P, _F, _I64, _I64, _P]
             L.orc_residual_scores.argtypes = [_P, ctypes.c_int, _I64, _P, _P, _F, _I64, _I64, _P]
             L.orc_topk.argtypes = [_P, _I64, _I64, _P]
@@ -144,6 +150,41 @@ def quantize(x, amax_in=None, threshold_form=False):
     if rc != 0:
         raise ValueError("oracle quantize failed: %d" % rc)
     return codes, scales, float(st[0])
+
+
+GUIDE_MANTISSA, GUIDE_DIRECTION = 0, 1
+
+
+def guidance_record(codes, scales, s_t, mode, x=None):
+    """TRACE guidance record of a quantized [rows, K] tensor: bits [rows, K/8]
+    (element c in bit c % 8 of byte c // 8).  Mantissa mode keeps each code's
+    mantissa bit; direction mode keeps whether the rollout rounded |x| up
+    (x needed)."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    rows, K = codes.shape[0], codes.shape[1] * 2
+    xa, dt = (None, F32) if x is None else _as_input(x)
+    bits = np.empty((rows, K // 8), np.uint8)
+    rc = lib().orc_guidance_record(_ptr(xa), dt, rows, K, _ptr(codes), _ptr(scales), s_t, mode,
+                                   _ptr(bits))
+    if rc != 0:
+        raise ValueError("oracle guidance_record failed: %d" % rc)
+    return bits
+
+
+def guided_quantize(w, bits, scales, s_t, mode):
+    """Codes [rows, K/2] of a (drifted) master tensor w rebuilt from a guidance
+    record (bits, cached scales, cached s_t)."""
+    wa, dt = _as_input(w)
+    rows, K = wa.shape
+    bits = _c(bits, np.uint8)
+    scales = _c(scales, np.uint8)
+    codes = np.empty((rows, K // 2), np.uint8)
+    rc = lib().orc_guided_quantize(_ptr(wa), dt, rows, K, _ptr(bits), _ptr(scales), s_t, mode,
+                                   _ptr(codes))
+    if rc != 0:
+        raise ValueError("oracle guided_quantize failed: %d" % rc)
+    return codes
 
 
 def dequantize(codes, scales, s_t, out="f32"):

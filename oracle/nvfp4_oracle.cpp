@@ -259,6 +259,55 @@ double residual_bf16(const void* x, int dtype, int64_t ldx, const uint8_t* codes
   return (double)bf16_bits_to_float(float_to_bf16_rne(res));
 }
 
+// ------------------------------------------------ rollout-guided rounding --
+//
+// TRACE post, "L'idée centrale de TRACE": the rollout's quantization result
+// guides the trainer's rounding, and the cache keeps only the mantissa and the
+// scale factors.  "Fonctionnement, côté ingénierie": for each value, rounding
+// to the grid point above or below is the one discrete choice that the trainer
+// must make the same way as the rollout.  Two one-bit-per-element records are
+// defined (the second is the up/down reading of the same passage):
+//   mantissa  (mode 0): the mantissa bit of the rollout's E2M1 code (index & 1);
+//   direction (mode 1): 1 when the rollout's magnitude G[i] s_b s_t lies
+//                       strictly above |x| (rounded up), else 0.
+// The record also carries the rollout's block scales and tensor scale, which
+// the trainer reuses unchanged.
+
+// One record bit for element x whose rollout code has magnitude index i.
+// G[i] * s_b * s_t is exact in fp64 (<= 2 + 4 + 24 significant bits), so the
+// comparison with |x| is exact.
+int guidance_bit(float x, int i, double s_b, double s_t, int mode) {
+  if (mode == 0) return i & 1;
+  return kE2M1[i] * s_b * s_t > std::fabs((double)x) ? 1 : 0;
+}
+
+// Magnitude index chosen for a (possibly drifted) master value w under the
+// cached block scale s_b, tensor scale s_t and record bit.  On the scaled grid
+// G[i] s_b s_t the value |w| has a lower neighbour lo (largest i with
+// G[i] s_b s_t <= |w|) and an upper neighbour hi (smallest i with
+// G[i] s_b s_t >= |w|; none beyond 6 s_b s_t).
+//   mantissa:  the two adjacent grid points a = min(lo, 6) and a + 1 have
+//              different mantissa bits; take the one whose bit is the cached
+//              bit.
+//   direction: bit 1 takes hi (7 beyond the grid), bit 0 takes lo.
+// A block whose scale product is 0 has magnitude 0.  All products are exact
+// in fp64, so every comparison is exact.
+int guided_index(double aw, double s_b, double s_t, int mode, int bit) {
+  if (s_b * s_t == 0.0) return 0;
+  int lo = 0;
+  for (int i = 0; i < 8; ++i)
+    if (kE2M1[i] * s_b * s_t <= aw) lo = i;
+  int hi = -1;
+  for (int i = 7; i >= 0; --i)
+    if (kE2M1[i] * s_b * s_t >= aw) hi = i;
+  if (mode == 0) {
+    const int a = std::min(lo, 6);
+    return (a & 1) == bit ? a : a + 1;
+  }
+  if (bit) return hi < 0 ? 7 : hi;
+  return lo;
+}
+
 }  // namespace
 
 extern "C" {
@@ -293,6 +342,58 @@ int orc_quantize_threshold_form(const void* x, int dtype, int64_t rows, int64_t 
                                 const float* amax_in, uint8_t* codes, uint8_t* scales,
                                 float* s_t) {
   return quantize_impl(x, dtype, rows, K, ldx, amax_in, codes, scales, s_t, true);
+}
+
+// Guidance record of a quantized [rows, K] tensor (one s_t): bits
+// [rows, K/8], element c in bit (c & 7) of byte c / 8.  x (the value that was
+// quantized) is read only in direction mode and may be NULL in mantissa mode.
+// Returns 0, -2 (shape), -1 (mode or missing x).
+int orc_guidance_record(const void* x, int dtype, int64_t rows, int64_t K, const uint8_t* codes,
+                        const uint8_t* scales, float s_t, int mode, uint8_t* bits) {
+  if (K <= 0 || K % 16 != 0 || rows < 0) return -2;
+  if ((mode != 0 && mode != 1) || (mode == 1 && !x)) return -1;
+  parallel_for(rows, [&](int64_t r) {
+    for (int64_t c8 = 0; c8 < K / 8; ++c8) {
+      uint8_t byte = 0;
+      for (int j = 0; j < 8; ++j) {
+        const int64_t c = c8 * 8 + j;
+        const uint8_t cb = codes[r * (K / 2) + c / 2];
+        const int i = ((c & 1) ? (cb >> 4) : cb) & 7;
+        const double s_b = e4m3_value(scales[r * (K / 16) + c / 16]);
+        const float xv = mode == 1 ? load_elem(x, dtype, r, K, c) : 0.0f;
+        byte |= (uint8_t)(guidance_bit(xv, i, s_b, (double)s_t, mode) << j);
+      }
+      bits[r * (K / 8) + c8] = byte;
+    }
+  });
+  return 0;
+}
+
+// Codes of a (possibly drifted) master tensor w [rows, K] rebuilt from the
+// rollout's guidance record (bits, scales, s_t): sign from signbit(w),
+// magnitude from guided_index.  Returns 0, -2 (shape), -1 (mode),
+// -3 (non-finite w).
+int orc_guided_quantize(const void* w, int dtype, int64_t rows, int64_t K, const uint8_t* bits,
+                        const uint8_t* scales, float s_t, int mode, uint8_t* codes) {
+  if (K <= 0 || K % 16 != 0 || rows < 0) return -2;
+  if (mode != 0 && mode != 1) return -1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < K; ++c)
+      if (!std::isfinite(load_elem(w, dtype, r, K, c))) return -3;
+  parallel_for(rows, [&](int64_t r) {
+    for (int64_t c = 0; c < K; c += 2) {
+      uint8_t nib[2];
+      for (int h = 0; h < 2; ++h) {
+        const float v = load_elem(w, dtype, r, K, c + h);
+        const int bit = (bits[r * (K / 8) + (c + h) / 8] >> ((c + h) & 7)) & 1;
+        const double s_b = e4m3_value(scales[r * (K / 16) + (c + h) / 16]);
+        const int i = guided_index(std::fabs((double)v), s_b, (double)s_t, mode, bit);
+        nib[h] = (uint8_t)((std::signbit(v) ? 8 : 0) | i);
+      }
+      codes[r * (K / 2) + c / 2] = (uint8_t)(nib[0] | (nib[1] << 4));
+    }
+  });
+  return 0;
 }
 
 // Dequantize to fp32 [rows, K] (D).

@@ -21,6 +21,9 @@ shapes):
              weights N(0, 0.02^2) with 1% of each expert's K-channels x10.
   5 qat      T=16384, H=4096, E=128, I=1536, top-8, N(0,1) logits; bf16 master
              weights N(0, 0.02^2); X and per-projection dY bf16 N(0,1).
+             Drifted masters for the rollout-guided rounding (TRACE post): the
+             bf16 master plus an independent N(0, 0.002^2) draw (a tenth of the
+             weights' spread; the pages give no step size), rounded to bf16.
 """
 from __future__ import annotations
 
@@ -67,7 +70,9 @@ PREFILL = MoEShape(wid=4, T=32768, H=4096, E=128, I=1536, topk=8, k=128)
 QAT = MoEShape(wid=5, T=16384, H=4096, E=128, I=1536, topk=8, k=0)
 
 # tensor ids within a workload
-_X, _W, _OUTLIER, _LOGITS, _WGU, _WDN, _DYGU, _DYDN, _WOUT, _HID = range(10)
+_X, _W, _OUTLIER, _LOGITS, _WGU, _WDN, _DYGU, _DYDN, _WOUT, _HID, _DRIFT = range(11)
+
+DRIFT_STD = 0.002
 
 
 # ------------------------------------------------------------- workload 1 --
@@ -174,3 +179,27 @@ def weights_device(s: MoEShape, proj: str, device="cuda"):
             we[:, cols] *= 10.0
         w[e] = we.to(torch.bfloat16)
     return w
+
+
+def drifted_expert_weight(s: MoEShape, proj: str, e: int) -> np.ndarray:
+    """bf16 bits [N, K]: expert e's bf16 master plus its own N(0, DRIFT_STD^2)
+    draw, rounded to bf16 (the master after the trainer's update)."""
+    tid = _WGU if proj == "gu" else _WDN
+    w = bf16_bits_to_f32(expert_weight(s, proj, e))
+    d = rng(s.wid, _DRIFT, tid, e).standard_normal(w.shape, dtype=np.float32)
+    return to_bf16_bits(w + d * np.float32(DRIFT_STD))
+
+
+def drift_device(w, s: MoEShape, proj: str):
+    """bf16 [E, N, K]: the GPU-drawn masters w plus a seeded N(0, DRIFT_STD^2)
+    draw (torch Philox stream of its own), rounded to bf16."""
+    import torch
+
+    tid = _WGU if proj == "gu" else _WDN
+    g = torch.Generator(device=w.device)
+    g.manual_seed(BASE_SEED * 1_000_003 + s.wid * 1009 + 100 + tid)
+    out = torch.empty_like(w)
+    for e in range(w.shape[0]):
+        d = torch.randn(w.shape[1:], generator=g, device=w.device, dtype=torch.float32)
+        out[e] = (w[e].float() + d * DRIFT_STD).to(torch.bfloat16)
+    return out
