@@ -8,7 +8,9 @@ One step = one pass of every measured leg over its seeded synthetic workload
           per-channel residual sums, then the top-64 residual channels.
   moe     (when built) the MoE rollout layer with W4A4 grouped GEMMs and
           residual compensation.
-  qat     (when built) the asymmetric W4A16 QAT layer forward + backward.
+  qat     (when built) the asymmetric W4A16 QAT layer: codes of the drifted
+          master weights rebuilt from the rollout's guidance record, then
+          forward + backward.
 
 Prints ONE JSON line.  `value` is the quantizer's algorithmic GB/s (x read
 once, codes + scales + scores written); the GEMM legs report TFLOP/s in
@@ -275,11 +277,20 @@ class QatLeg:
         self.hin = torch.randn(s.P, s.I, generator=g, device=dev).to(bf)
         self.dy_gu = torch.randn(s.P, 2 * s.I, generator=g, device=dev).to(bf)
         self.dy_dn = torch.randn(s.P, s.H, generator=g, device=dev).to(bf)
-        self.q = {}
+        # The rollout's record of each projection (codes, scales, s_t) and its
+        # compact guidance record (mantissa bits); the trainer's masters have
+        # drifted since, and each step rebuilds their codes from the record.
+        self.q, self.rec, self.wd, self.gcodes = {}, {}, {}, {}
         for proj in ("gu", "dn"):
             w = inputs.weights_device(s, proj, dev)
             self.q[proj] = nvq.nvfp4_quantize(w)[:3]
+            self.rec[proj] = nvq.nvfp4_guidance_record(self.q[proj][0], nvq.NVQ_GUIDE_MANTISSA)
+            self.wd[proj] = inputs.drift_device(w, s, proj)
+            self.gcodes[proj] = torch.empty_like(self.q[proj][0])
             del w
+        n_gu, n_dn = self.wd["gu"].numel(), self.wd["dn"].numel()
+        # read w (bf16) + bits + scales, write codes: 2 + 1/8 + 1/16 + 1/2 B/elem
+        self.guide_bytes = {"gu": n_gu * 43 // 16, "dn": n_dn * 43 // 16}
         P = s.P
         self.y_gu = torch.empty(P, 2 * s.I, dtype=bf, device=dev)
         self.y_dn = torch.empty(P, s.H, dtype=bf, device=dev)
@@ -298,7 +309,13 @@ class QatLeg:
         nvq, s = self.nvq, self.s
         timer = lambda label, fn: timer_("qat/" + label, fn)
         F, D, W = nvq.NVQ_QAT_FWD, nvq.NVQ_QAT_DGRAD, nvq.NVQ_QAT_WGRAD
-        qg, qd = self.q["gu"], self.q["dn"]
+        for proj in ("gu", "dn"):
+            _, sc, st = self.q[proj]
+            timer("guide_" + proj, lambda proj=proj, sc=sc, st=st: nvq.nvfp4_guided_quantize(
+                self.wd[proj], self.rec[proj], sc, st, nvq.NVQ_GUIDE_MANTISSA,
+                out=self.gcodes[proj]))
+        qg = (self.gcodes["gu"], *self.q["gu"][1:])
+        qd = (self.gcodes["dn"], *self.q["dn"][1:])
         call = nvq.qat_fakequant_gemm_w4a16
         timer("fwd_gu", lambda: call(F, *qg, self.off, s.P, x=self.x, a_row=self.a_row, ws=self.ws,
                                      out=(self.y_gu, None)))
@@ -323,6 +340,16 @@ class QatLeg:
         out["tflops"] = round(tot_f / (tot_ms * 1e-3) / 1e12, 1)
         out["frac_bf16_mfma_peak"] = round(out["tflops"] / BF16_PEAK_TFLOPS, 4)
         out["algorithmic_tflop"] = round(tot_f / 1e12, 3)
+        g = {}
+        for proj in ("gu", "dn"):
+            ms = timer.avg_ms("qat/guide_" + proj)
+            g[proj + "_ms"] = round(ms, 4)
+            g[proj + "_GBps"] = round(self.guide_bytes[proj] / (ms * 1e-3) / 1e9, 1)
+        tot = sum(self.guide_bytes.values()) / ((g["gu_ms"] + g["dn_ms"]) * 1e-3) / 1e9
+        g["GBps"] = round(tot, 1)
+        g["frac_hbm_peak"] = round(tot / HBM_PEAK_GBS, 4)
+        g["algorithmic_bytes"] = sum(self.guide_bytes.values())
+        out["guided_requantize"] = g
         return out
 
 

@@ -110,6 +110,53 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
                      int64_t batch, int64_t rows, int64_t K, void* y, int y_dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Rollout-guided rounding (TRACE post: "L'idée centrale de TRACE" -- the
+ * rollout's quantization guides the trainer's rounding and the cache keeps
+ * only the mantissa and the scale factors; "Fonctionnement, côté ingénierie"
+ * -- each value rounds to the grid point above or below, the discrete choice
+ * both sides must share).
+ *
+ * The guidance record of a quantized tensor is one bit per element, bits
+ * [batch, rows, K/8] u8 (element c of a row in bit c % 8 of byte c / 8), kept
+ * with the rollout's block scales and tensor scale: 0.1875 byte per element
+ * against 0.5625 for codes + scales.
+ *   NVQ_GUIDE_MANTISSA   the mantissa bit (index & 1) of the rollout's code;
+ *   NVQ_GUIDE_DIRECTION  1 when the rollout's magnitude G s_b s_t lies strictly
+ *                        above |x| (rounded up), else 0.
+ */
+enum { NVQ_GUIDE_MANTISSA = 0, NVQ_GUIDE_DIRECTION = 1 };
+
+/* Writes the guidance record `bits` of the NVFP4 record (codes [batch, rows,
+ * K/2], scales [batch, rows, K/16], tensor_scale [batch]) of x.  Mantissa mode
+ * reads only the codes (x, scales, tensor_scale may be NULL); direction mode
+ * reads x [batch, rows, K] (x_dtype NVQ_F32 or NVQ_BF16, 16-byte aligned), the
+ * value that was quantized.  K % 16 == 0; codes 8-byte and bits 2-byte
+ * aligned.  Device pointers, caller-owned; asynchronous on stream.  Errors
+ * (NVQ_EINVAL, NVQ_ESHAPE, NVQ_EALIGN) launch nothing. */
+int nvfp4_guidance_record(const void* x, int x_dtype, const uint8_t* codes, const uint8_t* scales,
+                          const float* tensor_scale, int64_t batch, int64_t rows, int64_t K,
+                          int mode, uint8_t* bits, void* stream);
+
+/* Rebuilds NVFP4 codes [batch, rows, K/2] for master values w [batch, rows, K]
+ * (w_dtype NVQ_F32 or NVQ_BF16, e.g. weights the trainer has updated since the
+ * rollout quantized them) from a guidance record: the rollout's scales
+ * [batch, rows, K/16] and tensor_scale [batch] are reused unchanged, and for
+ * each element, with lo / hi the indices of the grid points G s_b s_t at or
+ * below / at or above |w| (hi = 7 beyond the grid):
+ *   mantissa:  of a = min(lo, 6) and a + 1, the one whose mantissa bit is the
+ *              recorded bit (adjacent E2M1 points differ in that bit);
+ *   direction: recorded 1 -> hi, 0 -> lo.
+ * The sign is signbit(w); a zero block or tensor scale gives magnitude 0.
+ * Decisions are exact.  With w equal to the quantized tensor this gives back
+ * the rollout's codes.  ws is nullable (else 256-byte aligned, >= 256 bytes):
+ * a non-finite w sets NVQ_STATUS_NONFINITE in its status word (that element's
+ * code is then unspecified).  w 16-byte, codes 8-byte, bits 2-byte aligned.
+ * Errors (NVQ_EINVAL, NVQ_ESHAPE, NVQ_EALIGN, NVQ_EWORKSPACE) launch nothing. */
+int nvfp4_guided_quantize(const void* w, int w_dtype, int64_t batch, int64_t rows, int64_t K,
+                          const uint8_t* bits, const uint8_t* scales, const float* tensor_scale,
+                          int mode, uint8_t* codes, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Residual-channel selection (QUADS §2.2-B).
  *
  * Selects the k channels with the largest residual score (ties to the lower

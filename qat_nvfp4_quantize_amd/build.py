@@ -23,6 +23,7 @@ ARCH = os.environ.get("NVQ_OFFLOAD_ARCH", "gfx950")
 EXTRA = {
     "quantize.hip": ["-ffp-contract=off"],
     "moe.hip": ["-ffp-contract=off"],
+    "guided.hip": ["-ffp-contract=off"],
 }
 
 COMMON = [

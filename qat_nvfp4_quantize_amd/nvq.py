@@ -20,6 +20,7 @@ NVQ_EPI_NONE, NVQ_EPI_SWIGLU = 0, 1
 NVQ_GEMM_AUTO, NVQ_GEMM_DEQ16, NVQ_GEMM_FP8_BLOCK = 0, 1, 2
 NVQ_QAT_FWD, NVQ_QAT_DGRAD, NVQ_QAT_WGRAD = 0, 1, 2
 NVQ_STATUS_NONFINITE, NVQ_STATUS_BAD_EXPERT = 1, 2
+NVQ_GUIDE_MANTISSA, NVQ_GUIDE_DIRECTION = 0, 1
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -65,6 +66,10 @@ _SIGS = [
     ("nvfp4_quantize", ctypes.c_int,
      [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("nvfp4_dequantize", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P]),
+    ("nvfp4_guidance_record", ctypes.c_int,
+     [_P, ctypes.c_int, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
+    ("nvfp4_guided_quantize", ctypes.c_int,
+     [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, ctypes.c_int, _P, _P, _SZ, _P]),
     ("residual_topk_workspace_bytes", _SZ, [_I64, _I64, _I32]),
     ("residual_topk_channels", ctypes.c_int,
      [_P, ctypes.c_int, _I64, _I64, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
@@ -183,6 +188,46 @@ def nvfp4_dequantize(codes, scales, tensor_scale, out_dtype=torch.float32, batch
                                  _ptr(y), _dtype_code(y), _stream())
     _check("nvfp4_dequantize", rc)
     return y
+
+
+def _batch_rows(t, per_row, batch):
+    """(batch, rows) of a [rows, n] or [batch, rows, n] tensor."""
+    if batch is None:
+        batch = t.shape[0] if t.dim() == 3 else 1
+    return batch, t.numel() // per_row // batch
+
+
+def nvfp4_guidance_record(codes, mode, x=None, scales=None, tensor_scale=None, batch=None,
+                          out=None):
+    """TRACE guidance record of an NVFP4 record: bits u8 [..., K/8].  Mantissa
+    mode needs only the codes; direction mode needs x (the quantized values),
+    scales and tensor_scale."""
+    _dev(codes, "codes")
+    K = codes.shape[-1] * 2
+    batch, rows = _batch_rows(codes, K // 2, batch)
+    bits = out if out is not None else torch.empty(
+        *codes.shape[:-1], K // 8, dtype=torch.uint8, device=codes.device)
+    xd = _dtype_code(x) if x is not None else NVQ_F32
+    rc = load().nvfp4_guidance_record(_ptr(x), xd, _ptr(codes), _ptr(scales), _ptr(tensor_scale),
+                                      batch, rows, K, mode, _ptr(bits), _stream())
+    _check("nvfp4_guidance_record", rc)
+    return bits
+
+
+def nvfp4_guided_quantize(w, bits, scales, tensor_scale, mode, ws=None, out=None):
+    """Codes u8 [..., K/2] of master values w rebuilt from a guidance record
+    (bits, the rollout's scales and tensor scales).  ws (optional, >= 256
+    bytes) receives the non-finite status bit."""
+    _dev(w, "w")
+    K = w.shape[-1]
+    batch, rows = _batch_rows(w, K, None)
+    codes = out if out is not None else torch.empty(
+        *w.shape[:-1], K // 2, dtype=torch.uint8, device=w.device)
+    rc = load().nvfp4_guided_quantize(_ptr(w), _dtype_code(w), batch, rows, K, _ptr(bits),
+                                      _ptr(scales), _ptr(tensor_scale), mode, _ptr(codes),
+                                      _ptr(ws), 0 if ws is None else ws.numel(), _stream())
+    _check("nvfp4_guided_quantize", rc)
+    return codes
 
 
 def residual_topk_channels(x, codes, scales, tensor_scale, k, scores=None, want_scores=False,

@@ -89,3 +89,32 @@ def test_gemm_args_validation():
     q = nvq.QatGemmArgs()
     q.struct_size = 8
     assert L.qat_fakequant_gemm_w4a16(ctypes.byref(q), None) in (-1, -6)
+
+
+def test_guided_rounding_validation():
+    L = _lib()
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    # record: bad mode, direction mode without x, K % 16, misaligned codes / bits / x
+    assert L.nvfp4_guidance_record(None, 0, fake, None, None, 1, 4, 32, 2, fake, None) == -1
+    assert L.nvfp4_guidance_record(None, 0, fake, fake, fake, 1, 4, 32, 1, fake, None) == -1
+    assert L.nvfp4_guidance_record(None, 0, fake, None, None, 1, 4, 24, 0, fake, None) == -2
+    assert L.nvfp4_guidance_record(None, 0, P(0x1004), None, None, 1, 4, 32, 0, fake, None) == -3
+    assert L.nvfp4_guidance_record(None, 0, fake, None, None, 1, 4, 32, 0, P(0x1001), None) == -3
+    assert L.nvfp4_guidance_record(P(0x1008), 1, fake, fake, fake, 1, 4, 32, 1, fake, None) == -3
+    # no rows: nothing to do, NULL buffers allowed
+    assert L.nvfp4_guidance_record(None, 0, None, None, None, 1, 0, 32, 0, None, None) == 0
+    # guided requantization: bad dtype / mode, null pointers, shape, alignment, workspace
+    assert L.nvfp4_guided_quantize(fake, 5, 1, 4, 32, fake, fake, fake, 0, fake, None, 0, None) == -1
+    assert L.nvfp4_guided_quantize(fake, 1, 1, 4, 32, fake, fake, fake, 3, fake, None, 0, None) == -1
+    assert L.nvfp4_guided_quantize(fake, 1, 1, 4, 32, None, fake, fake, 0, fake, None, 0, None) == -1
+    assert L.nvfp4_guided_quantize(fake, 1, 1, 4, 40, fake, fake, fake, 0, fake, None, 0, None) == -2
+    assert L.nvfp4_guided_quantize(fake, 1, 0, 4, 32, fake, fake, fake, 0, fake, None, 0, None) == -2
+    assert L.nvfp4_guided_quantize(P(0x1008), 1, 1, 4, 32, fake, fake, fake, 0, fake, None, 0,
+                                   None) == -3
+    assert L.nvfp4_guided_quantize(fake, 1, 1, 4, 32, fake, fake, fake, 0, P(0x1004), None, 0,
+                                   None) == -3
+    assert L.nvfp4_guided_quantize(fake, 1, 1, 4, 32, fake, fake, fake, 0, fake, P(0x1080), 256,
+                                   None) == -3
+    assert L.nvfp4_guided_quantize(fake, 1, 1, 4, 32, fake, fake, fake, 0, fake, fake, 255,
+                                   None) == -4
