@@ -130,8 +130,8 @@ enum { NVQ_GUIDE_MANTISSA = 0, NVQ_GUIDE_DIRECTION = 1 };
  * K/2], scales [batch, rows, K/16], tensor_scale [batch]) of x.  Mantissa mode
  * reads only the codes (x, scales, tensor_scale may be NULL); direction mode
  * reads x [batch, rows, K] (x_dtype NVQ_F32 or NVQ_BF16, 16-byte aligned), the
- * value that was quantized.  K % 16 == 0; codes 8-byte and bits 2-byte
- * aligned.  Device pointers, caller-owned; asynchronous on stream.  Errors
+ * value that was quantized.  K % 16 == 0, 1 <= batch <= 65535; codes 8-byte
+ * and bits 2-byte aligned.  Device pointers, caller-owned; asynchronous on stream.  Errors
  * (NVQ_EINVAL, NVQ_ESHAPE, NVQ_EALIGN) launch nothing. */
 int nvfp4_guidance_record(const void* x, int x_dtype, const uint8_t* codes, const uint8_t* scales,
                           const float* tensor_scale, int64_t batch, int64_t rows, int64_t K,
@@ -150,7 +150,8 @@ int nvfp4_guidance_record(const void* x, int x_dtype, const uint8_t* codes, cons
  * Decisions are exact.  With w equal to the quantized tensor this gives back
  * the rollout's codes.  ws is nullable (else 256-byte aligned, >= 256 bytes):
  * a non-finite w sets NVQ_STATUS_NONFINITE in its status word (that element's
- * code is then unspecified).  w 16-byte, codes 8-byte, bits 2-byte aligned.
+ * code is then unspecified).  K % 16 == 0, 1 <= batch <= 65535; w 16-byte,
+ * codes 8-byte, bits 2-byte aligned.
  * Errors (NVQ_EINVAL, NVQ_ESHAPE, NVQ_EALIGN, NVQ_EWORKSPACE) launch nothing. */
 int nvfp4_guided_quantize(const void* w, int w_dtype, int64_t batch, int64_t rows, int64_t K,
                           const uint8_t* bits, const uint8_t* scales, const float* tensor_scale,

@@ -84,10 +84,11 @@ __device__ __forceinline__ void load_block(const void* __restrict__ x, int64_t b
 template <int kMode, bool kBF16>
 __global__ __launch_bounds__(kGuideThreads) void k_guidance_record(
     const void* __restrict__ x, const uint2* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const float* __restrict__ tensor_scale, int64_t n_blocks, int64_t blocks_per_item,
+    const float* __restrict__ tensor_scale, int64_t blocks_per_item,
     uint16_t* __restrict__ bits) {
-  const int64_t blk = (int64_t)blockIdx.x * kGuideThreads + threadIdx.x;
-  if (blk >= n_blocks) return;
+  const int64_t in_item = (int64_t)blockIdx.x * kGuideThreads + threadIdx.x;
+  if (in_item >= blocks_per_item) return;
+  const int64_t blk = (int64_t)blockIdx.y * blocks_per_item + in_item;
   const uint2 cw = codes[blk];
   uint32_t out = 0;
   if (kMode == NVQ_GUIDE_MANTISSA) {
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(kGuideThreads) void k_guidance_record(
     float v[16];
     load_block<kBF16>(x, blk, v);
     const float s_b = e4m3_to_f32(scales[blk]);
-    const double s_t = (double)tensor_scale[blk / blocks_per_item];
+    const double s_t = (double)tensor_scale[blockIdx.y];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const uint32_t nib = ((j < 8 ? cw.x : cw.y) >> (4 * (j & 7))) & 7u;
@@ -117,17 +118,49 @@ __global__ __launch_bounds__(kGuideThreads) void k_guidance_record(
 template <int kMode, bool kBF16>
 __global__ __launch_bounds__(kGuideThreads) void k_guided_quantize(
     const void* __restrict__ w, const uint16_t* __restrict__ bits,
-    const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t n_blocks,
+    const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale,
     int64_t blocks_per_item, uint2* __restrict__ codes, uint32_t* __restrict__ status) {
-  const int64_t blk = (int64_t)blockIdx.x * kGuideThreads + threadIdx.x;
-  if (blk >= n_blocks) return;
+  const int64_t in_item = (int64_t)blockIdx.x * kGuideThreads + threadIdx.x;
+  if (in_item >= blocks_per_item) return;
+  const int64_t blk = (int64_t)blockIdx.y * blocks_per_item + in_item;
   float v[16];
   load_block<kBF16>(w, blk, v);
   const uint32_t rec = bits[blk];
   const float s_b = e4m3_to_f32(scales[blk]);
-  const double s_t = (double)tensor_scale[blk / blocks_per_item];
+  const double s_t = (double)tensor_scale[blockIdx.y];
   const bool zero_scale = (double)s_b * s_t == 0.0;
 
+  // one non-finite test per block: the largest |w| bit pattern
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) amax_bits = max(amax_bits, __float_as_uint(v[j]) & 0x7FFFFFFFu);
+  const bool nonfinite = amax_bits >= 0x7F800000u;
+  uint32_t out[2] = {0u, 0u};
+  if (kMode == NVQ_GUIDE_MANTISSA && s_t >= 0x1p-100 && s_t <= 0x1p100 && !zero_scale) {
+    // Fast path.  Here every threshold is a normal fp32 number, RU(2^k p) =
+    // 2^k RU(p), and bits(2^k T) = bits(T) + k 2^23; the bit patterns of
+    // non-negative floats order as the values.  With R1 = RU(s_b s_t) and
+    // R15 = RU(1.5 s_b s_t) the grid thresholds are
+    //   points 1, 3, 5 (even result, bit 0): R1 / 2, R15, 2 R15
+    //   points 2, 4, 6 (odd result, bit 1):  R1, 2 R1, 4 R1
+    // and the chosen index is 2 * (number of those thresholds <= |w|) + bit:
+    // of the two neighbours of |w|, the one with the recorded mantissa bit.
+    // The last two thresholds of each set are one binade apart, so their
+    // count is clamp((bits(|w|) - bits(first) + 2^23) >> 23, 0, 2).
+    const int32_t r1 = (int32_t)__float_as_uint(f32_round_up((double)s_b * s_t));
+    const int32_t r15 = (int32_t)__float_as_uint(f32_round_up((double)(1.5f * s_b) * s_t));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t u = __float_as_uint(v[j]);
+      const int32_t a = (int32_t)(u & 0x7FFFFFFFu);
+      const uint32_t b = (rec >> j) & 1u;
+      const int32_t t0 = b ? r1 : r1 - (1 << 23);
+      const int32_t base = b ? r1 : r15 - (1 << 23);
+      const int32_t pair = min(max((a - base) >> 23, 0), 2);
+      const uint32_t idx = 2u * (uint32_t)(pair + (a >= t0)) + b;
+      out[j >> 3] |= (idx | ((u >> 28) & 8u)) << (4 * (j & 7));
+    }
+  } else {
   // thresholds of grid points 1..7: RU for "point <= |w|", RD for "point < |w|"
   float up[7], dn[7];
 #pragma unroll
@@ -136,13 +169,9 @@ __global__ __launch_bounds__(kGuideThreads) void k_guided_quantize(
     up[i] = f32_round_up(p);
     if (kMode == NVQ_GUIDE_DIRECTION) dn[i] = f32_round_down(p);
   }
-
-  uint32_t nonfinite = 0;
-  uint32_t out[2] = {0u, 0u};
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const uint32_t u = __float_as_uint(v[j]);
-    nonfinite |= (~u & 0x7F800000u) == 0u;
     const float aw = fabsf(v[j]);
     uint32_t lo = 0;
 #pragma unroll
@@ -163,9 +192,10 @@ __global__ __launch_bounds__(kGuideThreads) void k_guided_quantize(
     const uint32_t nib = idx | ((u >> 28) & 8u);
     out[j >> 3] |= nib << (4 * (j & 7));
   }
+  }
   codes[blk] = make_uint2(out[0], out[1]);
   if (status) {
-    const uint64_t any = __ballot(nonfinite != 0u);
+    const uint64_t any = __ballot(nonfinite);
     if (any != 0ull && (threadIdx.x & (kWave - 1)) == (unsigned)__builtin_ctzll(any))
       atomicOr(status, NVQ_STATUS_NONFINITE);
   }
@@ -190,22 +220,21 @@ extern "C" int nvfp4_guidance_record(const void* x, int x_dtype, const uint8_t* 
   if (mode == NVQ_GUIDE_DIRECTION && (!x || !scales || !tensor_scale)) return NVQ_EINVAL;
   if (((uintptr_t)codes & 7u) || ((uintptr_t)bits & 1u)) return NVQ_EALIGN;
   if (mode == NVQ_GUIDE_DIRECTION && !aligned16(x)) return NVQ_EALIGN;
-  if ((n_blocks + kGuideThreads - 1) / kGuideThreads > 0x7FFFFFFF) return NVQ_ESHAPE;
+  if ((per_item + kGuideThreads - 1) / kGuideThreads > 0x7FFFFFFF || batch > 65535)
+    return NVQ_ESHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)((n_blocks + kGuideThreads - 1) / kGuideThreads));
+  const dim3 grid((unsigned)((per_item + kGuideThreads - 1) / kGuideThreads), (unsigned)batch);
   const uint2* cw = reinterpret_cast<const uint2*>(codes);
   uint16_t* b16 = reinterpret_cast<uint16_t*>(bits);
   if (mode == NVQ_GUIDE_MANTISSA)
     hipLaunchKernelGGL((k_guidance_record<NVQ_GUIDE_MANTISSA, true>), grid, dim3(kGuideThreads),
-                       0, s, x, cw, scales, tensor_scale, n_blocks, per_item, b16);
+                       0, s, x, cw, scales, tensor_scale, per_item, b16);
   else if (x_dtype == NVQ_BF16)
     hipLaunchKernelGGL((k_guidance_record<NVQ_GUIDE_DIRECTION, true>), grid,
-                       dim3(kGuideThreads), 0, s, x, cw, scales, tensor_scale, n_blocks,
-                       per_item, b16);
+                       dim3(kGuideThreads), 0, s, x, cw, scales, tensor_scale, per_item, b16);
   else
     hipLaunchKernelGGL((k_guidance_record<NVQ_GUIDE_DIRECTION, false>), grid,
-                       dim3(kGuideThreads), 0, s, x, cw, scales, tensor_scale, n_blocks,
-                       per_item, b16);
+                       dim3(kGuideThreads), 0, s, x, cw, scales, tensor_scale, per_item, b16);
   return last_launch();
 }
 
@@ -219,7 +248,8 @@ extern "C" int nvfp4_guided_quantize(const void* w, int w_dtype, int64_t batch, 
   const int64_t per_item = rows * (K / 16);
   const int64_t n_blocks = batch * per_item;
   if (n_blocks > 0 && (!w || !bits || !scales || !codes)) return NVQ_EINVAL;
-  if ((n_blocks + kGuideThreads - 1) / kGuideThreads > 0x7FFFFFFF) return NVQ_ESHAPE;
+  if ((per_item + kGuideThreads - 1) / kGuideThreads > 0x7FFFFFFF || batch > 65535)
+    return NVQ_ESHAPE;
   if (!tensor_scale) return NVQ_EINVAL;
   if (ws && !aligned256(ws)) return NVQ_EALIGN;
   if (ws && ws_bytes < kAlign) return NVQ_EWORKSPACE;
@@ -232,28 +262,28 @@ extern "C" int nvfp4_guided_quantize(const void* w, int w_dtype, int64_t batch, 
     if (rc != NVQ_OK) return rc;
   }
   if (n_blocks == 0) return NVQ_OK;
-  const dim3 grid((unsigned)((n_blocks + kGuideThreads - 1) / kGuideThreads));
+  const dim3 grid((unsigned)((per_item + kGuideThreads - 1) / kGuideThreads), (unsigned)batch);
   const uint16_t* b16 = reinterpret_cast<const uint16_t*>(bits);
   uint2* cw = reinterpret_cast<uint2*>(codes);
   const bool bf16 = w_dtype == NVQ_BF16;
   if (mode == NVQ_GUIDE_MANTISSA) {
     if (bf16)
       hipLaunchKernelGGL((k_guided_quantize<NVQ_GUIDE_MANTISSA, true>), grid,
-                         dim3(kGuideThreads), 0, s, w, b16, scales, tensor_scale, n_blocks,
-                         per_item, cw, status);
+                         dim3(kGuideThreads), 0, s, w, b16, scales, tensor_scale, per_item,
+                         cw, status);
     else
       hipLaunchKernelGGL((k_guided_quantize<NVQ_GUIDE_MANTISSA, false>), grid,
-                         dim3(kGuideThreads), 0, s, w, b16, scales, tensor_scale, n_blocks,
-                         per_item, cw, status);
+                         dim3(kGuideThreads), 0, s, w, b16, scales, tensor_scale, per_item,
+                         cw, status);
   } else {
     if (bf16)
       hipLaunchKernelGGL((k_guided_quantize<NVQ_GUIDE_DIRECTION, true>), grid,
-                         dim3(kGuideThreads), 0, s, w, b16, scales, tensor_scale, n_blocks,
-                         per_item, cw, status);
+                         dim3(kGuideThreads), 0, s, w, b16, scales, tensor_scale, per_item,
+                         cw, status);
     else
       hipLaunchKernelGGL((k_guided_quantize<NVQ_GUIDE_DIRECTION, false>), grid,
-                         dim3(kGuideThreads), 0, s, w, b16, scales, tensor_scale, n_blocks,
-                         per_item, cw, status);
+                         dim3(kGuideThreads), 0, s, w, b16, scales, tensor_scale, per_item,
+                         cw, status);
   }
   return last_launch();
 }
