@@ -310,6 +310,10 @@ class QatLeg:
         timer = lambda label, fn: timer_("qat/" + label, fn)
         F, D, W = nvq.NVQ_QAT_FWD, nvq.NVQ_QAT_DGRAD, nvq.NVQ_QAT_WGRAD
         for proj in ("gu", "dn"):
+            # rollout side: export the compact record of its weight codes
+            timer("record_" + proj, lambda proj=proj: nvq.nvfp4_guidance_record(
+                self.q[proj][0], nvq.NVQ_GUIDE_MANTISSA, out=self.rec[proj]))
+        for proj in ("gu", "dn"):
             _, sc, st = self.q[proj]
             timer("guide_" + proj, lambda proj=proj, sc=sc, st=st: nvq.nvfp4_guided_quantize(
                 self.wd[proj], self.rec[proj], sc, st, nvq.NVQ_GUIDE_MANTISSA,
@@ -349,6 +353,11 @@ class QatLeg:
         g["GBps"] = round(tot, 1)
         g["frac_hbm_peak"] = round(tot / HBM_PEAK_GBS, 4)
         g["algorithmic_bytes"] = sum(self.guide_bytes.values())
+        # record: read codes (1/2 B/elem), write bits (1/8 B/elem)
+        rb = (self.wd["gu"].numel() + self.wd["dn"].numel()) * 5 // 8
+        rms = timer.avg_ms("qat/record_gu") + timer.avg_ms("qat/record_dn")
+        g["record_ms"] = round(rms, 4)
+        g["record_GBps"] = round(rb / (rms * 1e-3) / 1e9, 1)
         out["guided_requantize"] = g
         return out
 

@@ -114,6 +114,38 @@ __global__ __launch_bounds__(kGuideThreads) void k_guidance_record(
   bits[blk] = (uint16_t)out;
 }
 
+// Mantissa bits of one 32-bit word of codes (8 nibbles) -> 8 bits.
+__device__ __forceinline__ uint32_t mantissa8(uint32_t w) {
+  uint32_t x = w & 0x11111111u;          // bit 0 of every nibble
+  x = (x | (x >> 3)) & 0x03030303u;      // two per byte, at bits 0-1
+  x = (x | (x >> 6)) & 0x000F000Fu;      // four per half word, at bits 0-3
+  return (x | (x >> 12)) & 0xFFu;
+}
+
+// Mantissa record, four blocks per thread (32 bytes of codes -> 8 bytes of
+// bits); needs only the codes, so items do not matter.  The last thread
+// takes the 1-3 blocks past the last full group.
+__global__ __launch_bounds__(kGuideThreads) void k_mantissa_record4(
+    const uint4* __restrict__ codes, int64_t n_blocks, uint2* __restrict__ bits4,
+    uint16_t* __restrict__ bits) {
+  const int64_t t = (int64_t)blockIdx.x * kGuideThreads + threadIdx.x;
+  const int64_t b0 = 4 * t;
+  if (b0 >= n_blocks) return;
+  if (b0 + 4 <= n_blocks) {
+    const uint4 a = codes[2 * t], b = codes[2 * t + 1];
+    uint2 o;
+    o.x = mantissa8(a.x) | (mantissa8(a.y) << 8) | (mantissa8(a.z) << 16) | (mantissa8(a.w) << 24);
+    o.y = mantissa8(b.x) | (mantissa8(b.y) << 8) | (mantissa8(b.z) << 16) | (mantissa8(b.w) << 24);
+    bits4[t] = o;
+  } else {
+    const uint2* c2 = reinterpret_cast<const uint2*>(codes);
+    for (int64_t blk = b0; blk < n_blocks; ++blk) {
+      const uint2 cw = c2[blk];
+      bits[blk] = (uint16_t)(mantissa8(cw.x) | (mantissa8(cw.y) << 8));
+    }
+  }
+}
+
 // ------------------------------------------------------- requantization ----
 template <int kMode, bool kBF16>
 __global__ __launch_bounds__(kGuideThreads) void k_guided_quantize(
@@ -226,7 +258,14 @@ extern "C" int nvfp4_guidance_record(const void* x, int x_dtype, const uint8_t* 
   const dim3 grid((unsigned)((per_item + kGuideThreads - 1) / kGuideThreads), (unsigned)batch);
   const uint2* cw = reinterpret_cast<const uint2*>(codes);
   uint16_t* b16 = reinterpret_cast<uint16_t*>(bits);
-  if (mode == NVQ_GUIDE_MANTISSA)
+  if (mode == NVQ_GUIDE_MANTISSA && ((uintptr_t)codes & 15u) == 0 && ((uintptr_t)bits & 7u) == 0) {
+    const int64_t nthr = (n_blocks + 3) / 4;
+    if ((nthr + kGuideThreads - 1) / kGuideThreads > 0x7FFFFFFF) return NVQ_ESHAPE;
+    hipLaunchKernelGGL(k_mantissa_record4,
+                       dim3((unsigned)((nthr + kGuideThreads - 1) / kGuideThreads)),
+                       dim3(kGuideThreads), 0, s, reinterpret_cast<const uint4*>(codes), n_blocks,
+                       reinterpret_cast<uint2*>(bits), b16);
+  } else if (mode == NVQ_GUIDE_MANTISSA)
     hipLaunchKernelGGL((k_guidance_record<NVQ_GUIDE_MANTISSA, true>), grid, dim3(kGuideThreads),
                        0, s, x, cw, scales, tensor_scale, per_item, b16);
   else if (x_dtype == NVQ_BF16)

@@ -172,7 +172,15 @@ def test_mantissa_record_needs_only_codes():
     codes, scales, st, _, _ = nvq.nvfp4_quantize(to_gpu(x))
     bits = nvq.nvfp4_guidance_record(codes, 0)
     oc, os_, ost = oracle.quantize(x)
-    assert_bits_equal(to_np(bits), oracle.guidance_record(oc, os_, ost, 0), "mantissa bits")
+    ob = oracle.guidance_record(oc, os_, ost, 0)
+    assert_bits_equal(to_np(bits), ob, "mantissa bits")
+    # a bits buffer that is only 2-byte aligned takes the one-block-per-thread kernel
+    import torch
+
+    buf = torch.zeros(bits.numel() + 2, dtype=torch.uint8, device="cuda")
+    view = buf[2:].view(bits.shape)
+    nvq.nvfp4_guidance_record(codes, 0, out=view)
+    assert_bits_equal(to_np(view), ob, "mantissa bits, 2-byte aligned output")
 
 
 def test_nonfinite_master_sets_status_and_empty_inputs():
