@@ -11,6 +11,8 @@ One step = one pass of every measured leg over its seeded synthetic workload
   qat     (when built) the asymmetric W4A16 QAT layer: codes of the drifted
           master weights rebuilt from the rollout's guidance record, then
           forward + backward.
+  kv      FP4 KV cache: K/V caches of one attention layer quantized with a
+          static tensor scale, dequantized to bf16, one decode step appended.
 
 Prints ONE JSON line.  `value` is the quantizer's algorithmic GB/s (x read
 once, codes + scales + scores written); the GEMM legs report TFLOP/s in
@@ -46,7 +48,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--legs", default="quant,moe,qat")
+    p.add_argument("--legs", default="quant,moe,qat,kv")
     p.add_argument("--no-cpu-baseline", action="store_true")
     return p.parse_args()
 
@@ -362,6 +364,59 @@ class QatLeg:
         return out
 
 
+class KvLeg:
+    """FP4 KV cache of one attention layer: quantize the K and V caches
+    (2 x [64*8*4096, 128] bf16, static tensor scale), dequantize them to bf16
+    (what attention reads), and quantize one decode step's appended rows."""
+
+    name = "kv"
+
+    def __init__(self):
+        import torch
+
+        from qat_nvfp4_quantize_amd import inputs, nvq
+
+        self.nvq = nvq
+        log("[bench] kv: generating inputs")
+        self.kv = inputs.kv_cache(device="cuda")
+        self.new = torch.from_numpy(inputs.kv_append().view(np.int16)).view(torch.bfloat16).cuda()
+        self.amax = torch.full((2,), inputs.KV_STATIC_AMAX, dtype=torch.float32, device="cuda")
+        _, rows, D = self.kv.shape
+        dev = self.kv.device
+        self.out = (torch.empty(2, rows, D // 2, dtype=torch.uint8, device=dev),
+                    torch.empty(2, rows, D // 16, dtype=torch.uint8, device=dev),
+                    torch.empty(2, dtype=torch.float32, device=dev), None)
+        self.deq = torch.empty_like(self.kv)
+        n_new = self.new.shape[1]
+        self.out_new = (torch.empty(2, n_new, D // 2, dtype=torch.uint8, device=dev),
+                        torch.empty(2, n_new, D // 16, dtype=torch.uint8, device=dev),
+                        torch.empty(2, dtype=torch.float32, device=dev), None)
+        L = nvq.load()
+        self.ws = nvq.workspace(L.nvfp4_quantize_workspace_bytes(2, rows, D), dev)
+        self.ws_new = nvq.workspace(L.nvfp4_quantize_workspace_bytes(2, n_new, D), dev)
+        n = 2 * rows * D
+        self.q_bytes = n * 2 + n // 2 + n // 16 + 8      # read bf16; write codes, scales, s_t
+        self.d_bytes = n // 2 + n // 16 + n * 2           # read codes, scales; write bf16
+
+    def step(self, timer_):
+        nvq = self.nvq
+        timer = lambda label, fn: timer_("kv/" + label, fn)
+        timer("quantize", lambda: nvq.nvfp4_quantize(self.kv, amax_in=self.amax, ws=self.ws,
+                                                     out=self.out))
+        timer("dequantize", lambda: nvq.nvfp4_dequantize(*self.out[:3], out=self.deq))
+        timer("append", lambda: nvq.nvfp4_quantize(self.new, amax_in=self.amax, ws=self.ws_new,
+                                                   out=self.out_new))
+
+    def report(self, timer):
+        q, d = timer.avg_ms("kv/quantize"), timer.avg_ms("kv/dequantize")
+        return {"quantize_ms": round(q, 4), "quantize_GBps": round(self.q_bytes / (q * 1e-3) / 1e9, 1),
+                "quantize_frac_hbm_peak": round(self.q_bytes / (q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "dequantize_ms": round(d, 4),
+                "dequantize_GBps": round(self.d_bytes / (d * 1e-3) / 1e9, 1),
+                "dequantize_frac_hbm_peak": round(self.d_bytes / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "append_ms": round(timer.avg_ms("kv/append"), 4)}
+
+
 def profiled_traffic():
     """HBM bytes per nvfp4_quantize call on the sweep, from the committed
     rocprofv3 FETCH_SIZE/WRITE_SIZE summary (copy-kernel calibrated), when the
@@ -435,6 +490,8 @@ def main():
         legs.append(MoeLeg(_inputs.PREFILL))
     if "qat" in wanted:
         legs.append(QatLeg())
+    if "kv" in wanted:
+        legs.append(KvLeg())
     timer = EventTimer()
     for _ in range(args.warmup):
         for leg in legs:
@@ -490,7 +547,7 @@ def main():
                      "traffic": profiled_traffic()},
     }
     for leg in legs:
-        if leg.name.startswith("moe") or leg.name == "qat":
+        if leg.name.startswith("moe") or leg.name in ("qat", "kv"):
             result["legs"][leg.name] = leg.report(timer)
     moe_main = [l for l in legs if l.name == "moe_prefill"] or [l for l in legs if l.name == "moe_decode"]
     if moe_main:

@@ -82,7 +82,7 @@ int nvq_device_status(const void* ws, void* stream, uint32_t* flags);
 /* NVFP4 quantization (QUADS §1, §2.1; TRACE "Fonctionnement").
  *
  * x        [batch, rows, K] of dtype x_dtype (NVQ_F32 or NVQ_BF16), 16-byte
- *          aligned; K % 16 == 0.
+ *          aligned; K % 16 == 0; 1 <= batch <= 65535.
  * amax_in  nullable device [batch] fp32: replaces amax_t = max|x| of each
  *          batch item (e.g. to requantize with a known scale).
  * codes    [batch, rows, K/2]  E2M1 codes, even element in the low nibble.
@@ -105,7 +105,11 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t rows, int6
 
 /* NVFP4 dequantization: y = sign * fl32(fl32(G * s_b) * s_t), written as fp32
  * (y_dtype NVQ_F32) or rounded to nearest-even bf16 (NVQ_BF16).  This is the
- * quantize-dequantize image both sides use for the weights (QUADS §2.1). */
+ * quantize-dequantize image both sides use for the weights (QUADS §2.1).
+ * codes [batch, rows, K/2] (8-byte aligned), scales [batch, rows, K/16],
+ * tensor_scale [batch], y [batch, rows, K] (16-byte aligned); K % 16 == 0,
+ * 1 <= batch <= 65535.  No rows: nothing is written.  Errors (NVQ_EINVAL,
+ * NVQ_ESHAPE, NVQ_EALIGN) launch nothing. */
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                      int64_t batch, int64_t rows, int64_t K, void* y, int y_dtype, void* stream);
 

@@ -478,6 +478,85 @@ __global__ __launch_bounds__(512, 2) void k_quantize(
   if (wave_or_u32(bad) && lane == 0) atomicOr(status, (uint32_t)NVQ_STATUS_NONFINITE);
 }
 
+// Score-free quantization: without residual sums there is no row order to
+// keep, so thread t of item z takes blocks t, t + T, t + 2T, ... of the item's
+// flat block list (block f = elements 16f..16f+15 of the row-major tensor,
+// codes at byte 8f, scale at byte f).  Consecutive lanes read consecutive
+// blocks whatever K is; with the row-major tile of k_quantize a K of 128
+// would leave 56 of 64 lanes idle.  One block in flight ahead, clamped to
+// the item's last block.
+constexpr int kFlatThreads = 256;
+constexpr int kFlatBlocksPerThread = 4;
+
+template <bool kBF16>
+__global__ __launch_bounds__(kFlatThreads) void k_quantize_flat(
+    const void* __restrict__ xv, int64_t nb_item, const uint32_t* __restrict__ amax_partial,
+    int n_partial, const float* __restrict__ amax_in, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tensor_scale,
+    uint32_t* __restrict__ status) {
+  constexpr int64_t kBlockBytes = 16 * (kBF16 ? 2 : 4);
+  __shared__ uint32_t s_slot[kFlatThreads * (kBF16 ? 8 : 16)];
+  __shared__ uint32_t s_wmax[kFlatThreads / kWave];
+  __shared__ float s_amax;
+  const int item = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t* slot = s_slot + threadIdx.x * (kBF16 ? 8 : 16);
+  const int64_t base = (int64_t)item * nb_item;
+  const char* xb = static_cast<const char*>(xv) + base * kBlockBytes;
+  const int64_t stride = (int64_t)gridDim.x * kFlatThreads;
+  const int64_t last = nb_item - 1;
+  int64_t f = (int64_t)blockIdx.x * kFlatThreads + threadIdx.x;
+  RowBlock<kBF16> cur;
+  cur.load_at(xb + min(f, last) * kBlockBytes);
+
+  uint32_t m = 0;
+  if (amax_in) {
+    m = __float_as_uint(amax_in[item]);
+  } else {
+    const uint32_t* p = amax_partial + (int64_t)item * n_partial;
+    for (int i = threadIdx.x; i < n_partial; i += kFlatThreads) m = max(m, p[i]);
+    m = wave_max_u32(m);
+  }
+  if (lane == 0) s_wmax[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = s_wmax[0];
+#pragma unroll
+    for (int w = 1; w < kFlatThreads / kWave; ++w) r = max(r, s_wmax[w]);
+    s_amax = __uint_as_float(r);
+  }
+  __syncthreads();
+  // s_t exactly as in k_quantize
+  const float s_t = (float)((double)s_amax / 2688.0);
+  if (blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[item] = s_t;
+  const double six_st = 6.0 * (double)s_t;
+  const bool fast = (s_t >= 0x1p-100f) && (s_t <= 0x1p100f);
+  const float g = fast ? (float)(1.0 / six_st) : 0.0f;
+  const float inv_st = fast ? (float)(1.0 / (double)s_t) : 0.0f;
+
+  float acc[16];  // no residual sums on this path
+  uint32_t bad = 0;
+  uint2* cw_out = reinterpret_cast<uint2*>(codes) + base;
+  uint8_t* sc_out = scales + base;
+#pragma unroll 1
+  while (f < nb_item) {
+    const int64_t fn = f + stride;
+    RowBlock<kBF16> nxt;
+    nxt.load_at(xb + min(fn, last) * kBlockBytes);
+    uint32_t sc;
+    uint2 cw;
+    if (fast)
+      encode_block_fast<kBF16, false>(cur, s_t, g, inv_st, sc, cw, acc, bad, slot);
+    else
+      encode_block_exact<kBF16, false>(cur, s_t, six_st, sc, cw, acc, bad, slot);
+    cw_out[f] = cw;
+    sc_out[f] = (uint8_t)sc;
+    cur = nxt;
+    f = fn;
+  }
+  if (wave_or_u32(bad) && lane == 0) atomicOr(status, (uint32_t)NVQ_STATUS_NONFINITE);
+}
+
 // score[c] = sum over chunks j ascending of P[j][c] (fp32, sequential).  One
 // column per thread, 64-thread workgroups so the columns spread over many CUs;
 // the partials of a group of 64 chunks are all loaded before the in-order sum.
@@ -785,41 +864,49 @@ __global__ __launch_bounds__(256) void k_resid_gather(const void* __restrict__ x
 }
 
 // Dequantize 8 elements (one code word) per thread.
+// y = sign * fl32(fl32(G s_b) s_t) for one 16-element block per thread: 8
+// bytes of codes and one scale in, 32 (bf16) or 64 (fp32) bytes out; the
+// item (tensor scale) comes from the grid, not a division.
 template <bool kOutBF16>
-__global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ codes,
+__global__ __launch_bounds__(256) void k_dequant(const uint2* __restrict__ codes,
                                                 const uint8_t* __restrict__ scales,
                                                 const float* __restrict__ tensor_scale,
-                                                int64_t n_words, int64_t words_per_item,
-                                                void* __restrict__ y) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n_words) return;
-  const float s_t = tensor_scale[i / words_per_item];
-  const float s_b = e4m3_to_f32(scales[i >> 1]);
-  const uint32_t w = codes[i];
-  float v[8];
+                                                int64_t blocks_per_item, void* __restrict__ y) {
+  const int64_t in_item = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (in_item >= blocks_per_item) return;
+  const int64_t blk = (int64_t)blockIdx.y * blocks_per_item + in_item;
+  const float s_t = tensor_scale[blockIdx.y];
+  const float s_b = e4m3_to_f32(scales[blk]);
+  const uint2 cw = codes[blk];
+  float v[16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float2 gg;
-    switch (j) {
-      case 0: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); gg = make_float2(t[0], t[1]); break; }
-      case 1: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); gg = make_float2(t[0], t[1]); break; }
-      case 2: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); gg = make_float2(t[0], t[1]); break; }
-      default: { auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); gg = make_float2(t[0], t[1]); break; }
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t w = h ? cw.y : cw.x;
+    float2 g[4];
+    g[0] = fp4_pair_to_f32<0>(w);
+    g[1] = fp4_pair_to_f32<1>(w);
+    g[2] = fp4_pair_to_f32<2>(w);
+    g[3] = fp4_pair_to_f32<3>(w);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * h + 2 * j] = (g[j].x * s_b) * s_t;
+      v[8 * h + 2 * j + 1] = (g[j].y * s_b) * s_t;
     }
-    v[2 * j] = (gg.x * s_b) * s_t;
-    v[2 * j + 1] = (gg.y * s_b) * s_t;
   }
   if (kOutBF16) {
-    uint4 o;
-    o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-    o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-    o.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
-    o.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
-    static_cast<uint4*>(y)[i] = o;
+    uint4* o = static_cast<uint4*>(y) + 2 * blk;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float* u = v + 8 * q;
+      o[q] = make_uint4(f32_to_bf16_rne(u[0]) | (f32_to_bf16_rne(u[1]) << 16),
+                        f32_to_bf16_rne(u[2]) | (f32_to_bf16_rne(u[3]) << 16),
+                        f32_to_bf16_rne(u[4]) | (f32_to_bf16_rne(u[5]) << 16),
+                        f32_to_bf16_rne(u[6]) | (f32_to_bf16_rne(u[7]) << 16));
+    }
   } else {
-    float4* o = static_cast<float4*>(y) + 2 * i;
-    o[0] = make_float4(v[0], v[1], v[2], v[3]);
-    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    float4* o = static_cast<float4*>(y) + 4 * blk;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
   }
 }
 
@@ -887,7 +974,7 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
                               void* stream) {
   if (!tensor_scale || !ws || (rows != 0 && (!x || !codes || !scales))) return NVQ_EINVAL;
   if (x_dtype != NVQ_F32 && x_dtype != NVQ_BF16) return NVQ_EINVAL;
-  if (batch <= 0 || rows < 0 || K <= 0 || (K & 15)) return NVQ_ESHAPE;
+  if (batch <= 0 || batch > 65535 || rows < 0 || K <= 0 || (K & 15)) return NVQ_ESHAPE;
   if (chan_score && batch != 1) return NVQ_ESHAPE;
   if (!aligned16(x) || ((uintptr_t)codes & 7u)) return NVQ_EALIGN;
   if (!aligned256(ws)) return NVQ_EALIGN;
@@ -914,9 +1001,22 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
     hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, s, L.status);
   }
   if (int rc = last_launch()) return rc;
+  const bool score = chan_score != nullptr;
+  if (!score) {
+    const int64_t nb_item = rows * (K / 16);
+    const int64_t per_wg = (int64_t)kFlatThreads * kFlatBlocksPerThread;
+    const int64_t nwg = std::min<int64_t>(std::max<int64_t>(1, (nb_item + per_wg - 1) / per_wg), 65535);
+    dim3 fgrid((unsigned)nwg, (unsigned)batch);
+    if (bf16)
+      hipLaunchKernelGGL(k_quantize_flat<true>, fgrid, dim3(kFlatThreads), 0, s, x, nb_item,
+                         L.amax_partial, L.n_partial, amax_in, codes, scales, tensor_scale, L.status);
+    else
+      hipLaunchKernelGGL(k_quantize_flat<false>, fgrid, dim3(kFlatThreads), 0, s, x, nb_item,
+                         L.amax_partial, L.n_partial, amax_in, codes, scales, tensor_scale, L.status);
+    return last_launch();
+  }
   dim3 grid((unsigned)((K / 16 + kQBlocksPerWave - 1) / kQBlocksPerWave), (unsigned)L.nchunks,
             (unsigned)batch);
-  const bool score = chan_score != nullptr;
 #define NVQ_LAUNCH_Q(B, S)                                                                    \
   hipLaunchKernelGGL((k_quantize<B, S>), grid, dim3(512), 0, s, x, rows, K, L.amax_partial, \
                      L.n_partial, amax_in, codes, scales, tensor_scale, L.chunk_partial, L.status)
@@ -938,22 +1038,20 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
 extern "C" int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
                                 const float* tensor_scale, int64_t batch, int64_t rows, int64_t K,
                                 void* y, int y_dtype, void* stream) {
-  if (!codes || !scales || !tensor_scale || !y) return NVQ_EINVAL;
   if (y_dtype != NVQ_F32 && y_dtype != NVQ_BF16) return NVQ_EINVAL;
-  if (batch <= 0 || rows < 0 || K <= 0 || (K & 15)) return NVQ_ESHAPE;
-  if (((uintptr_t)codes & 3u) || !aligned16(y)) return NVQ_EALIGN;
-  const int64_t n_words = batch * rows * K / 8;
-  if (n_words == 0) return NVQ_OK;
+  if (batch <= 0 || batch > 65535 || rows < 0 || K <= 0 || (K & 15)) return NVQ_ESHAPE;
+  const int64_t per_item = rows * (K / 16);
+  if (per_item == 0) return NVQ_OK;
+  if (!codes || !scales || !tensor_scale || !y) return NVQ_EINVAL;
+  if (((uintptr_t)codes & 7u) || !aligned16(y)) return NVQ_EALIGN;
+  if ((per_item + 255) / 256 > 0x7FFFFFFF) return NVQ_ESHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid((unsigned)((n_words + 255) / 256));
+  const dim3 grid((unsigned)((per_item + 255) / 256), (unsigned)batch);
+  const uint2* cw = reinterpret_cast<const uint2*>(codes);
   if (y_dtype == NVQ_BF16)
-    hipLaunchKernelGGL(k_dequant<true>, grid, dim3(256), 0, s,
-                       reinterpret_cast<const uint32_t*>(codes), scales, tensor_scale, n_words,
-                       rows * K / 8, y);
+    hipLaunchKernelGGL(k_dequant<true>, grid, dim3(256), 0, s, cw, scales, tensor_scale, per_item, y);
   else
-    hipLaunchKernelGGL(k_dequant<false>, grid, dim3(256), 0, s,
-                       reinterpret_cast<const uint32_t*>(codes), scales, tensor_scale, n_words,
-                       rows * K / 8, y);
+    hipLaunchKernelGGL(k_dequant<false>, grid, dim3(256), 0, s, cw, scales, tensor_scale, per_item, y);
   return last_launch();
 }
 

@@ -24,6 +24,13 @@ shapes):
              Drifted masters for the rollout-guided rounding (TRACE post): the
              bf16 master plus an independent N(0, 0.002^2) draw (a tenth of the
              weights' spread; the pages give no step size), rounded to bf16.
+  6 kv       FP4 KV cache of one attention layer (TRACE post: FP4 KV cache in
+             the rollout): K and V [B * Hkv * S, D] with B=64 sequences, Hkv=8
+             KV heads, S=4096 positions, D=128 (16-element blocks along the head
+             dimension), bf16 N(0,1), K with 2 seeded head-dim channels x10;
+             a decode step appends B * Hkv rows per tensor, N(0, 1.5^2) with 1%
+             of the elements x30.  The
+             cache keeps a static tensor scale: amax 42 = 2688 * 2^-6.
 """
 from __future__ import annotations
 
@@ -203,3 +210,41 @@ def drift_device(w, s: MoEShape, proj: str):
         d = torch.randn(w.shape[1:], generator=g, device=w.device, dtype=torch.float32)
         out[e] = (w[e].float() + d * DRIFT_STD).to(torch.bfloat16)
     return out
+
+
+KV_SHAPE = dict(B=64, Hkv=8, S=4096, D=128)
+KV_STATIC_AMAX = 42.0  # 2688 * 2^-6: tensor scale 2^-6 exactly
+_KV_K, _KV_V, _KV_OUT, _KV_NEW = range(4)
+
+
+def kv_cache(B=64, Hkv=8, S=4096, D=128, wid=6, device=None):
+    """bf16 [2, B*Hkv*S, D]: the K (item 0) and V (item 1) caches.  numpy bits
+    on the host, or a torch bf16 tensor drawn on `device` (torch Philox
+    stream seeded per workload; same recipe, another stream)."""
+    rows = B * Hkv * S
+    cols = rng(wid, _KV_OUT).permutation(D)[:2]
+    if device is None:
+        k = rng(wid, _KV_K).standard_normal((rows, D), dtype=np.float32)
+        k[:, cols] *= np.float32(10.0)
+        v = rng(wid, _KV_V).standard_normal((rows, D), dtype=np.float32)
+        return np.stack([to_bf16_bits(k), to_bf16_bits(v)])
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(BASE_SEED * 1_000_003 + wid * 1009)
+    out = torch.empty(2, rows, D, dtype=torch.bfloat16, device=device)
+    for i in range(2):
+        t = torch.randn(rows, D, generator=g, device=device, dtype=torch.float32)
+        if i == 0:
+            t[:, torch.from_numpy(cols).to(device)] *= 10.0
+        out[i] = t.to(torch.bfloat16)
+    return out
+
+
+def kv_append(B=64, Hkv=8, D=128, wid=6, step=0):
+    """bf16 bits [2, B*Hkv, D]: one decode step's new K and V rows, N(0, 1.5^2),
+    with 1% of the elements x30 (some beyond the cache's static amax)."""
+    g = rng(wid, _KV_NEW, step)
+    x = g.standard_normal((2, B * Hkv, D), dtype=np.float32) * np.float32(1.5)
+    x[g.random(x.shape) < 0.01] *= np.float32(30.0)
+    return to_bf16_bits(x)

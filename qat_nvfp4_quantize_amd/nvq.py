@@ -177,13 +177,14 @@ def nvfp4_quantize(x, amax_in=None, score=False, ws=None, out=None):
     return codes, scales, st, sc, ws
 
 
-def nvfp4_dequantize(codes, scales, tensor_scale, out_dtype=torch.float32, batch=None):
+def nvfp4_dequantize(codes, scales, tensor_scale, out_dtype=torch.float32, batch=None, out=None):
     _dev(codes, "codes")
     K = codes.shape[-1] * 2
     if batch is None:
         batch = tensor_scale.numel()
     rows = codes.numel() // (K // 2) // batch
-    y = torch.empty(*codes.shape[:-1], K, dtype=out_dtype, device=codes.device)
+    y = out if out is not None else torch.empty(*codes.shape[:-1], K, dtype=out_dtype,
+                                                device=codes.device)
     rc = load().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(tensor_scale), batch, rows, K,
                                  _ptr(y), _dtype_code(y), _stream())
     _check("nvfp4_dequantize", rc)
