@@ -333,6 +333,34 @@ class QatLeg:
         timer("wgrad_gu", lambda: call(W, *qg, self.off, s.P, x=self.x, dy=self.dy_gu, a_row=self.a_row,
                                        dw=self.dw_gu, ws=self.ws))
 
+    def symmetric(self, timer_):
+        """Ablation (outside the timed steps): symmetric W4A4 QAT, i.e. the
+        trainer's activations NVFP4-quantized too.  Forward = quantize X +
+        W4A4 grouped GEMM without compensation; weight gradient on the
+        dequantized activations."""
+        import torch
+
+        nvq, s = self.nvq, self.s
+        timer = lambda label, fn: timer_("qat_sym/" + label, fn)
+        if not hasattr(self, "sym_ws"):
+            L = nvq.load()
+            self.sym_ws = nvq.workspace(max(L.moe_gemm_workspace_bytes(s.P, s.E, 2 * s.I, 0),
+                                            L.moe_gemm_workspace_bytes(s.P, s.E, s.H, 0)), "cuda")
+            self.xhat = {"gu": torch.empty_like(self.x), "dn": torch.empty_like(self.hin)}
+        for proj, xin, y, a_row, dy, dw in (("gu", self.x, self.y_gu, self.a_row, self.dy_gu, self.dw_gu),
+                                            ("dn", self.hin, self.y_dn, None, self.dy_dn, self.dw_dn)):
+            qw = (self.gcodes[proj], *self.q[proj][1:])
+            qx = timer("quant_" + proj, lambda xin=xin: nvq.nvfp4_quantize(xin))
+            timer("fwd_" + proj, lambda qx=qx, qw=qw, y=y, a_row=a_row: nvq.moe_grouped_gemm_w4a4_comp(
+                qx[0], qx[1], qx[2], *qw, self.off, rows=s.P, a_row=a_row, ws=self.sym_ws,
+                out=(y, None)))
+            timer("dequant_" + proj, lambda qx=qx, proj=proj: nvq.nvfp4_dequantize(
+                qx[0], qx[1], qx[2], out=self.xhat[proj]))
+            timer("wgrad_" + proj, lambda qw=qw, proj=proj, a_row=a_row, dy=dy, dw=dw:
+                  nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *qw, self.off, s.P,
+                                               x=self.xhat[proj], dy=dy, a_row=a_row, dw=dw,
+                                               ws=self.ws))
+
     def report(self, timer):
         out = {}
         tot_ms, tot_f = 0.0, 0.0
@@ -361,6 +389,19 @@ class QatLeg:
         g["record_ms"] = round(rms, 4)
         g["record_GBps"] = round(rb / (rms * 1e-3) / 1e9, 1)
         out["guided_requantize"] = g
+        if "qat_sym/fwd_gu" in timer.total:
+            sym = {}
+            for proj in ("gu", "dn"):
+                f = self.flops["fwd_" + proj]
+                q = timer.avg_ms("qat_sym/quant_" + proj)
+                fw = timer.avg_ms("qat_sym/fwd_" + proj)
+                sym[proj + "_quant_ms"] = round(q, 4)
+                sym[proj + "_fwd_w4a4_k0_ms"] = round(fw, 4)
+                sym[proj + "_fwd_w4a4_k0_tflops"] = round(f / (fw * 1e-3) / 1e12, 1)
+                sym[proj + "_dequant_ms"] = round(timer.avg_ms("qat_sym/dequant_" + proj), 4)
+                sym[proj + "_wgrad_ms"] = round(timer.avg_ms("qat_sym/wgrad_" + proj), 4)
+                sym[proj + "_fwd_vs_asymmetric"] = round((q + fw) / out["fwd_" + proj + "_ms"], 3)
+            out["symmetric_w4a4_ablation"] = sym
         return out
 
 
@@ -518,6 +559,9 @@ def main():
                 leg.step(timer, comp=False)
             for _ in range(2):
                 leg.step(timer, path=_nvq.NVQ_GEMM_FP8_BLOCK)
+        if leg.name == "qat":
+            for _ in range(3):
+                leg.symmetric(timer)
     timer.collect()
 
     q = next(l for l in legs if l.name == "quant")
