@@ -140,7 +140,8 @@ class QuantLeg:
 class MoeLeg:
     """One W4A4 MoE layer with residual compensation: route, permute, quantize X
     (+ residual scores), top-k channels + residual columns, gate/up grouped GEMM
-    with SwiGLU epilogue, quantize H (+ scores), top-k + residuals, down grouped
+    with SwiGLU epilogue (which also records max |h|), quantize H with that
+    amax (+ scores), top-k + residuals, down grouped
     GEMM, combine.  Expert weights are quantized (and their channel-major copy
     made) once outside the timed step
     (they are static during a rollout)."""
@@ -182,6 +183,9 @@ class MoeLeg:
         self.qh = (torch.empty(P, I // 2, dtype=u8, device=dev), torch.empty(P, I // 16, dtype=u8, device=dev),
                    torch.empty(1, dtype=f32, device=dev), torch.empty(I, dtype=f32, device=dev))
         self.h = torch.empty(P, I, dtype=bf, device=dev)
+        # max |h|, produced by the gate/up epilogue and consumed as amax_in by
+        # the quantization of h (which then skips its own amax pass)
+        self.h_amax = torch.zeros(1, dtype=f32, device=dev)
         self.y2 = torch.empty(P, H, dtype=bf, device=dev)
         self.flops_gu = 2.0 * P * H * 2 * I
         self.flops_dn = 2.0 * P * I * H
@@ -194,7 +198,7 @@ class MoeLeg:
             a[0], a[1], a[2], codes, scales, st, self.off, rows=rows, a_row=a_row,
             a_resid=resid if comp else None, comp_idx=idx if comp else None, epilogue=epi,
             ws=self.ws_g, a_row_div=self.s.topk if a_row is not None else 0, out=out, path=path,
-            w_cm=self.wcm[proj])
+            w_cm=self.wcm[proj], h_amax=self.h_amax if epi == nvq.NVQ_EPI_SWIGLU else None)
 
     def step(self, timer_, comp=True, path=0):
         """path 0: the library's choice (exact fp16 dequantization); 2: the
@@ -210,7 +214,8 @@ class MoeLeg:
             self.x, self.qx[0], self.qx[1], self.qx[2], s.k, scores=self.qx[3], ws=self.ws_t1))
         timer("gemm_gu" + tag, lambda: self.gemm("gu", self.qx, s.P, self.sp, r1, idx1, (self.h, None),
                                                   nvq.NVQ_EPI_SWIGLU, comp, path))
-        timer("quant_h", lambda: nvq.nvfp4_quantize(self.h, score=True, ws=self.ws_q2, out=self.qh))
+        timer("quant_h", lambda: nvq.nvfp4_quantize(self.h, amax_in=self.h_amax, score=True,
+                                                    ws=self.ws_q2, out=self.qh))
         idx2, r2, _ = timer("topk_h", lambda: nvq.residual_topk_channels(
             self.h, self.qh[0], self.qh[1], self.qh[2], s.k, scores=self.qh[3], ws=self.ws_t2))
         timer("gemm_dn" + tag, lambda: self.gemm("dn", self.qh, s.P, None, r2, idx2, (self.y2, None),

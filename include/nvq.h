@@ -256,6 +256,14 @@ typedef struct nvq_moe_gemm_args {
    * contiguous rows there) instead of from every row of w_codes. */
   const uint8_t* w_codes_cm;     /* [E, K, N/2] or NULL */
   const uint8_t* w_scales_cm;    /* [E, K/16, N] or NULL */
+  /* Optional, read only when struct_size covers it: with NVQ_EPI_SWIGLU, a
+   * device fp32 word (4-byte aligned) that receives max |h| over every row
+   * the call writes, taken on the stored bf16 values (the call clears it
+   * first; 0 for no rows).  Passed as amax_in to nvfp4_quantize of h, it
+   * replaces that call's own amax pass with an identical result (a maximum
+   * does not depend on order).  NULL: not computed.  NVQ_EINVAL with another
+   * epilogue.  Calls sharing the word must be ordered on one stream. */
+  float* h_amax;
 } nvq_moe_gemm_args;
 
 /* Channel-major copy of an NVFP4 weight record (same codes and scales, other

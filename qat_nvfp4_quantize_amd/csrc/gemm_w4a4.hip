@@ -85,14 +85,18 @@ struct GemmParams {
   int n_tiles_n;
   int swiglu;             // 1: gate/up fused weight, epilogue h = silu(gate) * up
   int bm;                 // row tile of the tile table
+  uint32_t* h_amax;       // SwiGLU: max |h| over the stored bf16 h, as fp32 bits; or NULL
 };
 
 // Tile table: expert e's rows [off[e], off[e+1]) split into BM-row tiles.
+// Also clears the h amax word, ahead of the GEMM on the same stream.
 __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__ off, int E, int BM,
                                                     int32_t* __restrict__ tiles,
-                                                    int32_t* __restrict__ ntiles, int max_tiles) {
+                                                    int32_t* __restrict__ ntiles, int max_tiles,
+                                                    uint32_t* __restrict__ h_amax) {
   __shared__ int32_t s_first[1025];
   const int e = threadIdx.x;
+  if (h_amax && threadIdx.x == 0) *h_amax = 0u;
   int nt = 0;
   if (e < E) nt = (off[e + 1] - off[e] + BM - 1) / BM;
   if (e < E) s_first[e + 1] = nt;
@@ -111,6 +115,8 @@ __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__
     }
   }
 }
+
+__global__ void k_clear_word(uint32_t* w) { *w = 0u; }
 
 // Row of the A record (token) feeding sorted row pr.
 __device__ __forceinline__ int64_t a_source_row(const GemmParams& p, int64_t pr) {
@@ -449,6 +455,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c,
   } else {
     const int64_t I = N >> 1;
     const int64_t ng = (int64_t)c.nt * (BN / 2) + 32 * wave + l32;
+    uint32_t hmax = 0;  // largest |h| stored by this lane, as bf16 bits
     auto emit = [&](bool check) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -464,13 +471,21 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c,
           }
           // silu(g) u; the result is rounded to bf16, so an rcp suffices
           const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-          if (p.out_bf16) p.out_bf16[pr * I + ng] = (uint16_t)f32_to_bf16_rne(hv);
+          const uint32_t hb = f32_to_bf16_rne(hv);
+          if (p.out_bf16) p.out_bf16[pr * I + ng] = (uint16_t)hb;
+          hmax = max(hmax, hb & 0x7FFFu);
         }
     };
     if (rows_full && (int64_t)c.nt * (BN / 2) + 32 * (wave + 1) <= I)
       emit(false);
     else
       emit(true);
+    // amax of H for its quantization: bit patterns of non-negative values
+    // order as the values; one device-scope atomic per wave.
+    if (p.h_amax) {
+      const uint32_t m = wave_max_u32(hmax);
+      if (lane == 0 && m != 0u) atomicMax(p.h_amax, m << 16);
+    }
   }
 }
 
@@ -789,7 +804,13 @@ extern "C" size_t moe_gemm_workspace_bytes(int64_t rows, int64_t E, int64_t N, i
 
 extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stream) {
   if (!a || a->struct_size < offsetof(nvq_moe_gemm_args, w_codes_cm)) return NVQ_EINVAL;
-  const bool has_cm = a->struct_size >= sizeof(nvq_moe_gemm_args) && a->w_codes_cm && a->w_scales_cm;
+  const bool has_cm = a->struct_size >= offsetof(nvq_moe_gemm_args, w_scales_cm) + sizeof(void*) &&
+                      a->w_codes_cm && a->w_scales_cm;
+  uint32_t* h_amax = a->struct_size >= offsetof(nvq_moe_gemm_args, h_amax) + sizeof(void*)
+                         ? reinterpret_cast<uint32_t*>(a->h_amax)
+                         : nullptr;
+  if (h_amax && a->epilogue != NVQ_EPI_SWIGLU) return NVQ_EINVAL;
+  if (h_amax && ((uintptr_t)h_amax & 3u)) return NVQ_EALIGN;
   if (!a->expert_offsets || !a->w_codes || !a->w_scales || !a->w_tensor_scale || !a->ws) return NVQ_EINVAL;
   // the row buffers may be NULL when there are no rows
   if (a->rows != 0 && (!a->a_codes || !a->a_scales || !a->a_tensor_scale)) return NVQ_EINVAL;
@@ -810,10 +831,14 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   if (!aligned256(a->ws)) return NVQ_EALIGN;
   MoeLayout L = moe_layout(a->ws, a->rows, a->E, a->N, a->k);
   if (a->ws_bytes < L.bytes) return NVQ_EWORKSPACE;
-  if (a->rows == 0) return NVQ_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a->rows == 0) {
+    if (!h_amax) return NVQ_OK;
+    hipLaunchKernelGGL(k_clear_word, dim3(1), dim3(1), 0, s, h_amax);  // amax of no rows: 0
+    return last_launch();
+  }
   hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, a->expert_offsets, (int)a->E, BM, L.tiles,
-                     L.ntiles, L.max_tiles);
+                     L.ntiles, L.max_tiles, h_amax);
   if (int rc = last_launch()) return rc;
   GemmParams p;
   p.rows = a->rows; p.K = a->K; p.N = a->N; p.E = a->E; p.a_rows = a->a_rows;
@@ -835,6 +860,7 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   p.w_codes = a->w_codes; p.w_scales = a->w_scales; p.w_st = a->w_tensor_scale;
   p.out_bf16 = a->out_bf16; p.out_f32 = a->out_f32;
   p.tiles = L.tiles; p.ntiles = L.ntiles; p.max_tiles = L.max_tiles;
+  p.h_amax = h_amax;
   const bool swiglu = a->epilogue == NVQ_EPI_SWIGLU;
   p.swiglu = swiglu ? 1 : 0;
   p.bm = BM;

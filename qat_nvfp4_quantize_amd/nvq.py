@@ -45,7 +45,7 @@ class MoeGemmArgs(ctypes.Structure):
         ("k", _I32), ("w_codes", _P), ("w_scales", _P), ("w_tensor_scale", _P),
         ("epilogue", _I32), ("path", _I32), ("out_bf16", _P), ("out_f32", _P),
         ("ws", _P), ("ws_bytes", _SZ), ("a_row_div", _I32), ("w_codes_cm", _P),
-        ("w_scales_cm", _P),
+        ("w_scales_cm", _P), ("h_amax", _P),
     ]
 
 
@@ -308,7 +308,7 @@ def moe_grouped_gemm_w4a4_comp(a_codes, a_scales, a_tensor_scale, w_codes, w_sca
                                w_tensor_scale, expert_offsets, rows, a_row=None, a_resid=None,
                                comp_idx=None, epilogue=NVQ_EPI_NONE, path=NVQ_GEMM_AUTO,
                                want_bf16=True, want_f32=False, ws=None, a_row_div=0, out=None,
-                               w_cm=None):
+                               w_cm=None, h_amax=None):
     """Returns (out_bf16 or None, out_f32 or None).  w_cm: optional
     (codes_cm, scales_cm) from nvfp4_channel_major for the compensation gather."""
     L = load()
@@ -341,6 +341,7 @@ def moe_grouped_gemm_w4a4_comp(a_codes, a_scales, a_tensor_scale, w_codes, w_sca
     a.a_row_div = int(a_row_div)
     if w_cm is not None:
         a.w_codes_cm, a.w_scales_cm = _ptr(w_cm[0]), _ptr(w_cm[1])
+    a.h_amax = _ptr(h_amax)
     _check("moe_grouped_gemm_w4a4_comp", L.moe_grouped_gemm_w4a4_comp(ctypes.byref(a), _stream()))
     return ob, of
 

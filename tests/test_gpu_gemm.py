@@ -320,6 +320,62 @@ def test_grouped_gemm_no_rows():
     assert ob.shape == (0, N) and of.shape == (0, N)
 
 
+@pytest.mark.parametrize("path", ["deq16", "fp8_block"])
+def test_h_amax_from_the_swiglu_epilogue(path):
+    """max |h| recorded by the gate/up epilogue on a small ragged layer (both
+    paths), cleared per call, 0 without rows, refused with another epilogue,
+    and not read when the caller's struct predates the field."""
+    import ctypes
+
+    import torch
+
+    nvq = _nvq()
+    gp = nvq.NVQ_GEMM_DEQ16 if path == "deq16" else nvq.NVQ_GEMM_FP8_BLOCK
+    s = inputs.small_moe(wid=101, T=77, E=5, topk=3, k=24)
+    run = MoeRun(s, gp)
+    h_amax = torch.full((1,), 1e30, dtype=torch.float32, device="cuda")
+    h, _ = nvq.moe_grouped_gemm_w4a4_comp(
+        run.qx[0], run.qx[1], run.qx[2], run.qgu[0], run.qgu[1], run.qgu[2], run.off, rows=s.P,
+        a_row=run.a_row, a_resid=run.r1.contiguous(), comp_idx=run.idx1,
+        epilogue=nvq.NVQ_EPI_SWIGLU, path=gp, h_amax=h_amax)
+    torch.cuda.synchronize()
+    assert float(to_np(h_amax)[0]) == float(np.abs(inputs.bf16_bits_to_f32(to_np(h))).max())
+    assert float(to_np(h_amax)[0]) > 0
+    # no rows: the amax of nothing is 0
+    qa0 = nvq.nvfp4_quantize(torch.empty(0, s.H, dtype=torch.float32, device="cuda"))
+    nvq.moe_grouped_gemm_w4a4_comp(qa0[0], qa0[1], qa0[2], run.qgu[0], run.qgu[1], run.qgu[2],
+                                   to_gpu(np.zeros(s.E + 1, np.int32)), rows=0,
+                                   epilogue=nvq.NVQ_EPI_SWIGLU, h_amax=h_amax)
+    torch.cuda.synchronize()
+    assert float(to_np(h_amax)[0]) == 0.0
+    with pytest.raises(nvq.NvqError):
+        nvq.moe_grouped_gemm_w4a4_comp(run.qx[0], run.qx[1], run.qx[2], run.qgu[0], run.qgu[1],
+                                       run.qgu[2], run.off, rows=s.P, a_row=run.a_row,
+                                       epilogue=nvq.NVQ_EPI_NONE, h_amax=h_amax)
+    # a caller built against the earlier struct: the field is never read
+    L = nvq.load()
+    a = nvq.MoeGemmArgs()
+    a.struct_size = nvq.MoeGemmArgs.h_amax.offset
+    a.rows, a.K, a.N, a.E = s.P, s.H, 2 * s.I, s.E
+    a.a_rows = s.T
+    a.a_row, a.expert_offsets = ctypes.c_void_p(run.a_row.data_ptr()), ctypes.c_void_p(run.off.data_ptr())
+    a.a_codes, a.a_scales = ctypes.c_void_p(run.qx[0].data_ptr()), ctypes.c_void_p(run.qx[1].data_ptr())
+    a.a_tensor_scale = ctypes.c_void_p(run.qx[2].data_ptr())
+    a.w_codes, a.w_scales = ctypes.c_void_p(run.qgu[0].data_ptr()), ctypes.c_void_p(run.qgu[1].data_ptr())
+    a.w_tensor_scale = ctypes.c_void_p(run.qgu[2].data_ptr())
+    a.epilogue, a.path = nvq.NVQ_EPI_SWIGLU, gp
+    out = torch.empty(s.P, s.I, dtype=torch.bfloat16, device="cuda")
+    a.out_bf16 = ctypes.c_void_p(out.data_ptr())
+    ws = nvq.workspace(L.moe_gemm_workspace_bytes(s.P, s.E, 2 * s.I, 0), "cuda")
+    a.ws, a.ws_bytes = ctypes.c_void_p(ws.data_ptr()), ws.numel()
+    h_amax.fill_(7.0)
+    a.h_amax = ctypes.c_void_p(h_amax.data_ptr())
+    assert L.moe_grouped_gemm_w4a4_comp(ctypes.byref(a), ctypes.c_void_p(
+        torch.cuda.current_stream().cuda_stream)) == 0
+    torch.cuda.synchronize()
+    assert float(to_np(h_amax)[0]) == 7.0
+
+
 def _prefill_weights(nvq, s, proj):
     """The benchmark's weights: drawn on the device, quantized there, with the
     channel-major copy the benchmark passes for the compensation gather."""
@@ -372,11 +428,22 @@ def test_prefill_gate_up_full_size_sampled():
     qx = nvq.nvfp4_quantize(xg, score=True)
     idx1, r1, _ = nvq.residual_topk_channels(xg, *qx[:3], s.k, scores=qx[3])
     w, q, cm = _prefill_weights(nvq, s, "gu")
-    _, y1 = nvq.moe_grouped_gemm_w4a4_comp(qx[0], qx[1], qx[2], q[0], q[1], q[2], off, rows=s.P, a_row=sp,
+    h_amax = torch.full((1,), 123.0, dtype=torch.float32, device="cuda")  # the call clears it
+    h, y1 = nvq.moe_grouped_gemm_w4a4_comp(qx[0], qx[1], qx[2], q[0], q[1], q[2], off, rows=s.P, a_row=sp,
                                            a_resid=r1.contiguous(), comp_idx=idx1,
                                            epilogue=nvq.NVQ_EPI_SWIGLU, want_f32=True, a_row_div=s.topk,
-                                           w_cm=cm)
+                                           w_cm=cm, h_amax=h_amax)
     torch.cuda.synchronize()
+    # the epilogue's max |h| is the amax of the stored H, and quantizing H with
+    # it gives the same record as quantizing H on its own
+    hb = to_np(h)
+    assert float(to_np(h_amax)[0]) == float(np.abs(inputs.bf16_bits_to_f32(hb)).max())
+    qa = nvq.nvfp4_quantize(h, amax_in=h_amax, score=True)
+    qb = nvq.nvfp4_quantize(h, score=True)
+    torch.cuda.synchronize()
+    for u, v, what in zip(qa[:4], qb[:4], ("codes", "scales", "s_t", "scores")):
+        assert_bits_equal(to_np(u), to_np(v), "H with epilogue amax: " + what)
+    del h, hb, qa, qb
     oqx = oracle.quantize(x)
     assert_bits_equal(to_np(qx[0]), oqx[0], "X codes")
     oidx1 = oracle.topk(oracle.residual_scores(x, *oqx), s.k)
