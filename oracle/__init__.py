@@ -83,6 +83,8 @@ def lib():
             L.orc_moe_gemm_w4a4.argtypes = [_P, _P, _F, _P, ctypes.c_int, _I64, _P, _I64, _P, _P,
                                             _P, _I64, _P, _P, _I64, _P, _I64, _P]
             L.orc_swiglu_bf16.argtypes = [_P, _I64, _I64, _P]
+            L.orc_swiglu_backward.argtypes = [_P, ctypes.c_int, _I64, _I64, _P, _P]
+            L.orc_combine_backward.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]
             L.orc_combine_bf16.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
             L.orc_qat_fwd.argtypes = [_P, _I64, _P, _P, _I64, _I64, _P, _P, _P, _I64, _P, _I64, _P]
             L.orc_qat_dgrad.argtypes = [_P, _I64, _P, _P, _I64, _I64, _P, _P, _P, _I64, _P, _I64, _P]
@@ -281,6 +283,31 @@ def swiglu_bf16(y):
     h = np.empty((rows, two_i // 2), np.uint16)
     lib().orc_swiglu_bf16(_ptr(y), rows, two_i // 2, _ptr(h))
     return h
+
+
+def swiglu_backward(y1, dh_bf16):
+    """fp64 [rows, 2I] gradient of h = silu(g) u with respect to (g, u), given
+    the pre-activation y1 [rows, 2I] (fp32, or bf16 as uint16) and dh (bf16)."""
+    ya, dt = _as_input(y1)
+    rows, two_i = ya.shape
+    dh = _c(dh_bf16, np.uint16)
+    out = np.empty((rows, two_i), np.float64)
+    lib().orc_swiglu_backward(_ptr(ya), dt, rows, two_i // 2, _ptr(dh), _ptr(out))
+    return out
+
+
+def combine_backward(dout_bf16, y_bf16, pos, w):
+    """(dy bf16 [P, N], dw fp64 [T, topk]) of out = sum_j w y[pos]."""
+    dout = _c(dout_bf16, np.uint16)
+    y = _c(y_bf16, np.uint16)
+    w = _c(w, np.float32)
+    T, topk_ = w.shape
+    N = dout.shape[1]
+    dy = np.zeros((y.shape[0], N), np.uint16)
+    dw = np.empty((T, topk_), np.float64)
+    lib().orc_combine_backward(_ptr(dout), _ptr(y), _ptr(_c(pos, np.int32)), _ptr(w), T, topk_, N,
+                               _ptr(dy), _ptr(dw))
+    return dy, dw
 
 
 def combine_bf16(y, pos, w):

@@ -585,6 +585,56 @@ void orc_combine_bf16(const float* y, const int32_t* pos, const float* w, int64_
   });
 }
 
+// Backward of the MoE layer's glue for the chained QAT backward (the
+// straight-through GEMMs are the QAT functions below).
+//
+// SwiGLU backward.  h = silu(g) u with silu(g) = g s, s = 1 / (1 + exp(-g)),
+// so dh/dg = u s (1 + g (1 - s)) and dh/du = g s.  y1 [rows, 2I] holds the
+// gate pre-activation in columns [0, I) and the up one in [I, 2I) (dtype 0 =
+// fp32, 1 = bf16); dh bf16 [rows, I]; dy1 [rows, 2I] fp64 = (dh dh/dg, dh dh/du).
+void orc_swiglu_backward(const void* y1, int dtype, int64_t rows, int64_t I, const uint16_t* dh,
+                         double* dy1) {
+  parallel_for(rows, [&](int64_t r) {
+    for (int64_t i = 0; i < I; ++i) {
+      const double g = load_elem(y1, dtype, r, 2 * I, i);
+      const double u = load_elem(y1, dtype, r, 2 * I, I + i);
+      const double d = bf16_bits_to_float(dh[r * I + i]);
+      const double sg = 1.0 / (1.0 + std::exp(-g));
+      dy1[r * 2 * I + i] = d * u * sg * (1.0 + g * (1.0 - sg));
+      dy1[r * 2 * I + I + i] = d * g * sg;
+    }
+  });
+}
+
+// Combine backward.  out[t] = sum_j w[t,j] y[pos[t,j]] gives
+//   dy[pos[t,j], n] = bf16(fl32(w[t,j] dout[t,n]))   (the gradient the down
+//                     projection's bf16 backward consumes; the fp32 product of
+//                     a 24-bit and an 8-bit significand is exact in fp64, so
+//                     rounding it to fp32 is fl32 of the real product)
+//   dw[t,j]         = sum_n dout[t,n] y[pos[t,j], n]   (fp64; the routing
+//                     weights' gradient).
+// dout bf16 [T, N], y bf16 [P, N] (sorted-pair order), pos [T*topk].  Pairs
+// with pos < 0 are skipped (dw = 0).  dw may be NULL.
+void orc_combine_backward(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
+                          const float* w, int64_t T, int64_t topk, int64_t N, uint16_t* dy,
+                          double* dw) {
+  parallel_for(T, [&](int64_t t) {
+    for (int64_t j = 0; j < topk; ++j) {
+      const int64_t p = pos[t * topk + j];
+      if (dw) dw[t * topk + j] = 0.0;
+      if (p < 0) continue;
+      const double wj = w[t * topk + j];
+      double acc = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        const double d = bf16_bits_to_float(dout[t * N + n]);
+        dy[p * N + n] = float_to_bf16_rne((float)(wj * d));
+        acc += d * (double)bf16_bits_to_float(y[p * N + n]);
+      }
+      if (dw) dw[t * topk + j] = acc;
+    }
+  });
+}
+
 // Asymmetric W4A16 QAT forward (QUADS explainer §2.2-A; TRACE post: the
 // trainer takes its rounding from the rollout's recorded codes and scales):
 //   Y[s, n] = sum_c a[a_row[s], c] * W^_e[n, c],   e = row_expert[s],
