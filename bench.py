@@ -274,8 +274,9 @@ class QatLeg:
         s = self.s = inputs.QAT
         dev = torch.device("cuda")
         log("[bench] qat: generating inputs")
-        ids, _ = nvq.nvq_moe_route(torch.from_numpy(inputs.logits(s)).to(dev), s.topk)
-        self.sp, self.off, _, _ = nvq.nvq_moe_permute(ids, s.E)
+        ids, self.w = nvq.nvq_moe_route(torch.from_numpy(inputs.logits(s)).to(dev), s.topk)
+        self.sp, self.off, self.pos, _ = nvq.nvq_moe_permute(ids, s.E)
+        self.ones = torch.ones_like(self.w)
         self.a_row = (self.sp // s.topk).to(torch.int32).contiguous()
         g = torch.Generator(device=dev)
         g.manual_seed(5)
@@ -284,6 +285,10 @@ class QatLeg:
         self.hin = torch.randn(s.P, s.I, generator=g, device=dev).to(bf)
         self.dy_gu = torch.randn(s.P, 2 * s.I, generator=g, device=dev).to(bf)
         self.dy_dn = torch.randn(s.P, s.H, generator=g, device=dev).to(bf)
+        self.dout = torch.randn(s.T, s.H, generator=g, device=dev).to(bf)  # gradient of the layer output
+        self.out = torch.empty(s.T, s.H, dtype=bf, device=dev)
+        self.dx_tok = torch.empty(s.T, s.H, dtype=bf, device=dev)
+        self.dw_route = torch.empty(s.T, s.topk, dtype=torch.float32, device=dev)
         # The rollout's record of each projection (codes, scales, s_t) and its
         # compact guidance record (mantissa bits); the trainer's masters have
         # drifted since, and each step rebuilds their codes from the record.
@@ -328,15 +333,23 @@ class QatLeg:
         qg = (self.gcodes["gu"], *self.q["gu"][1:])
         qd = (self.gcodes["dn"], *self.q["dn"][1:])
         call = nvq.qat_fakequant_gemm_w4a16
+        # forward through the layer
         timer("fwd_gu", lambda: call(F, *qg, self.off, s.P, x=self.x, a_row=self.a_row, ws=self.ws,
                                      out=(self.y_gu, None)))
+        timer("swiglu_fwd", lambda: nvq.nvq_swiglu_forward(self.y_gu, out=self.hin))
         timer("fwd_dn", lambda: call(F, *qd, self.off, s.P, x=self.hin, ws=self.ws, out=(self.y_dn, None)))
+        timer("combine", lambda: nvq.nvq_moe_combine(self.y_dn, self.pos, self.w, out=self.out))
+        # chained backward from the output gradient (identity straight-through)
+        timer("combine_bwd", lambda: nvq.nvq_moe_combine_backward(
+            self.dout, self.pos, self.w, s.P, y=self.y_dn, out=(self.dy_dn, self.dw_route)))
         timer("dgrad_dn", lambda: call(D, *qd, self.off, s.P, dy=self.dy_dn, ws=self.ws, out=(self.dh, None)))
         timer("wgrad_dn", lambda: call(W, *qd, self.off, s.P, x=self.hin, dy=self.dy_dn, dw=self.dw_dn,
                                        ws=self.ws))
+        timer("swiglu_bwd", lambda: nvq.nvq_swiglu_backward(self.y_gu, self.dh, out=self.dy_gu))
         timer("dgrad_gu", lambda: call(D, *qg, self.off, s.P, dy=self.dy_gu, ws=self.ws, out=(self.dx, None)))
         timer("wgrad_gu", lambda: call(W, *qg, self.off, s.P, x=self.x, dy=self.dy_gu, a_row=self.a_row,
                                        dw=self.dw_gu, ws=self.ws))
+        timer("token_sum", lambda: nvq.nvq_moe_combine(self.dx, self.pos, self.ones, out=self.dx_tok))
 
     def symmetric(self, timer_):
         """Ablation (outside the timed steps): symmetric W4A4 QAT, i.e. the
@@ -377,6 +390,10 @@ class QatLeg:
             tot_f += f
         out["total_ms"] = round(tot_ms, 4)
         out["tflops"] = round(tot_f / (tot_ms * 1e-3) / 1e12, 1)
+        glue = {k: round(timer.avg_ms("qat/" + k), 4)
+                for k in ("swiglu_fwd", "combine", "combine_bwd", "swiglu_bwd", "token_sum")}
+        out["glue_ms"] = glue
+        out["layer_ms"] = round(tot_ms + sum(glue.values()), 4)
         out["frac_bf16_mfma_peak"] = round(out["tflops"] / BF16_PEAK_TFLOPS, 4)
         out["algorithmic_tflop"] = round(tot_f / 1e12, 3)
         g = {}

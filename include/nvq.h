@@ -208,6 +208,40 @@ int nvq_moe_combine(const uint16_t* y, const int32_t* pos, const float* weights,
                     int64_t topk, int64_t N, uint16_t* out, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Chained backward of the MoE layer's glue (QUADS §2.2-A: the trainer's
+ * backward with the identity straight-through estimator runs through the
+ * layer's SwiGLU and expert combine; its GEMMs are qat_fakequant_gemm_w4a16).
+ * All tensors bf16 unless stated, row-major, 16-byte aligned device pointers,
+ * caller-owned; asynchronous on stream; errors (NVQ_EINVAL, NVQ_ESHAPE,
+ * NVQ_EALIGN) launch nothing.  Zero rows (tokens) do nothing. */
+
+/* h [rows, I] = bf16(silu(g) u) with g = y1[:, :I], u = y1[:, I:], y1
+ * [rows, 2I] of dtype y1_dtype (NVQ_F32 or NVQ_BF16), silu(g) = g / (1 +
+ * exp(-g)), evaluated in fp32 with the hardware exp and reciprocal (the
+ * result is rounded to bf16).  I % 8 == 0. */
+int nvq_swiglu_forward(const void* y1, int y1_dtype, int64_t rows, int64_t I, uint16_t* h,
+                       void* stream);
+
+/* dy1 [rows, 2I] = (dh u s (1 + g (1 - s)), dh g s), s = 1 / (1 + exp(-g)):
+ * the gradient of h = silu(g) u with respect to the gate and up
+ * pre-activations y1 (layout and dtype as above), given dh [rows, I].  fp32
+ * arithmetic, bf16 result.  I % 8 == 0. */
+int nvq_swiglu_backward(const void* y1, int y1_dtype, const uint16_t* dh, int64_t rows, int64_t I,
+                        uint16_t* dy1, void* stream);
+
+/* Backward of nvq_moe_combine (out[t] = sum_j w[t,j] y[pos[t,j]]):
+ *   dy[pos[t,j], :] = bf16(fl32(w[t,j] dout[t, :]))   dy [P, N] sorted-pair order
+ *   dw[t, j]       = sum_n dout[t,n] y[pos[t,j], n]   fp32 (nullable; y is read
+ *                    only for it)
+ * dout [T, N]; pos [T, topk] the permutation's inverse map (pairs with pos < 0
+ * are skipped, their dw is 0); weights [T, topk] fp32.  N % 8 == 0.  The token
+ * gradient of the gate/up input, sum_j dx_pairs[pos[t,j]], is nvq_moe_combine
+ * with unit weights. */
+int nvq_moe_combine_backward(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
+                             const float* weights, int64_t T, int64_t topk, int64_t N,
+                             uint16_t* dy, float* dw, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* W4A4 MoE grouped GEMM with residual compensation (QUADS §1, §2.2-B).
  *
  * For every sorted row p of expert e (off[e] <= p < off[e+1]) and t = a_row[p]:

@@ -228,6 +228,126 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
   reinterpret_cast<uint4*>(out + t * N)[v] = o;
 }
 
+// ------------------------------------------------ chained backward glue --
+// Eight consecutive columns of a [rows, ld] tensor of bf16 or fp32 as fp32.
+template <bool kF32>
+__device__ __forceinline__ void load8(const void* base, int64_t off, float (&v)[8]) {
+  if (kF32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      v[2 * h] = bf16_lo(w[h]);
+      v[2 * h + 1] = bf16_hi(w[h]);
+    }
+  }
+}
+
+__device__ __forceinline__ uint4 pack8_bf16(const float (&v)[8]) {
+  return make_uint4(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                    f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16),
+                    f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16),
+                    f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16));
+}
+
+// h = bf16(silu(g) u), gate in columns [0, I) and up in [I, 2I) of y1.  The
+// result is rounded to bf16, so the hardware exp and reciprocal suffice.
+template <bool kF32>
+__global__ __launch_bounds__(256) void k_swiglu_fwd(const void* __restrict__ y1, int64_t rows,
+                                                   int64_t I, uint16_t* __restrict__ h) {
+  const int64_t nvec = I / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * nvec) return;
+  const int64_t r = i / nvec, c = (i - r * nvec) * 8;
+  float g[8], u[8], o[8];
+  load8<kF32>(y1, r * 2 * I + c, g);
+  load8<kF32>(y1, r * 2 * I + I + c, u);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = g[k] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[k])) * u[k];
+  *reinterpret_cast<uint4*>(h + r * I + c) = pack8_bf16(o);
+}
+
+// (dg, du) = dh (u s (1 + g (1 - s)), g s) with s = 1 / (1 + exp(-g)),
+// written as bf16 [rows, 2I] in the layout of y1.  Very negative g gives
+// exp(-g) = inf and s = 0: both gradients 0.
+template <bool kF32>
+__global__ __launch_bounds__(256) void k_swiglu_bwd(const void* __restrict__ y1,
+                                                   const uint16_t* __restrict__ dh, int64_t rows,
+                                                   int64_t I, uint16_t* __restrict__ dy1) {
+  const int64_t nvec = I / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * nvec) return;
+  const int64_t r = i / nvec, c = (i - r * nvec) * 8;
+  float g[8], u[8], d[8], dg[8], du[8];
+  load8<kF32>(y1, r * 2 * I + c, g);
+  load8<kF32>(y1, r * 2 * I + I + c, u);
+  load8<false>(dh, r * I + c, d);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[k]));
+    const float ds = d[k] * sg;
+    dg[k] = ds * u[k] * (1.0f + g[k] * (1.0f - sg));
+    du[k] = ds * g[k];
+  }
+  *reinterpret_cast<uint4*>(dy1 + r * 2 * I + c) = pack8_bf16(dg);
+  *reinterpret_cast<uint4*>(dy1 + r * 2 * I + I + c) = pack8_bf16(du);
+}
+
+// One workgroup per token t: for each of its pairs j (p = pos[t, j] >= 0)
+//   dy[p, :] = bf16(fl32(w[t, j] dout[t, :]))
+//   dw[t, j] = sum_n dout[t, n] y[p, n]   (fp32; lanes stride the columns,
+//              then a wave tree and the four wave sums in order)
+constexpr int kCbThreads = 256;
+__global__ __launch_bounds__(kCbThreads) void k_combine_bwd(
+    const uint16_t* __restrict__ dout, const uint16_t* __restrict__ y,
+    const int32_t* __restrict__ pos, const float* __restrict__ w, int topk, int64_t N,
+    uint16_t* __restrict__ dy, float* __restrict__ dw) {
+  __shared__ float s_part[kCbThreads / kWave];
+  const int64_t t = blockIdx.x;
+  const int64_t nvec = N / 8;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int j = 0; j < topk; ++j) {
+    const int32_t p = pos[t * topk + j];  // uniform over the workgroup
+    if (p < 0) {
+      if (dw && threadIdx.x == 0) dw[t * topk + j] = 0.0f;
+      continue;
+    }
+    const float wj = w[t * topk + j];
+    float acc = 0.0f;
+    for (int64_t v = threadIdx.x; v < nvec; v += kCbThreads) {
+      float d[8], o[8];
+      load8<false>(dout, t * N + 8 * v, d);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = wj * d[k];
+      *reinterpret_cast<uint4*>(dy + (int64_t)p * N + 8 * v) = pack8_bf16(o);
+      if (dw) {
+        float yv[8];
+        load8<false>(y, (int64_t)p * N + 8 * v, yv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc += d[k] * yv[k];
+      }
+    }
+    if (dw) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+      if (lane == 0) s_part[wave] = acc;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float sum = s_part[0];
+#pragma unroll
+        for (int q = 1; q < kCbThreads / kWave; ++q) sum += s_part[q];
+        dw[t * topk + j] = sum;
+      }
+      __syncthreads();
+    }
+  }
+}
+
 }  // namespace
 }  // namespace nvq
 
@@ -293,5 +413,54 @@ extern "C" int nvq_moe_combine(const uint16_t* y, const int32_t* pos, const floa
   if (n == 0) return NVQ_OK;
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), y, pos, weights, T, (int)topk, N, out);
+  return last_launch();
+}
+
+extern "C" int nvq_swiglu_forward(const void* y1, int y1_dtype, int64_t rows, int64_t I,
+                                  uint16_t* h, void* stream) {
+  if (y1_dtype != NVQ_F32 && y1_dtype != NVQ_BF16) return NVQ_EINVAL;
+  if (rows < 0 || I <= 0 || (I & 7)) return NVQ_ESHAPE;
+  const int64_t n = rows * (I / 8);
+  if (n == 0) return NVQ_OK;
+  if (!y1 || !h) return NVQ_EINVAL;
+  if (!aligned16(y1) || !aligned16(h)) return NVQ_EALIGN;
+  if ((n + 255) / 256 > 0x7FFFFFFF) return NVQ_ESHAPE;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (y1_dtype == NVQ_F32)
+    hipLaunchKernelGGL(k_swiglu_fwd<true>, grid, dim3(256), 0, s, y1, rows, I, h);
+  else
+    hipLaunchKernelGGL(k_swiglu_fwd<false>, grid, dim3(256), 0, s, y1, rows, I, h);
+  return last_launch();
+}
+
+extern "C" int nvq_swiglu_backward(const void* y1, int y1_dtype, const uint16_t* dh, int64_t rows,
+                                   int64_t I, uint16_t* dy1, void* stream) {
+  if (y1_dtype != NVQ_F32 && y1_dtype != NVQ_BF16) return NVQ_EINVAL;
+  if (rows < 0 || I <= 0 || (I & 7)) return NVQ_ESHAPE;
+  const int64_t n = rows * (I / 8);
+  if (n == 0) return NVQ_OK;
+  if (!y1 || !dh || !dy1) return NVQ_EINVAL;
+  if (!aligned16(y1) || !aligned16(dh) || !aligned16(dy1)) return NVQ_EALIGN;
+  if ((n + 255) / 256 > 0x7FFFFFFF) return NVQ_ESHAPE;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (y1_dtype == NVQ_F32)
+    hipLaunchKernelGGL(k_swiglu_bwd<true>, grid, dim3(256), 0, s, y1, dh, rows, I, dy1);
+  else
+    hipLaunchKernelGGL(k_swiglu_bwd<false>, grid, dim3(256), 0, s, y1, dh, rows, I, dy1);
+  return last_launch();
+}
+
+extern "C" int nvq_moe_combine_backward(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
+                                        const float* weights, int64_t T, int64_t topk, int64_t N,
+                                        uint16_t* dy, float* dw, void* stream) {
+  if (T < 0 || topk < 1 || N <= 0 || (N & 7)) return NVQ_ESHAPE;
+  if (T == 0) return NVQ_OK;
+  if (!dout || !pos || !weights || !dy || (dw && !y)) return NVQ_EINVAL;
+  if (!aligned16(dout) || !aligned16(dy) || (dw && !aligned16(y))) return NVQ_EALIGN;
+  if (T > 0x7FFFFFFF) return NVQ_ESHAPE;
+  hipLaunchKernelGGL(k_combine_bwd, dim3((unsigned)T), dim3(kCbThreads), 0,
+                     static_cast<hipStream_t>(stream), dout, y, pos, weights, (int)topk, N, dy, dw);
   return last_launch();
 }

@@ -77,6 +77,9 @@ _SIGS = [
     ("nvq_moe_permute_workspace_bytes", _SZ, [_I64, _I64, _I64]),
     ("nvq_moe_permute", ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     ("nvq_moe_combine", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    ("nvq_swiglu_forward", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _P, _P]),
+    ("nvq_swiglu_backward", ctypes.c_int, [_P, ctypes.c_int, _P, _I64, _I64, _P, _P]),
+    ("nvq_moe_combine_backward", ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P]),
     ("nvfp4_channel_major", ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P]),
     ("moe_gemm_workspace_bytes", _SZ, [_I64, _I64, _I64, _I32]),
     ("moe_grouped_gemm_w4a4_comp", ctypes.c_int, [ctypes.POINTER(MoeGemmArgs), _P]),
@@ -275,14 +278,53 @@ def nvq_moe_permute(ids, E, ws=None):
     return sp, off, pos, ws
 
 
-def nvq_moe_combine(y, pos, weights):
+def nvq_moe_combine(y, pos, weights, out=None):
     _dev(y, "y")
     T, topk = weights.shape
     N = y.shape[1]
-    out = torch.empty(T, N, dtype=torch.bfloat16, device=y.device)
+    if out is None:
+        out = torch.empty(T, N, dtype=torch.bfloat16, device=y.device)
     _check("nvq_moe_combine", load().nvq_moe_combine(_ptr(y), _ptr(pos), _ptr(weights), T, topk,
                                                      N, _ptr(out), _stream()))
     return out
+
+
+def nvq_swiglu_forward(y1, out=None):
+    """h bf16 [rows, I] = silu(y1[:, :I]) * y1[:, I:] (y1 fp32 or bf16 [rows, 2I])."""
+    _dev(y1, "y1")
+    rows, two_i = y1.shape
+    h = out if out is not None else torch.empty(rows, two_i // 2, dtype=torch.bfloat16,
+                                                device=y1.device)
+    _check("nvq_swiglu_forward", load().nvq_swiglu_forward(_ptr(y1), _dtype_code(y1), rows,
+                                                           two_i // 2, _ptr(h), _stream()))
+    return h
+
+
+def nvq_swiglu_backward(y1, dh, out=None):
+    """dy1 bf16 [rows, 2I]: gradient of h = silu(g) u w.r.t. (g, u) given dh."""
+    _dev(y1, "y1")
+    _dev(dh, "dh")
+    rows, two_i = y1.shape
+    dy1 = out if out is not None else torch.empty(rows, two_i, dtype=torch.bfloat16,
+                                                  device=y1.device)
+    _check("nvq_swiglu_backward", load().nvq_swiglu_backward(
+        _ptr(y1), _dtype_code(y1), _ptr(dh), rows, two_i // 2, _ptr(dy1), _stream()))
+    return dy1
+
+
+def nvq_moe_combine_backward(dout, pos, weights, rows, y=None, want_dw=True, out=None):
+    """(dy bf16 [rows, N] in sorted-pair order, dw fp32 [T, topk] or None)."""
+    _dev(dout, "dout")
+    T, N = dout.shape
+    topk = weights.shape[1]
+    if out is not None:
+        dy, dw = out
+    else:
+        dy = torch.empty(rows, N, dtype=torch.bfloat16, device=dout.device)
+        dw = torch.empty(T, topk, dtype=torch.float32, device=dout.device) if want_dw else None
+    _check("nvq_moe_combine_backward", load().nvq_moe_combine_backward(
+        _ptr(dout), _ptr(y), _ptr(pos), _ptr(weights), T, topk, N, _ptr(dy), _ptr(dw), _stream()))
+    return dy, dw
 
 
 # ------------------------------------------------------------------- GEMMs --
