@@ -29,6 +29,7 @@
 #include "nvq.h"
 #include "nvq_device.h"
 #include "nvq_internal.h"
+#include "nvq_scan.h"
 
 namespace nvq {
 namespace {
@@ -69,20 +70,13 @@ __global__ __launch_bounds__(1024) void k_qat_tile_table(const int32_t* __restri
                                                         int32_t* __restrict__ tiles,
                                                         int32_t* __restrict__ ntiles, int max_tiles,
                                                         int bm) {
-  __shared__ int32_t s_first[1025];
+  __shared__ int32_t s_wave[16];
   const int e = threadIdx.x;
-  int nt = 0;
-  if (e < E) nt = (off[e + 1] - off[e] + bm - 1) / bm;
-  if (e < E) s_first[e + 1] = nt;
-  if (threadIdx.x == 0) s_first[0] = 0;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int i = 1; i <= E; ++i) s_first[i] += s_first[i - 1];
-    *ntiles = min(s_first[E], max_tiles);
-  }
-  __syncthreads();
+  const int nt = e < E ? (off[e + 1] - off[e] + bm - 1) / bm : 0;
+  const int incl = block_inclusive_scan(nt, s_wave);
+  if (e == E - 1) *ntiles = min(incl, max_tiles);
   if (e < E) {
-    const int base = s_first[e];
+    const int base = incl - nt;
     for (int t = 0; t < nt && base + t < max_tiles; ++t) {
       tiles[2 * (base + t)] = e;
       tiles[2 * (base + t) + 1] = off[e] + t * bm;
