@@ -480,3 +480,32 @@ def test_prefill_down_full_size_sampled():
     rows = _sample_rows(ooff, every=1499)
     row_e = np.searchsorted(ooff, rows, side="right") - 1
     _check_sampled(nvq, s, to_np(y2)[rows], rows, rows.astype(np.int32), row_e, oqh, hb, oidx2, w, q, "down")
+
+
+def test_decode_down_full_size_sampled():
+    """Full-size decode down projection (K=768, N=2048, k=64, P=32768 rows) in
+    the benchmark's launch configuration (channel-major record for the
+    compensation), on an independently drawn H of the layer's shape: H's
+    record and channels bit-exact, then sampled rows."""
+    import torch
+
+    nvq = _nvq()
+    s = inputs.DECODE
+    oids, _ = oracle.route(inputs.logits(s), s.topk)
+    _, ooff, _ = oracle.permute(oids, s.E)
+    hb = inputs.hidden(s)
+    hg = to_gpu(hb)
+    qh = nvq.nvfp4_quantize(hg, score=True)
+    idx2, r2, _ = nvq.residual_topk_channels(hg, *qh[:3], s.k, scores=qh[3])
+    w, q, cm = _prefill_weights(nvq, s, "dn")
+    _, y2 = nvq.moe_grouped_gemm_w4a4_comp(qh[0], qh[1], qh[2], q[0], q[1], q[2], to_gpu(ooff), rows=s.P,
+                                           a_resid=r2.contiguous(), comp_idx=idx2, want_f32=True, w_cm=cm)
+    torch.cuda.synchronize()
+    oqh = oracle.quantize(hb)
+    assert_bits_equal(to_np(qh[0]), oqh[0], "H codes")
+    oidx2 = oracle.topk(oracle.residual_scores(hb, *oqh), s.k)
+    assert_bits_equal(to_np(idx2), oidx2, "H channels")
+    rows = _sample_rows(ooff, every=173)
+    row_e = np.searchsorted(ooff, rows, side="right") - 1
+    _check_sampled(nvq, s, to_np(y2)[rows], rows, rows.astype(np.int32), row_e, oqh, hb, oidx2, w, q,
+                   "decode down")

@@ -188,3 +188,38 @@ def test_chained_layer_backward_small():
     e2e = np.abs(_f(to_np(dxt)) - _f(dx)).max() / max(np.abs(_f(dx)).max(), 1e-30)
     log(f"[chain] GPU chain end to end: dX max |err| / max |dX| = {e2e:.3e}")
     assert e2e < 0.1
+
+
+def test_glue_at_the_qat_layer_size_sampled():
+    """SwiGLU forward/backward and the combine backward at the trainer layer's
+    size (P = 131072 pairs, I = 1536, H = 4096) in the benchmark's launch
+    configuration, checked on sampled rows and tokens."""
+    import torch
+
+    nvq = _nvq()
+    s = inputs.QAT
+    oids, ow, osp, ooff, opos = _route(s)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    y1 = (torch.randn(s.P, 2 * s.I, generator=g, device="cuda") * 2).to(torch.bfloat16)
+    dh = torch.randn(s.P, s.I, generator=g, device="cuda").to(torch.bfloat16)
+    y2 = torch.randn(s.P, s.H, generator=g, device="cuda").to(torch.bfloat16)
+    dout = torch.randn(s.T, s.H, generator=g, device="cuda").to(torch.bfloat16)
+    h = nvq.nvq_swiglu_forward(y1)
+    dy1 = nvq.nvq_swiglu_backward(y1, dh)
+    dy2, dw = nvq.nvq_moe_combine_backward(dout, to_gpu(opos), to_gpu(ow), s.P, y=y2)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, s.P, 1009), [s.P - 1]]))
+    y1r, dhr = to_np(y1)[rows], to_np(dh)[rows]
+    np.testing.assert_allclose(_f(to_np(h)[rows]), _f(oracle.swiglu_bf16(_f(y1r))), rtol=2 ** -7,
+                               atol=1e-30)
+    _check_swiglu_bwd(to_np(dy1)[rows], oracle.swiglu_backward(y1r, dhr), _f(y1r), dhr, "QAT-size")
+    toks = np.unique(np.concatenate([np.arange(0, s.T, 331), [s.T - 1]]))
+    pos2 = opos.reshape(s.T, s.topk)[toks]
+    sub_pos = np.arange(toks.size * s.topk, dtype=np.int32)
+    y2s = to_np(y2)[pos2.ravel()]
+    rdy, rdw = oracle.combine_backward(to_np(dout)[toks], y2s, sub_pos, ow[toks])
+    assert_bits_equal(to_np(dy2)[pos2.ravel()], rdy, "QAT-size dY2")
+    D, Y = _f(to_np(dout)[toks]), _f(y2s).reshape(toks.size, s.topk, s.H)
+    den = np.linalg.norm(D, axis=1)[:, None] * np.linalg.norm(Y, axis=2)
+    assert (np.abs(to_np(dw)[toks] - rdw) / np.maximum(den, 1e-30)).max() <= TOL
