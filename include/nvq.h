@@ -203,7 +203,8 @@ int nvq_moe_permute(const int32_t* ids, int64_t T, int64_t topk, int64_t E,
                     size_t ws_bytes, void* stream);
 
 /* out[t, n] = bf16( sum_j w[t, j] * y[pos[t*topk + j], n] ), j ascending, fp32
- * accumulation.  y [P, N] bf16 in sorted-pair order. */
+ * accumulation.  y [P, N] bf16 in sorted-pair order; a pair the permutation
+ * dropped (pos < 0) is left out of the sum.  N % 8 == 0. */
 int nvq_moe_combine(const uint16_t* y, const int32_t* pos, const float* weights, int64_t T,
                     int64_t topk, int64_t N, uint16_t* out, void* stream);
 

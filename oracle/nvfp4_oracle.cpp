@@ -572,14 +572,18 @@ void orc_swiglu_bf16(const double* y, int64_t rows, int64_t I, uint16_t* h) {
 }
 
 // Combine: out[t, n] = bf16( sum_j w[t,j] * Y[pos[t*topk+j], n] ), j ascending,
-// fp64.  Y is fp32 [P, N] in sorted-pair order.
+// fp64.  Y is fp32 [P, N] in sorted-pair order; pairs with pos < 0 (dropped by
+// the permutation for an expert id outside [0, E)) are left out of the sum.
 void orc_combine_bf16(const float* y, const int32_t* pos, const float* w, int64_t T,
                       int64_t topk, int64_t N, uint16_t* out) {
   parallel_for(T, [&](int64_t t) {
     for (int64_t n = 0; n < N; ++n) {
       double acc = 0.0;
-      for (int64_t j = 0; j < topk; ++j)
-        acc += (double)w[t * topk + j] * (double)y[(int64_t)pos[t * topk + j] * N + n];
+      for (int64_t j = 0; j < topk; ++j) {
+        const int64_t p = pos[t * topk + j];
+        if (p < 0) continue;  // a pair the permutation dropped contributes nothing
+        acc += (double)w[t * topk + j] * (double)y[p * N + n];
+      }
       out[t * N + n] = float_to_bf16_rne((float)acc);
     }
   });

@@ -198,7 +198,49 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__
   }
 }
 
-// out[t, n..n+8) = bf16(sum_j w[t,j] * y[pos[t,j], n..n+8)), fp32, j ascending.
+// out[t, n..n+8) = bf16(sum_j w[t,j] * y[pos[t,j], n..n+8)), fp32, j ascending,
+// for topk <= kMaxK: every pair's row segment is loaded before the first add,
+// so all topk loads are in flight together (a dropped pair, pos < 0, reads
+// the token's own output row instead, always valid memory, and is skipped in
+// the sum).  The token comes from the grid's y index.
+template <int kMaxK>
+__global__ __launch_bounds__(256) void k_combine_n(const uint16_t* __restrict__ y,
+                                                  const int32_t* __restrict__ pos,
+                                                  const float* __restrict__ w, int topk,
+                                                  int64_t N, uint16_t* __restrict__ out) {
+  const int64_t nvec = N / 8;
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= nvec) return;
+  const int64_t t = blockIdx.y;
+  int32_t pj[kMaxK];
+  uint4 q[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    pj[j] = j < topk ? pos[t * topk + j] : -1;
+    const uint16_t* src = pj[j] >= 0 ? y + (int64_t)pj[j] * N : out + t * N;
+    if (j < topk) q[j] = reinterpret_cast<const uint4*>(src)[v];
+  }
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j >= topk || pj[j] < 0) continue;
+    const float wj = w[t * topk + j];
+    const uint32_t q4[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      acc[2 * h] += wj * bf16_lo(q4[h]);
+      acc[2 * h + 1] += wj * bf16_hi(q4[h]);
+    }
+  }
+  uint4 o;
+  o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+  o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+  o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+  o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+  reinterpret_cast<uint4*>(out + t * N)[v] = o;
+}
+
+// General topk: one pair at a time.
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
                                                 const int32_t* __restrict__ pos,
                                                 const float* __restrict__ w, int64_t T, int topk,
@@ -411,8 +453,14 @@ extern "C" int nvq_moe_combine(const uint16_t* y, const int32_t* pos, const floa
   if (!aligned16(y) || !aligned16(out)) return NVQ_EALIGN;
   const int64_t n = T * (N / 8);
   if (n == 0) return NVQ_OK;
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), y, pos, weights, T, (int)topk, N, out);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (topk <= 8 && T <= 65535 && (N / 8 + 255) / 256 <= 0x7FFFFFFF) {
+    const dim3 grid((unsigned)((N / 8 + 255) / 256), (unsigned)T);
+    hipLaunchKernelGGL(k_combine_n<8>, grid, dim3(256), 0, s, y, pos, weights, (int)topk, N, out);
+  } else {
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, pos,
+                       weights, T, (int)topk, N, out);
+  }
   return last_launch();
 }
 

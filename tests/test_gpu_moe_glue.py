@@ -93,3 +93,24 @@ def test_no_tokens():
     torch.cuda.synchronize()
     assert ids.shape == (0, topk) and sp.numel() == 0 and out.shape[0] == 0
     assert_bits_equal(to_np(off), np.zeros(E + 1, np.int32), "offsets of no tokens")
+
+
+@pytest.mark.parametrize("topk,N", [(3, 64), (8, 4096), (9, 72)])
+def test_combine_with_dropped_pairs(topk, N):
+    """Pairs the permutation dropped (pos = -1) are left out of the combine,
+    through the all-loads-first kernel (topk <= 8) and the general one."""
+    nvq = _nvq()
+    g = np.random.default_rng(topk * 1000 + N)
+    T, E = 300, 16
+    ids = np.stack([g.permutation(E)[:topk] for _ in range(T)]).astype(np.int32)
+    ids[g.random((T, topk)) < 0.05] = E + 1  # dropped
+    sp, off, pos, _ = nvq.nvq_moe_permute(to_gpu(ids), E)
+    opos = to_np(pos)
+    assert (opos < 0).any()
+    P = int(to_np(off)[-1])
+    y = inputs.to_bf16_bits(g.standard_normal((P, N)).astype(np.float32))
+    w = g.random((T, topk)).astype(np.float32)
+    out = nvq.nvq_moe_combine(to_gpu(y), pos, to_gpu(w))
+    ref = oracle.combine_bf16(inputs.bf16_bits_to_f32(y), opos, w)
+    np.testing.assert_allclose(inputs.bf16_bits_to_f32(to_np(out)), inputs.bf16_bits_to_f32(ref),
+                               rtol=2 ** -7, atol=1e-6)

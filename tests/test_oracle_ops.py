@@ -264,3 +264,22 @@ def test_qat_adjoint_identities():
         rows = slice(off[e], off[e + 1])
         np.testing.assert_allclose(dw.reshape(N, K), DY[rows].T @ X[rows], rtol=1e-12, atol=1e-12)
     assert tot == pytest.approx(lhs, rel=1e-12)
+
+
+def test_combine_leaves_out_dropped_pairs():
+    """A pair the permutation dropped (pos < 0) contributes nothing: the result
+    equals the combine over the remaining pairs, written out in numpy."""
+    g = np.random.default_rng(21)
+    T, topk, N = 5, 3, 16
+    y = g.standard_normal((T * topk, N)).astype(np.float32)
+    w = g.random((T, topk)).astype(np.float32)
+    pos = np.arange(T * topk, dtype=np.int32)
+    pos[[1, 7, 8]] = -1
+    got = inputs.bf16_bits_to_f32(oracle.combine_bf16(y, pos, w))
+    ref = np.zeros((T, N))
+    for t in range(T):
+        for j in range(topk):
+            p = pos[t * topk + j]
+            if p >= 0:
+                ref[t] += np.float64(w[t, j]) * y[p].astype(np.float64)
+    np.testing.assert_array_equal(got, inputs.bf16_bits_to_f32(inputs.to_bf16_bits(ref.astype(np.float32))))
