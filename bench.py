@@ -225,6 +225,34 @@ class MoeLeg:
                                                   nvq.NVQ_EPI_NONE, comp, path))
         timer("combine", lambda: nvq.nvq_moe_combine(self.y2, self.pos, self.w))
 
+    def time_graph(self, reps=20):
+        """The same layer step captured once into a HIP graph and replayed:
+        every kernel and its inputs as in the eager step, without the
+        per-launch host overhead between the small kernels."""
+        import torch
+
+        passthrough = lambda label, fn: fn()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step(passthrough)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(passthrough)
+        for _ in range(3):
+            g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        self.graph_ms = a.elapsed_time(b) / reps
+        del g
+
     def report(self, timer_):
         class _T:
             total = {k.split("/", 1)[1]: v for k, v in timer_.total.items() if k.startswith(self.name + "/")}
@@ -257,6 +285,8 @@ class MoeLeg:
                                      "gemm_tflops": round(tf8, 1),
                                      "frac_fp8_mfma_peak": round(tf8 / FP8_PEAK_TFLOPS, 4),
                                      "time_vs_chosen_path": round((g8 + d8) / (gu + dn), 3)}
+        if hasattr(self, "graph_ms"):
+            out["layer_ms_graph"] = round(self.graph_ms, 4)
         return out
 
 
@@ -588,6 +618,9 @@ def main():
             for _ in range(3):
                 leg.symmetric(timer)
     timer.collect()
+    for leg in legs:
+        if leg.name.startswith("moe"):
+            leg.time_graph()
 
     q = next(l for l in legs if l.name == "quant")
     q_ms = timer.avg_ms("quantize")
