@@ -513,16 +513,16 @@ class KvLeg:
                 "append_ms": round(timer.avg_ms("kv/append"), 4)}
 
 
-def profiled_traffic():
-    """HBM bytes per nvfp4_quantize call on the sweep, from the committed
-    rocprofv3 FETCH_SIZE/WRITE_SIZE summary (copy-kernel calibrated), when the
-    quantizer sources still hash to the value recorded there; else None."""
+def profiled_traffic(profile="quantize_sweep_8192x7168_bf16.txt",
+                     sources=("quantize.hip", "nvq_device.h", "nvq_internal.h")):
+    """HBM bytes per call from a committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary (copy-calibrated), when the kernel sources still hash to the value
+    recorded there; else None (the figure is stale once the kernel changes)."""
     import hashlib
 
     here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", "quantize_sweep_8192x7168_bf16.txt")
     try:
-        text = open(path).read()
+        text = open(os.path.join(here, "profiles", profile)).read()
     except OSError:
         return None
     m_b = re.search(r"^traffic_bytes_per_call: (\d+)", text, re.M)
@@ -530,7 +530,7 @@ def profiled_traffic():
     if not (m_b and m_h):
         return None
     h = hashlib.sha1()
-    for fn in ("quantize.hip", "nvq_device.h", "nvq_internal.h"):
+    for fn in sources:
         with open(os.path.join(here, "qat_nvfp4_quantize_amd", "csrc", fn), "rb") as fh:
             h.update(fh.read())
     return int(m_b.group(1)) if h.hexdigest() == m_h.group(1) else None
@@ -657,7 +657,11 @@ def main():
         result["roofline_gemm"] = {"kernel": "k_moe_gemm_deq16 (%s gate/up + down)" % moe_main[0].name,
                                    "bound": "mfma", "achieved": r["gemm_tflops"],
                                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                   "frac": r["gemm_frac_fp16_mfma_peak"], "traffic": None,
+                                   "frac": r["gemm_frac_fp16_mfma_peak"],
+                                   "traffic": profiled_traffic(
+                                       "moe_grouped_gemm_decode_prefill.txt",
+                                       ("gemm_w4a4.hip", "nvq_device.h", "nvq_internal.h",
+                                        "nvq_scan.h")) if moe_main[0].name == "moe_prefill" else None,
                                    "frac_of_fp4_peak": r["gemm_frac_fp4_peak"]}
     if any(l.name == "copy" for l in legs):
         c = next(l for l in legs if l.name == "copy")
