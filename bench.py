@@ -384,6 +384,27 @@ class QatLeg:
                                        dw=self.dw_gu, ws=self.ws))
         timer("token_sum", lambda: nvq.nvq_moe_combine(self.dx, self.pos, self.ones, out=self.dx_tok))
 
+    def direction_mode(self, timer_):
+        """The up/down-bit reading of the guidance record (outside the timed
+        steps): direction record of the gate/up weights from the rollout's
+        codes and its masters, then the guided requantization of the drifted
+        masters in direction mode."""
+        import torch
+
+        nvq = self.nvq
+        timer = lambda label, fn: timer_("qat_dir/" + label, fn)
+        if not hasattr(self, "dir_bits"):
+            from qat_nvfp4_quantize_amd import inputs
+
+            self.w_master_gu = inputs.weights_device(self.s, "gu")
+            self.dir_bits = torch.empty_like(self.rec["gu"])
+        codes, sc, st = self.q["gu"]
+        timer("record", lambda: nvq.nvfp4_guidance_record(
+            codes, nvq.NVQ_GUIDE_DIRECTION, x=self.w_master_gu, scales=sc, tensor_scale=st,
+            out=self.dir_bits))
+        timer("guide", lambda: nvq.nvfp4_guided_quantize(
+            self.wd["gu"], self.dir_bits, sc, st, nvq.NVQ_GUIDE_DIRECTION, out=self.gcodes["gu"]))
+
     def symmetric(self, timer_):
         """Ablation (outside the timed steps): symmetric W4A4 QAT, i.e. the
         trainer's activations NVFP4-quantized too.  Forward = quantize X +
@@ -443,6 +464,13 @@ class QatLeg:
         rms = timer.avg_ms("qat/record_gu") + timer.avg_ms("qat/record_dn")
         g["record_ms"] = round(rms, 4)
         g["record_GBps"] = round(rb / (rms * 1e-3) / 1e9, 1)
+        if "qat_dir/guide" in timer.total:
+            n = self.wd["gu"].numel()
+            rms, gms = timer.avg_ms("qat_dir/record"), timer.avg_ms("qat_dir/guide")
+            # direction record reads the master (2), codes (1/2), scales (1/16), writes bits (1/8)
+            g["direction_mode_gu"] = {
+                "record_ms": round(rms, 4), "record_GBps": round(n * 43 / 16 / (rms * 1e-3) / 1e9, 1),
+                "guide_ms": round(gms, 4), "guide_GBps": round(self.guide_bytes["gu"] / (gms * 1e-3) / 1e9, 1)}
         out["guided_requantize"] = g
         if "qat_sym/fwd_gu" in timer.total:
             sym = {}
@@ -617,6 +645,8 @@ def main():
         if leg.name == "qat":
             for _ in range(3):
                 leg.symmetric(timer)
+            for _ in range(3):
+                leg.direction_mode(timer)
     timer.collect()
     for leg in legs:
         if leg.name.startswith("moe"):

@@ -19,7 +19,9 @@
 //   mantissa:  of a = min(lo, 6) and a + 1 (adjacent points, whose mantissa
 //              bits differ), the one carrying the cached bit;
 //   direction: bit 1 -> hi, bit 0 -> lo.
-// Sign from signbit(w); a zero scale product gives magnitude 0.
+// Sign from signbit(w); a zero scale product gives magnitude 0.  Both modes
+// have a fast path on fp32 bit patterns for tensor scales in [2^-100, 2^100]
+// and a general seven-threshold path for the rest.
 //
 // Exactness: G s_b is exact in fp32 (<= 6 significant bits), and its product
 // with s_t (<= 30 bits) is exact in fp64.  Each block turns its seven grid
@@ -190,6 +192,34 @@ __global__ __launch_bounds__(kGuideThreads) void k_guided_quantize(
       const int32_t base = b ? r1 : r15 - (1 << 23);
       const int32_t pair = min(max((a - base) >> 23, 0), 2);
       const uint32_t idx = 2u * (uint32_t)(pair + (a >= t0)) + b;
+      out[j >> 3] |= (idx | ((u >> 28) & 8u)) << (4 * (j & 7));
+    }
+  } else if (kMode == NVQ_GUIDE_DIRECTION && s_t >= 0x1p-100 && s_t <= 0x1p100 && !zero_scale) {
+    // Fast path, direction mode.  The grid products p_i (i = 1..7) are
+    // {1/2, 1, 2, 4} P and {1, 2, 4} 1.5 P with P = s_b s_t: two chains of
+    // binade steps plus the first point.  lo counts p_i <= |w| against the
+    // round-up thresholds (R1 = RU(P), R15 = RU(1.5 P)); hi counts p_i < |w|
+    // (point 0 included) against the smallest floats above the round-down
+    // values (N1 = next(RD(P)), N15 = next(RD(1.5 P))), capped at 7.  In
+    // normal range both kinds of threshold scale exactly by 2 down a chain.
+    const double P = (double)s_b * s_t, P15 = (double)(1.5f * s_b) * s_t;
+    const int32_t r1 = (int32_t)__float_as_uint(f32_round_up(P));
+    const int32_t r15 = (int32_t)__float_as_uint(f32_round_up(P15));
+    const int32_t n1 = (int32_t)__float_as_uint(f32_round_down(P)) + 1;
+    const int32_t n15 = (int32_t)__float_as_uint(f32_round_down(P15)) + 1;
+    auto chain3 = [](int32_t a, int32_t base) {  // thresholds base, 2 base, 4 base
+      return min(max((a - base + (1 << 23)) >> 23, 0), 3);
+    };
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t u = __float_as_uint(v[j]);
+      const int32_t a = (int32_t)(u & 0x7FFFFFFFu);
+      const uint32_t b = (rec >> j) & 1u;
+      // one count with the thresholds of the recorded side (no divergence)
+      const int32_t base1 = b ? n1 : r1, base15 = b ? n15 : r15;
+      const int32_t cnt = (int32_t)(b & (uint32_t)(a > 0)) + (a >= base1 - (1 << 23)) +
+                          chain3(a, base1) + chain3(a, base15);
+      const uint32_t idx = (uint32_t)min(cnt, 7);
       out[j >> 3] |= (idx | ((u >> 28) & 8u)) << (4 * (j & 7));
     }
   } else {
