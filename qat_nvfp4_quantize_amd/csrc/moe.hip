@@ -53,8 +53,10 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
     key[i] = (e < E) ? (((uint64_t)ordered_key(l[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e))
                      : 0ull;
   }
-  double lmax = 0.0, den = 0.0;
-  double ex[8];
+  // Selection: lane j keeps the j-th chosen logit (topk <= 64), taken back
+  // from its key (no dependent reload; -0 comes back as +0, same exp).
+  double lmax = 0.0;
+  float my_lv = 0.0f;
   for (int j = 0; j < topk; ++j) {
     uint64_t best = 0;
 #pragma unroll
@@ -64,21 +66,24 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (key[i] == best) key[i] = 0ull;
-    // the logit from its key (no dependent reload); -0 comes back as +0,
-    // which gives the same exp
     const uint32_t kb = (uint32_t)(best >> 32);
     const float lv = __uint_as_float((kb & 0x80000000u) ? (kb & 0x7FFFFFFFu) : ~kb);
     if (j == 0) lmax = (double)lv;
-    const double x = exp((double)lv - lmax);
-    den += x;
-    if (j < 8) ex[j] = x;
+    if (lane == (j & 63)) my_lv = lv;
     if (lane == 0) ids[t * topk + j] = (int32_t)e;
   }
-  if (lane == 0) {
-    for (int j = 0; j < topk; ++j) {
-      const double x = j < 8 ? ex[j] : exp((double)l[ids[t * topk + j]] - lmax);
-      weights[t * topk + j] = (float)(x / den);
-    }
+  // Weights: softmax over the chosen logits in fp64, the exps one per lane,
+  // their sum in selection order (the same order on every lane).
+  if (topk <= 64) {
+    const double x = lane < topk ? exp((double)my_lv - lmax) : 0.0;
+    double den = 0.0;
+    for (int j = 0; j < topk; ++j) den += __shfl(x, j, 64);
+    if (lane < topk) weights[t * topk + lane] = (float)(x / den);
+  } else if (lane == 0) {
+    double den = 0.0;
+    for (int j = 0; j < topk; ++j) den += exp((double)l[ids[t * topk + j]] - lmax);
+    for (int j = 0; j < topk; ++j)
+      weights[t * topk + j] = (float)(exp((double)l[ids[t * topk + j]] - lmax) / den);
   }
 }
 
