@@ -118,3 +118,46 @@ def test_guided_rounding_validation():
                                    None) == -3
     assert L.nvfp4_guided_quantize(fake, 1, 1, 4, 32, fake, fake, fake, 0, fake, fake, 255,
                                    None) == -4
+
+
+def test_backward_glue_validation():
+    L = _lib()
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    # SwiGLU: bad dtype, I % 8, misaligned, null with rows
+    assert L.nvq_swiglu_forward(fake, 7, 4, 16, fake, None) == -1
+    assert L.nvq_swiglu_forward(fake, 1, 4, 12, fake, None) == -2
+    assert L.nvq_swiglu_forward(P(0x1008), 1, 4, 16, fake, None) == -3
+    assert L.nvq_swiglu_forward(None, 1, 4, 16, fake, None) == -1
+    assert L.nvq_swiglu_forward(None, 1, 0, 16, None, None) == 0  # no rows
+    assert L.nvq_swiglu_backward(fake, 1, fake, 4, 16, P(0x1004), None) == -3
+    assert L.nvq_swiglu_backward(fake, 1, None, 4, 16, fake, None) == -1
+    # combine backward: N % 8, topk < 1, dw without y, misaligned
+    assert L.nvq_moe_combine_backward(fake, fake, fake, fake, 4, 2, 12, fake, None, None) == -2
+    assert L.nvq_moe_combine_backward(fake, fake, fake, fake, 4, 0, 16, fake, None, None) == -2
+    assert L.nvq_moe_combine_backward(fake, None, fake, fake, 4, 2, 16, fake, fake, None) == -1
+    assert L.nvq_moe_combine_backward(P(0x1002), fake, fake, fake, 4, 2, 16, fake, None, None) == -3
+    assert L.nvq_moe_combine_backward(None, None, None, None, 0, 2, 16, None, None, None) == 0
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No library means an error, never a CPU fallback."""
+    from qat_nvfp4_quantize_amd import nvq as mod
+
+    saved = mod._lib
+    mod._lib = None
+    try:
+        with pytest.raises(RuntimeError):
+            mod.load(str(tmp_path / "missing.so"))
+    finally:
+        mod._lib = saved
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
