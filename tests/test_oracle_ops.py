@@ -283,3 +283,37 @@ def test_combine_leaves_out_dropped_pairs():
             if p >= 0:
                 ref[t] += np.float64(w[t, j]) * y[p].astype(np.float64)
     np.testing.assert_array_equal(got, inputs.bf16_bits_to_f32(inputs.to_bf16_bits(ref.astype(np.float32))))
+
+
+def test_residual_columns_hand_worked_and_bf16_ties():
+    """bf16 residual columns (QUADS explainer §2.2-B: the correction uses the
+    activation's quantization residual on the selected channels). Hand-worked:
+    with s_t = 1 and block scale 2, 9 + 2^-8 rounds to grid value 4 (value 8), so
+    r = 1 + 2^-8, a bf16 tie that goes to the even 1.0; 9 + 3*2^-8 leaves
+    1 + 3*2^-8, a tie that goes up to 1 + 2^-6; 7.2 rounds to 8 and leaves
+    -0.8 (bf16 -0.80078125); 2.5 gives the quotient 1.25, a midpoint that
+    goes to the even grid value 1.0 (value 2) and leaves 0.5."""
+    x = np.zeros((2, 32), np.float32)
+    x[0, 0] = 2688.0                       # tensor scale 1
+    x[1, :16] = [12.0, 9.00390625, 9.01171875, 7.2, 2.5] + [0.0] * 11  # block max 12: s_b = 2
+    x[1, 16:] = [100.0] + [0.125] * 15     # s_b = 16: 100 -> 96, 0.125 -> 0
+    codes, scales, st = oracle.quantize(x)
+    assert st == 1.0
+    idx = np.array([1, 2, 3, 4, 16, 17, 0], np.int32)
+    got = oracle.residual_columns_bf16(x, codes, scales, st, idx)
+    assert got.dtype == np.uint16 and got.shape == (2, 7)
+    assert got[0].tolist() == [0] * 7  # 2688 is 6 * 448 * 1, on the grid
+    assert got[1].tolist() == [0x3F80, 0x3F82, 0xBF4D, 0x3F00, 0x4080, 0x3E00, 0]
+
+
+def test_residual_columns_equal_bf16_of_x_minus_dequantize():
+    x = _x(3, 77, 96)
+    xb = inputs.to_bf16_bits(x)
+    for inp in (x, xb):
+        codes, scales, st = oracle.quantize(inp)
+        xf = inputs.bf16_bits_to_f32(inp) if inp.dtype == np.uint16 else inp
+        r = xf - oracle.dequantize(codes, scales, st)  # IEEE fp32 subtraction
+        idx = np.array([95, 0, 17, 16, 50, 50], np.int32)
+        got = oracle.residual_columns_bf16(inp, codes, scales, st, idx)
+        assert np.array_equal(got, inputs.to_bf16_bits(r[:, idx]))
+        assert oracle.residual_columns_bf16(inp, codes, scales, st, idx[:0]).shape == (77, 0)
