@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--legs", default="quant,moe,qat,kv")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--quant-shape", default="8192x7168",
+                   help="rows x K of the quantizer leg (the headline workload is 8192x7168; "
+                        "other shapes are for tile-count studies)")
     return p.parse_args()
 
 
@@ -92,13 +95,13 @@ class EventTimer:
 class QuantLeg:
     name = "quant"
 
-    def __init__(self):
+    def __init__(self, M=8192, K=7168):
         import torch
 
         from qat_nvfp4_quantize_amd import inputs, nvq
 
         self.nvq = nvq
-        self.x_np = inputs.quant_sweep()
+        self.x_np = inputs.quant_sweep(M, K)
         M, K = self.x_np.shape
         self.M, self.K, self.k = M, K, 64
         self.x = torch.from_numpy(self.x_np.view(np.int16)).view(torch.bfloat16).cuda()
@@ -135,7 +138,7 @@ class QuantLeg:
         dt = sorted(runs)[1]
         return {"value": round(self.bytes / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
                 "kind": "oracle",
-                "sample": "full 8192x7168 bf16 sweep tensor: fp64 exhaustive-search quantizer + "
+                "sample": f"full {self.M}x{self.K} bf16 sweep tensor: fp64 exhaustive-search quantizer + "
                           "residual scores, median of 3 runs (%.2f s each, %.1f s in all)"
                           % (dt, sum(runs))}
 
@@ -606,8 +609,9 @@ def main():
     from qat_nvfp4_quantize_amd import inputs as _inputs
     if "moe" in wanted or "decode" in wanted:
         legs.append(MoeLeg(_inputs.DECODE))
+    qM, qK = (int(v) for v in args.quant_shape.lower().split("x"))
     if "quant" in wanted:
-        legs.append(QuantLeg())
+        legs.append(QuantLeg(qM, qK))
     if "copy" in wanted:
         legs.append(CopyLeg())
     if "moe" in wanted or "prefill" in wanted:
@@ -668,15 +672,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16 in, e2m1/e4m3 out",
         "data": "synthetic",
-        "config": {"workload": "quantizer sweep: bf16 activation 8192x7168, Student-t nu=4, "
-                               "36 outlier channels x50; codes+scales+tensor scale+residual sums, "
-                               "then top-64 channels"},
+        "config": {"workload": f"quantizer sweep: bf16 activation {q.M}x{q.K}, Student-t nu=4, "
+                               f"{round(0.005 * q.K)} outlier channels x50; codes+scales+tensor "
+                               "scale+residual sums, then top-64 channels"},
         "legs": {"quant": {"quantize_ms": round(q_ms, 5), "topk_ms": round(timer.avg_ms("topk"), 5),
                            "algorithmic_bytes": q.bytes}},
         "roofline": {"kernel": "nvfp4_quantize (amax + quantize + score-reduce kernels)",
                      "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": profiled_traffic()},
+                     "traffic": profiled_traffic() if (q.M, q.K) == (8192, 7168) else None},
     }
     for leg in legs:
         if leg.name.startswith("moe") or leg.name in ("qat", "kv"):
