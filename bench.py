@@ -43,6 +43,47 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def host_cpu_info():
+    """CPU model (from /proc/cpuinfo) and the CPUs this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        ncpu = os.cpu_count() or 1
+    return model, ncpu
+
+
+def oracle_thread_count():
+    """Threads for the CPU baseline: ORACLE_THREADS if set, else the host's CPU
+    share as the job environment states it (OMP_NUM_THREADS), else every CPU
+    this process may run on."""
+    for var in ("ORACLE_THREADS", "OMP_NUM_THREADS"):
+        v = os.environ.get(var, "")
+        if v.isdigit() and int(v) > 0:
+            return int(v)
+    return host_cpu_info()[1]
+
+
+def timed_median(fn, runs=3, warm=None):
+    """One warm-up call (of `warm` if given: a smaller call of the same code),
+    then the median wall time of `runs` calls of fn."""
+    (warm or fn)()
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2], sum(ts)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -136,8 +177,9 @@ class QuantLeg:
             oracle.residual_scores(x, c, s, st)
             runs.append(time.perf_counter() - t0)
         dt = sorted(runs)[1]
+        model, ncpu = host_cpu_info()
         return {"value": round(self.bytes / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
-                "kind": "oracle",
+                "kind": "oracle", "cpu_model": model, "host_cpus": ncpu,
                 "sample": f"full {self.M}x{self.K} bf16 sweep tensor: fp64 exhaustive-search quantizer + "
                           "residual scores, median of 3 runs (%.2f s each, %.1f s in all)"
                           % (dt, sum(runs))}
@@ -227,6 +269,49 @@ class MoeLeg:
         timer("gemm_dn" + tag, lambda: self.gemm("dn", self.qh, s.P, None, r2, idx2, (self.y2, None),
                                                   nvq.NVQ_EPI_NONE, comp, path))
         timer("combine", lambda: nvq.nvq_moe_combine(self.y2, self.pos, self.w))
+
+    def cpu_baseline(self, max_rows=64):
+        """The oracle's W4A4 grouped GEMM with compensation (fp64, exhaustive
+        dequantization) on the first `max_rows` rows of one expert, gate/up
+        then down, timed on the host: a fixed, labelled subset of the layer,
+        reported as GFLOP/s of the algorithmic 2 rows K N (the compensation's
+        2 rows k N comes on top and is not counted)."""
+        import oracle
+        from qat_nvfp4_quantize_amd import inputs
+
+        s = self.s
+        e = 0 if self.name == "moe_decode" else s.E - 1
+        ids, _ = oracle.route(inputs.logits(s), s.topk)
+        sp, off, _ = oracle.permute(ids, s.E)
+        n_e = int(off[e + 1] - off[e])
+        toks = sp[off[e]:off[e + 1]][:max_rows] // s.topk
+        rows = toks.size
+        xe = inputs.activations(s)[toks]
+        he = inputs.to_bf16_bits(np.random.default_rng([0, s.wid, 991]).standard_normal(
+            (rows, s.I), dtype=np.float32))
+        legs = []
+        for proj, a in (("gu", xe), ("dn", he)):
+            ac, asc, ast = oracle.quantize(a)
+            idx = oracle.topk(oracle.residual_scores(a, ac, asc, ast), s.k)
+            wc, wsc, wst = oracle.quantize(inputs.expert_weight(s, proj, e))
+            args = (ac, asc, ast, a, idx, wc, wsc, wst, np.arange(rows, dtype=np.int32),
+                    np.zeros(rows, np.int32))
+            legs.append((oracle.moe_gemm_w4a4, args))
+        t = 0.0
+        total = 0.0
+        for fn, args in legs:
+            warm = args[:8] + (args[8][:2], args[9][:2])
+            dt, tot = timed_median(lambda: fn(*args), warm=lambda: fn(*warm))
+            t += dt
+            total += tot
+        flops = 2.0 * rows * s.H * 2 * s.I + 2.0 * rows * s.I * s.H
+        return {"value": round(flops / t / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.threads(),
+                "kind": "oracle",
+                "sample": f"first {rows} of expert {e}'s {n_e} rows ({s.P} in the layer): gate/up "
+                          f"K={s.H} N={2 * s.I} and down K={s.I} N={s.H} with k={s.k} compensation "
+                          "(its own inputs: those rows' tokens of X and a seeded N(0,1) H block), "
+                          "median of 3 runs after a 2-row warm-up (%.2f s per subset, %.1f s in all)"
+                          % (t, total)}
 
     def time_graph(self, reps=20):
         """The same layer step captured once into a HIP graph and replayed:
@@ -386,6 +471,43 @@ class QatLeg:
         timer("wgrad_gu", lambda: call(W, *qg, self.off, s.P, x=self.x, dy=self.dy_gu, a_row=self.a_row,
                                        dw=self.dw_gu, ws=self.ws))
         timer("token_sum", lambda: nvq.nvq_moe_combine(self.dx, self.pos, self.ones, out=self.dx_tok))
+
+    def cpu_baseline(self, rows=32):
+        """The oracle's QAT forward, input gradient and weight gradient (fp64,
+        exhaustive dequantization of the cached record) on the first `rows`
+        rows of expert 0, both projections: GFLOP/s of the algorithmic
+        2 rows K N per GEMM."""
+        import oracle
+        from qat_nvfp4_quantize_amd import inputs
+
+        s = self.s
+        g = np.random.default_rng([0, s.wid, 992])
+        legs, flops = [], 0.0
+        for proj in ("gu", "dn"):
+            K, N = (s.H, 2 * s.I) if proj == "gu" else (s.I, s.H)
+            x = inputs.to_bf16_bits(g.standard_normal((rows, K), dtype=np.float32))
+            dy = inputs.to_bf16_bits(g.standard_normal((rows, N), dtype=np.float32))
+            wc, wsc, wst = oracle.quantize(inputs.expert_weight(s, proj, 0))
+            r = np.arange(rows, dtype=np.int32)
+            z = np.zeros(rows, np.int32)
+            nn, cc = np.meshgrid(np.arange(N, dtype=np.int32), np.arange(K, dtype=np.int32),
+                                 indexing="ij")
+            legs += [(oracle.qat_fwd, (x, r, z, wc, wsc, wst), (x, r[:2], z[:2], wc, wsc, wst)),
+                     (oracle.qat_dgrad, (dy, r, z, wc, wsc, wst), (dy, r[:2], z[:2], wc, wsc, wst)),
+                     (oracle.qat_wgrad, (dy, x, r, 0, rows, nn.ravel(), cc.ravel()),
+                      (dy, x, r, 0, 2, nn.ravel()[:4096], cc.ravel()[:4096]))]
+            flops += 3 * 2.0 * rows * K * N
+        t = total = 0.0
+        for fn, args, warm in legs:
+            dt, tot = timed_median(lambda: fn(*args), warm=lambda: fn(*warm))
+            t += dt
+            total += tot
+        return {"value": round(flops / t / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.threads(),
+                "kind": "oracle",
+                "sample": f"expert 0, first {rows} rows: forward, input gradient and weight gradient "
+                          f"of gate/up (K={s.H}, N={2 * s.I}) and down (K={s.I}, N={s.H}) on seeded "
+                          "N(0,1) inputs, median of 3 runs after a 2-row warm-up (%.2f s per "
+                          "subset, %.1f s in all)" % (t, total)}
 
     def direction_mode(self, timer_):
         """The up/down-bit reading of the guidance record (outside the timed
@@ -597,7 +719,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    os.environ.setdefault("ORACLE_THREADS", "16")
+    os.environ["ORACLE_THREADS"] = str(oracle_thread_count())
     legs = []
     wanted = args.legs.split(",")
     if "quant" not in wanted:
@@ -703,6 +825,10 @@ def main():
                                   "GBps": round(c.bytes / timer.avg_ms("copy") / 1e6, 1)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = q.cpu_baseline()
+        for leg in legs:
+            if leg.name.startswith("moe") or leg.name == "qat":
+                log(f"[bench] cpu baseline: {leg.name}")
+                result["legs"][leg.name]["cpu_baseline"] = leg.cpu_baseline()
     print(json.dumps(result), flush=True)
 
 

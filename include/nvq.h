@@ -82,7 +82,11 @@ int nvq_device_status(const void* ws, void* stream, uint32_t* flags);
 /* NVFP4 quantization (QUADS §1, §2.1; TRACE "Fonctionnement").
  *
  * x        [batch, rows, K] of dtype x_dtype (NVQ_F32 or NVQ_BF16), 16-byte
- *          aligned; K % 16 == 0; 1 <= batch <= 65535.
+ *          aligned; K % 16 == 0; 1 <= batch <= 65535.  Row r of item b starts
+ *          at element (b * rows + r) * ldx: ldx >= K is the row stride in
+ *          elements (0 means K, a dense tensor) and ldx * element size must be
+ *          a multiple of 16 bytes (NVQ_EALIGN otherwise; ldx < K: NVQ_ESHAPE).
+ *          Outputs are always dense.
  * amax_in  nullable device [batch] fp32: replaces amax_t = max|x| of each
  *          batch item (e.g. to requantize with a known scale).
  * codes    [batch, rows, K/2]  E2M1 codes, even element in the low nibble.
@@ -100,8 +104,9 @@ int nvq_device_status(const void* ws, void* stream, uint32_t* flags);
  */
 size_t nvfp4_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t K);
 int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t rows, int64_t K,
-                   const float* amax_in, uint8_t* codes, uint8_t* scales, float* tensor_scale,
-                   float* chan_score, void* ws, size_t ws_bytes, void* stream);
+                   int64_t ldx, const float* amax_in, uint8_t* codes, uint8_t* scales,
+                   float* tensor_scale, float* chan_score, void* ws, size_t ws_bytes,
+                   void* stream);
 
 /* NVFP4 dequantization: y = sign * fl32(fl32(G * s_b) * s_t), written as fp32
  * (y_dtype NVQ_F32) or rounded to nearest-even bf16 (NVQ_BF16).  This is the
@@ -166,6 +171,9 @@ int nvfp4_guided_quantize(const void* w, int w_dtype, int64_t batch, int64_t row
  *
  * Selects the k channels with the largest residual score (ties to the lower
  * channel index) and writes them in rank order to idx_out [k] (int32).
+ * x [rows, K] (row stride ldx >= K elements, 0 means K) is the tensor whose
+ * NVFP4 record (codes [rows, K/2], scales [rows, K/16], tensor_scale [1],
+ * dense) is given; it is read only to recompute scores or residuals.
  * scores_in  nullable [K]: the chan_score of nvfp4_quantize.  When NULL the
  *            score is recomputed from x and its NVFP4 record (codes, scales,
  *            tensor_scale), in the same order as nvfp4_quantize.
@@ -177,7 +185,7 @@ int nvfp4_guided_quantize(const void* w, int w_dtype, int64_t batch, int64_t row
  * Scores compare as numbers (-0 equals +0); they must not be NaN.
  */
 size_t residual_topk_workspace_bytes(int64_t rows, int64_t K, int32_t k);
-int residual_topk_channels(const void* x, int x_dtype, int64_t rows, int64_t K,
+int residual_topk_channels(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t ldx,
                            const uint8_t* codes, const uint8_t* scales,
                            const float* tensor_scale, const float* scores_in, float* scores_out,
                            int32_t k, int32_t* idx_out, uint16_t* resid_out, void* ws,

@@ -60,6 +60,8 @@ def lib():
             L.orc_float_to_bf16.restype = ctypes.c_uint16
             L.orc_float_to_bf16.argtypes = [_F]
             L.orc_float_to_bf16_array.argtypes = [_P, _I64, _P]
+            L.orc_double_to_bf16.restype = ctypes.c_uint16
+            L.orc_double_to_bf16.argtypes = [ctypes.c_double]
             L.orc_threads.restype = ctypes.c_int
             for name in ("orc_quantize", "orc_quantize_threshold_form"):
                 f = getattr(L, name)
@@ -74,6 +76,8 @@ def lib():
                                               ctypes.c_int, _P]
             L.orc_dequantize_bf16.argtypes = [_P, _P, _F, _I64, _I64, _P]
             L.orc_residual_scores.argtypes = [_P, ctypes.c_int, _I64, _P, _P, _F, _I64, _I64, _P]
+            L.orc_residual_scores_chunk128.argtypes = [_P, ctypes.c_int, _I64, _P, _P, _F, _I64,
+                                                       _I64, _P]
             L.orc_topk.argtypes = [_P, _I64, _I64, _P]
             L.orc_residual_columns_bf16.argtypes = [_P, ctypes.c_int, _I64, _P, _P, _F, _I64,
                                                     _I64, _P, _I64, _P]
@@ -137,18 +141,21 @@ def _as_input(x):
     return _c(x, np.float32), F32
 
 
-def quantize(x, amax_in=None, threshold_form=False):
+def quantize(x, amax_in=None, threshold_form=False, K=None):
     """NVFP4 quantization of a [rows, K] tensor (fp32, or bf16 given as uint16 bits).
+    With K given, x is [rows, ldx] and its first K columns are the tensor
+    (row stride ldx = x.shape[1]).
 
     Returns (codes [rows, K/2] u8, scales [rows, K/16] u8, s_t float)."""
     xa, dt = _as_input(x)
-    rows, K = xa.shape
+    rows, ldx = xa.shape
+    K = ldx if K is None else int(K)
     codes = np.empty((rows, K // 2), np.uint8)
     scales = np.empty((rows, K // 16), np.uint8)
     st = np.zeros(1, np.float32)
     amax = None if amax_in is None else np.array([amax_in], np.float32)
     fn = lib().orc_quantize_threshold_form if threshold_form else lib().orc_quantize
-    rc = fn(_ptr(xa), dt, rows, K, K, _ptr(amax), _ptr(codes), _ptr(scales), _ptr(st))
+    rc = fn(_ptr(xa), dt, rows, K, ldx, _ptr(amax), _ptr(codes), _ptr(scales), _ptr(st))
     if rc != 0:
         raise ValueError("oracle quantize failed: %d" % rc)
     return codes, scales, float(st[0])
@@ -202,13 +209,26 @@ def dequantize(codes, scales, s_t, out="f32"):
     return y
 
 
-def residual_scores(x, codes, scales, s_t):
+def residual_scores(x, codes, scales, s_t, order="sub16", K=None):
+    """Per-channel residual score sum |x - deq(q(x))| (fp32 sums).  order
+    "sub16": 16-row sequential sub-chunk sums, summed in order within 128-row
+    chunks, chunks in order (the order the library computes); "chunk128": a
+    sequential sum inside each 128-row chunk, chunks in order.  With K given,
+    x is [rows, ldx] and its first K columns are the tensor."""
     xa, dt = _as_input(x)
-    rows, K = xa.shape
+    rows, ldx = xa.shape
+    K = ldx if K is None else int(K)
     s = np.empty(K, np.float32)
-    lib().orc_residual_scores(_ptr(xa), dt, K, _ptr(_c(codes, np.uint8)),
-                              _ptr(_c(scales, np.uint8)), s_t, rows, K, _ptr(s))
+    fn = {"sub16": lib().orc_residual_scores,
+          "chunk128": lib().orc_residual_scores_chunk128}[order]
+    fn(_ptr(xa), dt, ldx, _ptr(_c(codes, np.uint8)), _ptr(_c(scales, np.uint8)), s_t, rows, K,
+       _ptr(s))
     return s
+
+
+def double_to_bf16(v: float) -> int:
+    """bf16 bit pattern of the fp64 value v, rounded once, to nearest even."""
+    return int(lib().orc_double_to_bf16(float(v)))
 
 
 def topk(scores, k):
@@ -218,12 +238,15 @@ def topk(scores, k):
     return idx
 
 
-def residual_columns_bf16(x, codes, scales, s_t, idx):
+def residual_columns_bf16(x, codes, scales, s_t, idx, K=None):
+    """bf16(fl32(x - deq(q(x))))[:, idx]; with K given, x is [rows, ldx] and
+    its first K columns are the tensor."""
     xa, dt = _as_input(x)
-    rows, K = xa.shape
+    rows, ldx = xa.shape
+    K = ldx if K is None else int(K)
     idx = _c(idx, np.int32)
     out = np.empty((rows, idx.size), np.uint16)
-    lib().orc_residual_columns_bf16(_ptr(xa), dt, K, _ptr(_c(codes, np.uint8)),
+    lib().orc_residual_columns_bf16(_ptr(xa), dt, ldx, _ptr(_c(codes, np.uint8)),
                                     _ptr(_c(scales, np.uint8)), s_t, rows, K, _ptr(idx),
                                     idx.size, _ptr(out))
     return out

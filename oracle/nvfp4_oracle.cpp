@@ -81,6 +81,33 @@ uint16_t float_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Round a real number held exactly in fp64 to bf16, round-to-nearest-even, in
+// one step (no detour through fp32, which would round twice).  bf16 keeps 8
+// significant bits over fp32's exponent range: normal values are multiples of
+// 2^(e-7) in the binade [2^e, 2^(e+1)), e >= -126, and below 2^-126 the
+// subnormal spacing is 2^-133.  The scaled value is rounded to an integer with
+// ties to even (nearbyint in the default rounding mode), which is exact in
+// fp64; a carry to the next binade gives the right value.  Magnitudes at or
+// above the midpoint between the largest finite bf16 (2^127 * (2 - 2^-7)) and
+// 2^128 round to infinity.  NaN maps to the canonical quiet NaN.
+uint16_t double_to_bf16_rne(double v) {
+  if (std::isnan(v)) return 0x7FC0u;
+  const uint16_t sign = std::signbit(v) ? 0x8000u : 0u;
+  const double a = std::fabs(v);
+  if (a == 0.0) return sign;
+  const double kOverflow = std::ldexp(2.0 - std::ldexp(1.0, -8), 127);  // max + half ulp
+  if (a >= kOverflow) return sign | 0x7F80u;
+  int e2 = 0;
+  std::frexp(a, &e2);           // a = f 2^e2, f in [0.5, 1): binade [2^(e2-1), 2^e2)
+  int e = e2 - 1;               // a in [2^e, 2^(e+1))
+  if (e < -126) e = -126;       // subnormal range: fixed spacing 2^-133
+  const double q = std::nearbyint(std::ldexp(a, 7 - e));  // units of 2^(e-7)
+  const float r = (float)std::ldexp(q, e - 7);  // exact: <= 8 significant bits in fp32 range
+  uint32_t u;
+  std::memcpy(&u, &r, 4);
+  return (uint16_t)(sign | (u >> 16));
+}
+
 // Element (r, c) of a row-major [rows, ld] tensor of dtype 0 = f32, 1 = bf16,
 // returned as float (bf16 -> f32 is exact).
 float load_elem(const void* x, int dtype, int64_t r, int64_t ld, int64_t c) {
@@ -318,6 +345,7 @@ double orc_e2m1_value(int idx) { return kE2M1[idx & 7]; }
 double orc_e4m3_value(int code) { return e4m3_value(code); }
 float orc_tensor_scale(float amax) { return (float)((double)amax / kTensorScaleDivisor); }
 uint16_t orc_float_to_bf16(float f) { return float_to_bf16_rne(f); }
+uint16_t orc_double_to_bf16(double v) { return double_to_bf16_rne(v); }
 void orc_float_to_bf16_array(const float* x, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = float_to_bf16_rne(x[i]);
 }
@@ -445,6 +473,31 @@ void orc_residual_scores(const void* x, int dtype, int64_t ldx, const uint8_t* c
   });
 }
 
+// The same score in the plainer order of a sequential fp32 sum inside each
+// 128-row chunk (no 16-row level), chunks summed in ascending order.  The
+// pages fix no order; this one is kept beside the order above so the tests
+// can show that the choice of order does not change which channels are
+// selected on the workloads' activations.
+void orc_residual_scores_chunk128(const void* x, int dtype, int64_t ldx, const uint8_t* codes,
+                                  const uint8_t* scales, float s_t, int64_t rows, int64_t K,
+                                  float* scores) {
+  const int64_t kChunk = 128;
+  parallel_for(K, [&](int64_t c) {
+    float score = 0.0f;
+    for (int64_t m0 = 0; m0 < rows; m0 += kChunk) {
+      float part = 0.0f;
+      for (int64_t m = m0; m < std::min(rows, m0 + kChunk); ++m) {
+        const float xv = load_elem(x, dtype, m, ldx, c);
+        const float v = dequant_elem(codes, scales, s_t, K, m, c);
+        const float r = xv - v;
+        part += std::fabs(r);
+      }
+      score += part;
+    }
+    scores[c] = score;
+  });
+}
+
 // The k channels with the largest score, ties to the lower channel index,
 // written in rank order (QUADS explainer §2.2-B: binary mask of the top
 // residual channels).
@@ -559,21 +612,23 @@ void orc_moe_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, float a_
 }
 
 // SwiGLU on a fused gate/up output y [rows, 2I] (gate = first I columns):
-// h = bf16(silu(g) * u), silu(z) = z / (1 + exp(-z)), fp64.
+// h = bf16(silu(g) * u), silu(z) = z / (1 + exp(-z)), evaluated in fp64 and
+// rounded once from fp64 to bf16.
 void orc_swiglu_bf16(const double* y, int64_t rows, int64_t I, uint16_t* h) {
   parallel_for(rows, [&](int64_t r) {
     for (int64_t i = 0; i < I; ++i) {
       const double g = y[r * 2 * I + i];
       const double u = y[r * 2 * I + I + i];
       const double v = g / (1.0 + std::exp(-g)) * u;
-      h[r * I + i] = float_to_bf16_rne((float)v);
+      h[r * I + i] = double_to_bf16_rne(v);
     }
   });
 }
 
 // Combine: out[t, n] = bf16( sum_j w[t,j] * Y[pos[t*topk+j], n] ), j ascending,
-// fp64.  Y is fp32 [P, N] in sorted-pair order; pairs with pos < 0 (dropped by
-// the permutation for an expert id outside [0, E)) are left out of the sum.
+// fp64, rounded once from fp64 to bf16.  Y is fp32 [P, N] in sorted-pair
+// order; pairs with pos < 0 (dropped by the permutation for an expert id
+// outside [0, E)) are left out of the sum.
 void orc_combine_bf16(const float* y, const int32_t* pos, const float* w, int64_t T,
                       int64_t topk, int64_t N, uint16_t* out) {
   parallel_for(T, [&](int64_t t) {
@@ -584,7 +639,7 @@ void orc_combine_bf16(const float* y, const int32_t* pos, const float* w, int64_
         if (p < 0) continue;  // a pair the permutation dropped contributes nothing
         acc += (double)w[t * topk + j] * (double)y[p * N + n];
       }
-      out[t * N + n] = float_to_bf16_rne((float)acc);
+      out[t * N + n] = double_to_bf16_rne(acc);
     }
   });
 }

@@ -47,9 +47,38 @@ int amax_wg_per_item(int64_t batch, int64_t n_vec_per_item) {
 }
 
 // ---------------------------------------------------------------- pass 1 --
-// Per-workgroup partial max of |x| (as fp32 bits) over a strided slice of one
-// batch item; each wave reduces with DPP, the four wave maxima meet in LDS.  Non-finite values compare above all finite
-// ones and are reported by pass 2.  Also clears the status word.
+// Partial max of |x| (as fp32 bits) over a strided slice of one batch item:
+// each wave reduces with DPP and its lane 0 writes the wave's partial straight
+// to the workspace (kAmaxThreads / 64 partials per workgroup, no LDS).
+// Non-finite values compare above all finite ones and are reported by pass 2.
+// Also clears the status word.
+constexpr int kAmaxWaves = kAmaxThreads / 64;
+
+// |x| bits of the 8 bf16 or 4 fp32 values of a 16-byte vector, folded into m
+// (bf16 magnitudes as 16-bit patterns, shifted to fp32 position at the end).
+template <bool kBF16>
+__device__ __forceinline__ void amax_fold(uint32_t& m, uint4 q) {
+  if (kBF16) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+  } else {
+    m = max(m, max(max(q.x & 0x7FFFFFFFu, q.y & 0x7FFFFFFFu), max(q.z & 0x7FFFFFFFu, q.w & 0x7FFFFFFFu)));
+  }
+}
+
+template <bool kBF16>
+__device__ __forceinline__ void amax_store_wave(uint32_t m, uint32_t* __restrict__ partial, int nwg,
+                                                uint32_t* __restrict__ status) {
+  if (kBF16) m <<= 16;
+  m = wave_max_u32(m);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0)
+    partial[((int64_t)blockIdx.y * nwg + blockIdx.x) * kAmaxWaves + wave] = m;
+  if (status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;
+}
+
+// Dense tensor: the item is one flat run of vec_per_item 16-byte vectors.
 template <bool kBF16>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4* __restrict__ x,
                                                       int64_t vec_per_item, int nwg,
@@ -60,36 +89,33 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4* __restrict__
   const int64_t stride = (int64_t)nwg * kAmaxThreads;
   int64_t v = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
   uint32_t m = 0;
-  auto fold = [&](uint4 q) {
-    if (kBF16) {
-      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
-    } else {
-      m = max(m, max(max(q.x & 0x7FFFFFFFu, q.y & 0x7FFFFFFFu),
-                     max(q.z & 0x7FFFFFFFu, q.w & 0x7FFFFFFFu)));
-    }
-  };
   for (; v + 3 * stride < vec_per_item; v += 4 * stride) {
     const uint4 a = xi[v], b = xi[v + stride], c = xi[v + 2 * stride], d = xi[v + 3 * stride];
-    fold(a);
-    fold(b);
-    fold(c);
-    fold(d);
+    amax_fold<kBF16>(m, a);
+    amax_fold<kBF16>(m, b);
+    amax_fold<kBF16>(m, c);
+    amax_fold<kBF16>(m, d);
   }
-  for (; v < vec_per_item; v += stride) fold(xi[v]);
-  if (kBF16) m <<= 16;
-  m = wave_max_u32(m);
-  __shared__ uint32_t s_wmax[kAmaxThreads / 64];
-  if ((threadIdx.x & 63) == 0) s_wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = s_wmax[0];
-#pragma unroll
-    for (int w = 1; w < kAmaxThreads / 64; ++w) r = max(r, s_wmax[w]);
-    partial[(int64_t)item * nwg + blockIdx.x] = r;
+  for (; v < vec_per_item; v += stride) amax_fold<kBF16>(m, xi[v]);
+  amax_store_wave<kBF16>(m, partial, nwg, status);
+}
+
+// Row-strided tensor: rows of vpr vectors, ldv vectors apart (item b starts
+// at row b * rows).  Wave w of workgroup g takes rows 4 g + w, 4 g + w +
+// 4 nwg, ...; its lanes stride along the row.
+template <bool kBF16>
+__global__ __launch_bounds__(kAmaxThreads) void k_amax_rows(const uint4* __restrict__ x, int64_t rows,
+                                                           int64_t vpr, int64_t ldv, int nwg,
+                                                           uint32_t* __restrict__ partial,
+                                                           uint32_t* __restrict__ status) {
+  const uint4* xi = x + (int64_t)blockIdx.y * rows * ldv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t m = 0;
+  for (int64_t r = (int64_t)blockIdx.x * kAmaxWaves + wave; r < rows; r += (int64_t)nwg * kAmaxWaves) {
+    const uint4* row = xi + r * ldv;
+    for (int64_t c = lane; c < vpr; c += 64) amax_fold<kBF16>(m, row[c]);
   }
-  if (status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;
+  amax_store_wave<kBF16>(m, partial, nwg, status);
 }
 
 __global__ void k_clear_status(uint32_t* status) { *status = 0; }
@@ -157,8 +183,9 @@ __device__ __forceinline__ uint32_t e4m3_code_fast(float am, float g, float s_t)
 template <bool kBF16>
 struct RowBlock {
   uint4 q[kBF16 ? 2 : 4];
-  __device__ __forceinline__ void load(const void* xv, int64_t row, int64_t K, int64_t blk) {
-    load_at(static_cast<const char*>(xv) + (row * K + blk * 16) * (kBF16 ? 2 : 4));
+  // block blk of row `row` of a tensor whose rows are ld elements apart
+  __device__ __forceinline__ void load(const void* xv, int64_t row, int64_t ld, int64_t blk) {
+    load_at(static_cast<const char*>(xv) + (row * ld + blk * 16) * (kBF16 ? 2 : 4));
   }
   __device__ __forceinline__ void load_at(const char* at) {
     const uint4* p = reinterpret_cast<const uint4*>(at);
@@ -328,8 +355,8 @@ struct RowsResult {
 
 template <bool kBF16, bool kScore>
 __device__ __attribute__((noinline)) RowsResult quantize_rows_exact(
-    const void* xv, int64_t row0, int nrows, int64_t K, int64_t blk, float s_t, double six_st,
-    uint8_t* codes, uint8_t* scales, uint32_t* slot) {
+    const void* xv, int64_t row0, int nrows, int64_t K, int64_t ldx, int64_t blk, float s_t,
+    double six_st, uint8_t* codes, uint8_t* scales, uint32_t* slot) {
   RowsResult res;
 #pragma unroll
   for (int j = 0; j < 16; ++j) res.acc[j] = 0.0f;
@@ -337,7 +364,7 @@ __device__ __attribute__((noinline)) RowsResult quantize_rows_exact(
   const int64_t nblk = K >> 4;
   for (int rr = 0; rr < nrows; ++rr) {
     RowBlock<kBF16> rb;
-    rb.load(xv, row0 + rr, K, blk);
+    rb.load(xv, row0 + rr, ldx, blk);
     uint32_t sc;
     uint2 cw;
     encode_block_exact<kBF16, kScore>(rb, s_t, six_st, sc, cw, res.acc, res.bad, slot);
@@ -354,8 +381,9 @@ __device__ __attribute__((noinline)) RowsResult quantize_rows_exact(
 // sum of the 8 wave sums, via LDS.
 template <bool kBF16, bool kScore>
 __global__ __launch_bounds__(512, 2) void k_quantize(
-    const void* __restrict__ xv, int64_t rows, int64_t K, const uint32_t* __restrict__ amax_partial,
-    int n_partial, const float* __restrict__ amax_in, uint8_t* __restrict__ codes,
+    const void* __restrict__ xv, int64_t rows, int64_t K, int64_t ldx,
+    const uint32_t* __restrict__ amax_partial, int n_partial, const float* __restrict__ amax_in,
+    uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tensor_scale,
     float* __restrict__ chunk_partial, uint32_t* __restrict__ status) {
   __shared__ float s_part[kScore ? 8 * kQCols : 1];
@@ -375,9 +403,9 @@ __global__ __launch_bounds__(512, 2) void k_quantize(
   // first rows in flight before the tensor amax is known
   RowBlock<kBF16> b0, b1, b2;
   if (active && nrows > 0) {
-    b0.load(xv, row0, K, blk);
-    b1.load(xv, min(row0 + 1, last), K, blk);
-    b2.load(xv, min(row0 + 2, last), K, blk);
+    b0.load(xv, row0, ldx, blk);
+    b1.load(xv, min(row0 + 1, last), ldx, blk);
+    b2.load(xv, min(row0 + 2, last), ldx, blk);
   }
 
   {
@@ -418,16 +446,16 @@ __global__ __launch_bounds__(512, 2) void k_quantize(
   uint32_t bad = 0;
 
   if (active && !fast) {
-    const RowsResult res = quantize_rows_exact<kBF16, kScore>(xv, row0, nrows, K, blk, s_t, six_st,
-                                                              codes, scales, slot);
+    const RowsResult res = quantize_rows_exact<kBF16, kScore>(xv, row0, nrows, K, ldx, blk, s_t,
+                                                              six_st, codes, scales, slot);
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = res.acc[j];
     bad = res.bad;
   } else if (active && nrows > 0) {
     // Row addresses advance by adds (no 64-bit multiply per row); refills
     // past the sub-chunk's last row are clamped to it.
-    const int64_t xrow = K * (kBF16 ? 2 : 4), crow = K >> 1;
-    const char* xp = static_cast<const char*>(xv) + (row0 * K + blk * 16) * (kBF16 ? 2 : 4);
+    const int64_t xrow = ldx * (kBF16 ? 2 : 4), crow = K >> 1;
+    const char* xp = static_cast<const char*>(xv) + (row0 * ldx + blk * 16) * (kBF16 ? 2 : 4);
     const char* const xlast = xp + (last - row0) * xrow;
     uint8_t* cp = codes + row0 * crow + blk * 8;
     uint8_t* sp = scales + row0 * nblk + blk;
@@ -621,7 +649,8 @@ __global__ __launch_bounds__(256) void k_score_reduce(const float* __restrict__ 
 // record (no requantization): same order as k_quantize.
 template <bool kBF16>
 __global__ __launch_bounds__(512) void k_resid_partials(const void* __restrict__ xv, int64_t rows,
-                                                       int64_t K, const uint8_t* __restrict__ codes,
+                                                       int64_t K, int64_t ldx,
+                                                       const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ scales,
                                                        const float* __restrict__ tensor_scale,
                                                        float* __restrict__ chunk_partial) {
@@ -644,8 +673,8 @@ __global__ __launch_bounds__(512) void k_resid_partials(const void* __restrict__
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int64_t c = blk * 16 + j;
-        const float xj = kBF16 ? bf16_to_f32(static_cast<const uint16_t*>(xv)[r * K + c])
-                               : static_cast<const float*>(xv)[r * K + c];
+        const float xj = kBF16 ? bf16_to_f32(static_cast<const uint16_t*>(xv)[r * ldx + c])
+                               : static_cast<const float*>(xv)[r * ldx + c];
         const uint32_t nib = (cw[j >> 3] >> (4 * (j & 7))) & 7u;
         const float v = (e2m1_mag(nib) * s_b) * s_t;
         acc[j] += fabsf(fabsf(xj) - v);
@@ -843,7 +872,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_radix(const float* __rest
 // resid[m, j] = bf16(fl32(x[m, idx[j]] - v[m, idx[j]])).
 template <bool kBF16>
 __global__ __launch_bounds__(256) void k_resid_gather(const void* __restrict__ xv, int64_t rows,
-                                                     int64_t K, const uint8_t* __restrict__ codes,
+                                                     int64_t K, int64_t ldx,
+                                                     const uint8_t* __restrict__ codes,
                                                      const uint8_t* __restrict__ scales,
                                                      const float* __restrict__ tensor_scale,
                                                      const int32_t* __restrict__ idx, int k,
@@ -852,8 +882,8 @@ __global__ __launch_bounds__(256) void k_resid_gather(const void* __restrict__ x
   if (i >= rows * k) return;
   const int64_t m = i / k;
   const int64_t c = idx[i - m * k];
-  const float xj = kBF16 ? bf16_to_f32(static_cast<const uint16_t*>(xv)[m * K + c])
-                         : static_cast<const float*>(xv)[m * K + c];
+  const float xj = kBF16 ? bf16_to_f32(static_cast<const uint16_t*>(xv)[m * ldx + c])
+                         : static_cast<const float*>(xv)[m * ldx + c];
   const uint32_t byte = codes[m * (K >> 1) + (c >> 1)];
   const uint32_t nib = (c & 1) ? (byte >> 4) : (byte & 15u);
   const uint32_t mi = nib & 7u;
@@ -925,7 +955,7 @@ QuantLayout quant_layout(void* ws, int64_t batch, int64_t rows, int64_t K, int x
   const int64_t elem_bytes = (x_dtype == NVQ_BF16) ? 2 : 4;
   const int64_t vec_per_item = rows * K * elem_bytes / 16;
   L.nwg = amax_wg_per_item(batch, vec_per_item);
-  L.n_partial = L.nwg;
+  L.n_partial = L.nwg * kAmaxWaves;
   L.nchunks = (rows + kQRows - 1) / kQRows;
   WsCarve c(ws);
   L.amax_partial = c.take<uint32_t>((size_t)batch * L.n_partial);
@@ -969,14 +999,17 @@ extern "C" size_t nvfp4_quantize_workspace_bytes(int64_t batch, int64_t rows, in
 }
 
 extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t rows, int64_t K,
-                              const float* amax_in, uint8_t* codes, uint8_t* scales,
+                              int64_t ldx, const float* amax_in, uint8_t* codes, uint8_t* scales,
                               float* tensor_scale, float* chan_score, void* ws, size_t ws_bytes,
                               void* stream) {
   if (!tensor_scale || !ws || (rows != 0 && (!x || !codes || !scales))) return NVQ_EINVAL;
   if (x_dtype != NVQ_F32 && x_dtype != NVQ_BF16) return NVQ_EINVAL;
   if (batch <= 0 || batch > 65535 || rows < 0 || K <= 0 || (K & 15)) return NVQ_ESHAPE;
+  if (ldx == 0) ldx = K;
+  if (ldx < K) return NVQ_ESHAPE;
   if (chan_score && batch != 1) return NVQ_ESHAPE;
-  if (!aligned16(x) || ((uintptr_t)codes & 7u)) return NVQ_EALIGN;
+  const int64_t eb = (x_dtype == NVQ_BF16) ? 2 : 4;
+  if (!aligned16(x) || ((uintptr_t)codes & 7u) || (ldx * eb) % 16) return NVQ_EALIGN;
   if (!aligned256(ws)) return NVQ_EALIGN;
   QuantLayout L = quant_layout(ws, batch, rows, K, x_dtype);
   if (ws_bytes < L.bytes) return NVQ_EWORKSPACE;
@@ -989,20 +1022,33 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
     return last_launch();
   }
   if (!amax_in) {
-    const int64_t vec_per_item = rows * K * (bf16 ? 2 : 4) / 16;
     dim3 grid(L.nwg, (unsigned)batch);
-    if (bf16)
-      hipLaunchKernelGGL(k_amax<true>, grid, dim3(kAmaxThreads), 0, s,
-                         static_cast<const uint4*>(x), vec_per_item, L.nwg, L.amax_partial, L.status);
-    else
-      hipLaunchKernelGGL(k_amax<false>, grid, dim3(kAmaxThreads), 0, s,
-                         static_cast<const uint4*>(x), vec_per_item, L.nwg, L.amax_partial, L.status);
+    const uint4* xv = static_cast<const uint4*>(x);
+    if (ldx == K) {
+      const int64_t vec_per_item = rows * K * eb / 16;
+      if (bf16)
+        hipLaunchKernelGGL(k_amax<true>, grid, dim3(kAmaxThreads), 0, s, xv, vec_per_item, L.nwg,
+                           L.amax_partial, L.status);
+      else
+        hipLaunchKernelGGL(k_amax<false>, grid, dim3(kAmaxThreads), 0, s, xv, vec_per_item, L.nwg,
+                           L.amax_partial, L.status);
+    } else {
+      const int64_t vpr = K * eb / 16, ldv = ldx * eb / 16;
+      if (bf16)
+        hipLaunchKernelGGL(k_amax_rows<true>, grid, dim3(kAmaxThreads), 0, s, xv, rows, vpr, ldv,
+                           L.nwg, L.amax_partial, L.status);
+      else
+        hipLaunchKernelGGL(k_amax_rows<false>, grid, dim3(kAmaxThreads), 0, s, xv, rows, vpr, ldv,
+                           L.nwg, L.amax_partial, L.status);
+    }
   } else {
     hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, s, L.status);
   }
   if (int rc = last_launch()) return rc;
   const bool score = chan_score != nullptr;
-  if (!score) {
+  // The flat score-free kernel walks the item as one run of blocks, so it
+  // takes dense tensors only; row-strided ones go through the row tile.
+  if (!score && ldx == K) {
     const int64_t nb_item = rows * (K / 16);
     const int64_t per_wg = (int64_t)kFlatThreads * kFlatBlocksPerThread;
     const int64_t nwg = std::min<int64_t>(std::max<int64_t>(1, (nb_item + per_wg - 1) / per_wg), 65535);
@@ -1018,7 +1064,7 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
   dim3 grid((unsigned)((K / 16 + kQBlocksPerWave - 1) / kQBlocksPerWave), (unsigned)L.nchunks,
             (unsigned)batch);
 #define NVQ_LAUNCH_Q(B, S)                                                                    \
-  hipLaunchKernelGGL((k_quantize<B, S>), grid, dim3(512), 0, s, x, rows, K, L.amax_partial, \
+  hipLaunchKernelGGL((k_quantize<B, S>), grid, dim3(512), 0, s, x, rows, K, ldx, L.amax_partial, \
                      L.n_partial, amax_in, codes, scales, tensor_scale, L.chunk_partial, L.status)
   if (bf16) {
     if (score) NVQ_LAUNCH_Q(true, true); else NVQ_LAUNCH_Q(true, false);
@@ -1065,13 +1111,15 @@ extern "C" size_t residual_topk_workspace_bytes(int64_t rows, int64_t K, int32_t
 }
 
 extern "C" int residual_topk_channels(const void* x, int x_dtype, int64_t rows, int64_t K,
-                                      const uint8_t* codes, const uint8_t* scales,
+                                      int64_t ldx, const uint8_t* codes, const uint8_t* scales,
                                       const float* tensor_scale, const float* scores_in,
                                       float* scores_out, int32_t k, int32_t* idx_out,
                                       uint16_t* resid_out, void* ws, size_t ws_bytes,
                                       void* stream) {
   if (x_dtype != NVQ_F32 && x_dtype != NVQ_BF16) return NVQ_EINVAL;
   if (rows < 0 || K <= 0 || (K & 15) || k < 0 || k > K) return NVQ_ESHAPE;
+  if (ldx == 0) ldx = K;
+  if (ldx < K) return NVQ_ESHAPE;
   if (k > 0 && !idx_out) return NVQ_EINVAL;
   if (!ws || !aligned256(ws)) return ws ? NVQ_EALIGN : NVQ_EINVAL;
   const bool need_record = !scores_in || resid_out;
@@ -1089,10 +1137,10 @@ extern "C" int residual_topk_channels(const void* x, int x_dtype, int64_t rows, 
     if (rows > 0) {
       dim3 grid((unsigned)((K / 16 + kQBlocksPerWave - 1) / kQBlocksPerWave), (unsigned)nchunks);
       if (bf16)
-        hipLaunchKernelGGL(k_resid_partials<true>, grid, dim3(512), 0, s, x, rows, K, codes, scales,
-                           tensor_scale, chunk_partial);
+        hipLaunchKernelGGL(k_resid_partials<true>, grid, dim3(512), 0, s, x, rows, K, ldx, codes,
+                           scales, tensor_scale, chunk_partial);
       else
-        hipLaunchKernelGGL(k_resid_partials<false>, grid, dim3(512), 0, s, x, rows, K, codes,
+        hipLaunchKernelGGL(k_resid_partials<false>, grid, dim3(512), 0, s, x, rows, K, ldx, codes,
                            scales, tensor_scale, chunk_partial);
       if (int rc = last_launch()) return rc;
     }
@@ -1110,11 +1158,11 @@ extern "C" int residual_topk_channels(const void* x, int x_dtype, int64_t rows, 
     const int64_t n = rows * k;
     dim3 grid((unsigned)((n + 255) / 256));
     if (bf16)
-      hipLaunchKernelGGL(k_resid_gather<true>, grid, dim3(256), 0, s, x, rows, K, codes, scales,
-                         tensor_scale, idx_out, (int)k, resid_out);
+      hipLaunchKernelGGL(k_resid_gather<true>, grid, dim3(256), 0, s, x, rows, K, ldx, codes,
+                         scales, tensor_scale, idx_out, (int)k, resid_out);
     else
-      hipLaunchKernelGGL(k_resid_gather<false>, grid, dim3(256), 0, s, x, rows, K, codes, scales,
-                         tensor_scale, idx_out, (int)k, resid_out);
+      hipLaunchKernelGGL(k_resid_gather<false>, grid, dim3(256), 0, s, x, rows, K, ldx, codes,
+                         scales, tensor_scale, idx_out, (int)k, resid_out);
     return last_launch();
   }
   return NVQ_OK;

@@ -64,7 +64,7 @@ _SIGS = [
     ("nvq_device_status", ctypes.c_int, [_P, _P, ctypes.POINTER(ctypes.c_uint32)]),
     ("nvfp4_quantize_workspace_bytes", _SZ, [_I64, _I64, _I64]),
     ("nvfp4_quantize", ctypes.c_int,
-     [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+     [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("nvfp4_dequantize", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P]),
     ("nvfp4_guidance_record", ctypes.c_int,
      [_P, ctypes.c_int, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
@@ -72,7 +72,7 @@ _SIGS = [
      [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, ctypes.c_int, _P, _P, _SZ, _P]),
     ("residual_topk_workspace_bytes", _SZ, [_I64, _I64, _I32]),
     ("residual_topk_channels", ctypes.c_int,
-     [_P, ctypes.c_int, _I64, _I64, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
+     [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     ("nvq_moe_route", ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     ("nvq_moe_permute_workspace_bytes", _SZ, [_I64, _I64, _I64]),
     ("nvq_moe_permute", ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
@@ -135,6 +135,25 @@ def _dev(t, name):
     return t
 
 
+def _dev_rows(t, name):
+    """A GPU tensor whose rows may be strided: [rows, K] or [batch, rows, K]
+    with unit element stride and (for 3-D) items rows * ldx elements apart.
+    Returns ldx, the row stride in elements."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() not in (2, 3) or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be [rows, K] or [batch, rows, K] with unit column stride")
+    rows, K = t.shape[-2], t.shape[-1]
+    many = t.dim() == 3 and t.shape[0] > 1
+    if rows > 1:
+        ldx = t.stride(-2)
+    else:  # one row per item: the item stride is the row stride
+        ldx = t.stride(0) if many else K
+    if many and t.stride(0) != rows * ldx:
+        raise ValueError(f"{name}: batch items must be rows * ldx elements apart")
+    return ldx
+
+
 def _dtype_code(t):
     if t.dtype == torch.float32:
         return NVQ_F32
@@ -155,11 +174,12 @@ def device_status(ws: torch.Tensor) -> int:
 
 # ----------------------------------------------------------------- quantize --
 def nvfp4_quantize(x, amax_in=None, score=False, ws=None, out=None):
-    """NVFP4-quantize x [rows, K] or [batch, rows, K] (fp32/bf16).
+    """NVFP4-quantize x [rows, K] or [batch, rows, K] (fp32/bf16); rows may be
+    strided (a column slice of a wider tensor).
 
     Returns (codes u8 [..., K/2], scales u8 [..., K/16], tensor_scale f32 [batch],
     score f32 [K] or None, ws)."""
-    _dev(x, "x")
+    ldx = _dev_rows(x, "x")
     L = load()
     batch, rows, K = (1, *x.shape) if x.dim() == 2 else tuple(x.shape)
     lead = x.shape[:-1]
@@ -174,8 +194,9 @@ def nvfp4_quantize(x, amax_in=None, score=False, ws=None, out=None):
         ws = workspace(L.nvfp4_quantize_workspace_bytes(batch, rows, K), x.device)
     if amax_in is not None:
         _dev(amax_in, "amax_in")
-    rc = L.nvfp4_quantize(_ptr(x), _dtype_code(x), batch, rows, K, _ptr(amax_in), _ptr(codes),
-                          _ptr(scales), _ptr(st), _ptr(sc), _ptr(ws), ws.numel(), _stream())
+    rc = L.nvfp4_quantize(_ptr(x), _dtype_code(x), batch, rows, K, ldx, _ptr(amax_in),
+                          _ptr(codes), _ptr(scales), _ptr(st), _ptr(sc), _ptr(ws), ws.numel(),
+                          _stream())
     _check("nvfp4_quantize", rc)
     return codes, scales, st, sc, ws
 
@@ -236,8 +257,9 @@ def nvfp4_guided_quantize(w, bits, scales, tensor_scale, mode, ws=None, out=None
 
 def residual_topk_channels(x, codes, scales, tensor_scale, k, scores=None, want_scores=False,
                            want_resid=True, ws=None):
-    """Returns (idx int32 [k], resid bf16 [rows, k] or None, scores f32 [K] or None)."""
-    _dev(x, "x")
+    """Returns (idx int32 [k], resid bf16 [rows, k] or None, scores f32 [K] or None).
+    x [rows, K] may have strided rows."""
+    ldx = _dev_rows(x, "x")
     L = load()
     rows, K = x.shape
     idx = torch.empty(max(k, 1), dtype=torch.int32, device=x.device)
@@ -245,7 +267,7 @@ def residual_topk_channels(x, codes, scales, tensor_scale, k, scores=None, want_
     sc_out = torch.empty(K, dtype=torch.float32, device=x.device) if want_scores else None
     if ws is None:
         ws = workspace(L.residual_topk_workspace_bytes(rows, K, k), x.device)
-    rc = L.residual_topk_channels(_ptr(x), _dtype_code(x), rows, K, _ptr(codes), _ptr(scales),
+    rc = L.residual_topk_channels(_ptr(x), _dtype_code(x), rows, K, ldx, _ptr(codes), _ptr(scales),
                                   _ptr(tensor_scale), _ptr(scores), _ptr(sc_out), k, _ptr(idx),
                                   _ptr(resid), _ptr(ws), ws.numel(), _stream())
     _check("residual_topk_channels", rc)

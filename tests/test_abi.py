@@ -54,25 +54,37 @@ def test_host_side_validation_launches_nothing():
     assert L.nvfp4_channel_major(fake, fake, 1, 24, 32, fake, fake, None) == -2
     assert L.nvfp4_channel_major(P(0x1004), fake, 1, 32, 32, fake, fake, None) == -3
     # null x
-    assert L.nvfp4_quantize(None, 1, 1, 4, 32, None, fake, fake, fake, None, fake, 1 << 20, None) == -1
+    assert L.nvfp4_quantize(None, 1, 1, 4, 32, 0, None, fake, fake, fake, None, fake, 1 << 20,
+                            None) == -1
     # K not a multiple of 16
-    assert L.nvfp4_quantize(fake, 1, 1, 4, 24, None, fake, fake, fake, None, fake, 1 << 20, None) == -2
+    assert L.nvfp4_quantize(fake, 1, 1, 4, 24, 0, None, fake, fake, fake, None, fake, 1 << 20,
+                            None) == -2
     # bad dtype
-    assert L.nvfp4_quantize(fake, 7, 1, 4, 32, None, fake, fake, fake, None, fake, 1 << 20, None) == -1
+    assert L.nvfp4_quantize(fake, 7, 1, 4, 32, 0, None, fake, fake, fake, None, fake, 1 << 20,
+                            None) == -1
     # misaligned x
-    assert L.nvfp4_quantize(P(0x1002), 1, 1, 4, 32, None, fake, fake, fake, None, fake, 1 << 20,
+    assert L.nvfp4_quantize(P(0x1002), 1, 1, 4, 32, 0, None, fake, fake, fake, None, fake, 1 << 20,
+                            None) == -3
+    # row stride: shorter than a row, or rows not 16-byte aligned (bf16: ldx % 8)
+    assert L.nvfp4_quantize(fake, 1, 1, 4, 32, 16, None, fake, fake, fake, None, fake, 1 << 20,
+                            None) == -2
+    assert L.nvfp4_quantize(fake, 1, 1, 4, 32, 36, None, fake, fake, fake, None, fake, 1 << 20,
+                            None) == -3
+    assert L.nvfp4_quantize(fake, 0, 1, 4, 32, 34, None, fake, fake, fake, None, fake, 1 << 20,
                             None) == -3
     # workspace too small
     need = L.nvfp4_quantize_workspace_bytes(1, 4, 32)
     assert need >= 256
-    assert L.nvfp4_quantize(fake, 1, 1, 4, 32, None, fake, fake, fake, None, fake, need - 1,
+    assert L.nvfp4_quantize(fake, 1, 1, 4, 32, 0, None, fake, fake, fake, None, fake, need - 1,
                             None) == -4
     # scores need batch == 1
-    assert L.nvfp4_quantize(fake, 1, 2, 4, 32, None, fake, fake, fake, fake, fake, 1 << 20,
+    assert L.nvfp4_quantize(fake, 1, 2, 4, 32, 0, None, fake, fake, fake, fake, fake, 1 << 20,
                             None) == -2
-    # k > K
-    assert L.residual_topk_channels(fake, 1, 4, 32, fake, fake, fake, None, None, 33, fake, None,
+    # k > K; row stride shorter than a row
+    assert L.residual_topk_channels(fake, 1, 4, 32, 0, fake, fake, fake, None, None, 33, fake, None,
                                     fake, 1 << 20, None) == -2
+    assert L.residual_topk_channels(fake, 1, 4, 32, 31, fake, fake, fake, None, None, 3, fake,
+                                    None, fake, 1 << 20, None) == -2
     # route: topk > E, E too large
     assert L.nvq_moe_route(fake, 4, 8, 9, fake, fake, None) == -2
     assert L.nvq_moe_route(fake, 4, 2048, 8, fake, fake, None) == -2

@@ -193,65 +193,98 @@ def test_forward_uses_the_cached_rounding():
               np.linalg.norm(W, axis=1), "fwd vs dense on dequantized cache")
 
 
-def test_qat_layer_full_size_sampled():
-    """Trainer QAT layer at full size (T=16384, H=4096, E=128, I=1536, top-8):
-    gate/up forward, input and weight gradients on sampled outputs."""
+@pytest.mark.parametrize("proj,guided", [("gu", False), ("gu", True), ("dn", True)])
+def test_qat_layer_full_size_sampled(proj, guided):
+    """Trainer QAT layer at full size (T=16384, H=4096, E=128, I=1536, top-8,
+    P=131072) in the benchmark's launch configuration: forward, input and
+    weight gradients of one projection on sampled outputs.  guided: the codes
+    are the drifted masters' codes rebuilt from the rollout's mantissa record
+    (what the benchmark's layer step runs); else the rollout's cached codes.
+    gate/up: K=4096, N=3072, x gathered by token; down: K=1536, N=4096, x in
+    sorted-pair order.  Rows: every 97th row of four experts plus each one's
+    first and last row."""
     import torch
 
     nvq = _nvq()
     s = inputs.QAT
-    log("[qat] full size: generating on device")
+    log(f"[qat] full size {proj} guided={guided}: generating on device")
     logits = inputs.logits(s)
     ids, _ = nvq.nvq_moe_route(to_gpu(logits), s.topk)
     sp, off, _, _ = nvq.nvq_moe_permute(ids, s.E)
-    a_row = (sp // s.topk).to(torch.int32).contiguous()
-    K, N = s.H, 2 * s.I
+    K, N = (s.H, 2 * s.I) if proj == "gu" else (s.I, s.H)
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(77)
-    x = torch.randn(s.T, K, generator=gen, device="cuda").to(torch.bfloat16)
+    gen.manual_seed(77 if proj == "gu" else 78)
+    if proj == "gu":
+        x = torch.randn(s.T, K, generator=gen, device="cuda").to(torch.bfloat16)
+        a_row = (sp // s.topk).to(torch.int32).contiguous()
+    else:
+        x = torch.randn(s.P, K, generator=gen, device="cuda").to(torch.bfloat16)
+        a_row = None
     dy = torch.randn(s.P, N, generator=gen, device="cuda").to(torch.bfloat16)
-    wm = inputs.weights_device(s, "gu")
+    wm = inputs.weights_device(s, proj)
     q = nvq.nvfp4_quantize(wm)
-    yb, yf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_FWD, *q[:3], off, s.P, x=x, a_row=a_row,
+    wd = None
+    if guided:
+        rec = nvq.nvfp4_guidance_record(q[0], nvq.NVQ_GUIDE_MANTISSA)
+        wd = inputs.drift_device(wm, s, proj)
+        codes = nvq.nvfp4_guided_quantize(wd, rec, q[1], q[2], nvq.NVQ_GUIDE_MANTISSA)
+        del rec
+    else:
+        codes = q[0]
+    rec_w = (codes, q[1], q[2])
+    yb, yf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_FWD, *rec_w, off, s.P, x=x, a_row=a_row,
                                          want_f32=True)
-    dxb, dxf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *q[:3], off, s.P, dy=dy, want_f32=True)
-    dw = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *q[:3], off, s.P, x=x, dy=dy, a_row=a_row)
+    dxb, dxf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *rec_w, off, s.P, dy=dy, want_f32=True)
+    dw = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *rec_w, off, s.P, x=x, dy=dy, a_row=a_row)
     torch.cuda.synchronize()
     offn = to_np(off)
-    row_tok = to_np(sp) // s.topk
+    x_of_row = to_np(sp) // s.topk if proj == "gu" else np.arange(s.P)
     xn = to_np(x)
-    for e in (0, 37, 127):
+    X = inputs.bf16_bits_to_f32(xn).astype(np.float64)
+    for e in (0, 37, 90, 127):
         rows = np.arange(offn[e], offn[e + 1])
         if rows.size == 0:
             continue
-        samp = rows[:: max(1, rows.size // 24)]
+        samp = np.unique(np.concatenate([rows[::97], rows[-1:]]))
+        # the oracle builds the record itself from the expert's master weights
         wmb = to_np(wm[e])
         oq = oracle.quantize(wmb)
-        assert_bits_equal(to_np(q[0][e]), oq[0], f"cache codes e={e}")
-        W = oracle.dequantize(*oq).astype(np.float64)
-        cols = np.arange(0, N, 97)
-        ref = oracle.qat_fwd(xn, row_tok[samp], np.zeros(samp.size, np.int32), oq[0], oq[1],
+        assert_bits_equal(to_np(q[0][e]), oq[0], f"{proj} cache codes e={e}")
+        assert float(to_np(q[2])[e]) == oq[2]
+        ocodes = oq[0]
+        if guided:
+            orec = oracle.guidance_record(oq[0], oq[1], oq[2], oracle.GUIDE_MANTISSA)
+            ocodes = oracle.guided_quantize(to_np(wd[e]), orec, oq[1], oq[2], oracle.GUIDE_MANTISSA)
+            assert_bits_equal(to_np(codes[e]), ocodes, f"{proj} guided codes e={e}")
+        W = oracle.dequantize(ocodes, oq[1], oq[2]).astype(np.float64)
+        cols = np.unique(np.concatenate([np.arange(0, N, 97), [N - 1]]))
+        ref = oracle.qat_fwd(xn, x_of_row[samp], np.zeros(samp.size, np.int32), ocodes, oq[1],
                              np.float32(oq[2]), cols=cols)
-        X = inputs.bf16_bits_to_f32(xn).astype(np.float64)
-        _norm_err(to_np(yf)[samp][:, cols], ref, np.linalg.norm(X[row_tok[samp]], axis=1),
-                  np.linalg.norm(W[cols], axis=1), f"full fwd e={e}")
+        _norm_err(to_np(yf)[samp][:, cols], ref, np.linalg.norm(X[x_of_row[samp]], axis=1),
+                  np.linalg.norm(W[cols], axis=1), f"full {proj} fwd e={e}")
         dyn = to_np(dy[samp])
-        cc = np.arange(0, K, 101)
-        refd = oracle.qat_dgrad(dyn, np.arange(samp.size), np.zeros(samp.size, np.int32), oq[0],
+        cc = np.unique(np.concatenate([np.arange(0, K, 31), [K - 1]]))
+        refd = oracle.qat_dgrad(dyn, np.arange(samp.size), np.zeros(samp.size, np.int32), ocodes,
                                 oq[1], np.float32(oq[2]), cols=cc)
         DY = inputs.bf16_bits_to_f32(dyn).astype(np.float64)
         _norm_err(to_np(dxf)[samp][:, cc], refd, np.linalg.norm(DY, axis=1),
-                  np.linalg.norm(W[:, cc], axis=0), f"full dgrad e={e}")
-        ns = np.arange(0, N, 211)
-        cs = np.arange(0, K, 223)
+                  np.linalg.norm(W[:, cc], axis=0), f"full {proj} dgrad e={e}")
+        ns = np.unique(np.concatenate([np.arange(0, N, 211), [N - 1]]))
+        cs = np.unique(np.concatenate([np.arange(0, K, 223), [K - 1]]))
         nn, ccw = np.meshgrid(ns, cs, indexing="ij")
         dye = to_np(dy[offn[e]:offn[e + 1]])
-        refw = oracle.qat_wgrad(dye, xn, row_tok[rows], 0, rows.size, nn.ravel(), ccw.ravel())
+        refw = oracle.qat_wgrad(dye, xn, x_of_row[rows], 0, rows.size, nn.ravel(), ccw.ravel())
         DYe = inputs.bf16_bits_to_f32(dye).astype(np.float64)
-        Xe = X[row_tok[rows]]
+        Xe = X[x_of_row[rows]]
         _norm_err(to_np(dw[e])[np.ix_(ns, cs)], refw.reshape(ns.size, cs.size),
                   np.linalg.norm(DYe[:, ns], axis=0), np.linalg.norm(Xe[:, cs], axis=0),
-                  f"full wgrad e={e}")
+                  f"full {proj} wgrad e={e}")
+    # the bf16 outputs are the fp32 ones rounded
+    rs = np.arange(0, s.P, 1013)
+    assert_bits_equal(to_np(yb[rs]), inputs.to_bf16_bits(to_np(yf[rs])), f"{proj} fwd bf16")
+    assert_bits_equal(to_np(dxb[rs]), inputs.to_bf16_bits(to_np(dxf[rs])), f"{proj} dgrad bf16")
+    del wm, wd, q, codes, dw, x, dy
+    torch.cuda.empty_cache()
 
 
 def test_qat_no_rows():

@@ -208,3 +208,55 @@ def test_quantize_no_rows(dtype):
         assert_bits_equal(to_np(st), np.array([ost], np.float32), f"s_t of no rows (amax {amax})")
         assert_bits_equal(to_np(score), oracle.residual_scores(np.zeros((0, K), np.float32), oc, osc, ost),
                           "scores of no rows")
+
+
+@pytest.mark.parametrize("rows,K,ldx,dtype", [(300, 272, 336, "bf16"), (129, 1040, 1044, "f32"),
+                                              (17, 16, 32, "bf16"), (1, 48, 64, "f32")])
+def test_row_strided_input(rows, K, ldx, dtype):
+    """x given as the first K columns of a wider [rows, ldx] tensor (row stride
+    ldx): the same record, scores, channels and residuals as the oracle on
+    those columns; the padding columns (filled with huge values) are never
+    read.  Also without a score (the strided score-free path) and stacked
+    [3, rows, K] items with their own tensor scales."""
+    import torch
+
+    nvq = _nvq()
+    g = np.random.default_rng(rows + K + ldx)
+    wide = (g.standard_t(4, (rows, ldx)) * np.exp(g.uniform(-3, 3, (1, ldx)))).astype(np.float32)
+    wide[:, K:] = np.float32(3e38)  # never part of the tensor
+    if dtype == "bf16":
+        wide = inputs.to_bf16_bits(wide)
+    log(f"[quant] strided {rows}x{K} ldx={ldx} {dtype}")
+    xg = to_gpu(wide)[:, :K]
+    assert xg.stride(0) == ldx and not xg.is_contiguous() or rows == 1
+    codes, scales, st, score, ws = nvq.nvfp4_quantize(xg, score=True)
+    k = min(7, K)
+    idx, resid, sc2 = nvq.residual_topk_channels(xg, codes, scales, st, k, want_scores=True)
+    c2, s2, st2, _, _ = nvq.nvfp4_quantize(xg)  # score-free
+    torch.cuda.synchronize()
+    oc, os_, ost = oracle.quantize(wide, K=K)
+    assert_bits_equal(to_np(st), np.array([ost], np.float32), "strided s_t")
+    assert_bits_equal(to_np(codes), oc, "strided codes")
+    assert_bits_equal(to_np(scales), os_, "strided scales")
+    assert_bits_equal(to_np(c2), oc, "strided codes (no score)")
+    assert_bits_equal(to_np(s2), os_, "strided scales (no score)")
+    assert_bits_equal(to_np(st2), np.array([ost], np.float32), "strided s_t (no score)")
+    osc = oracle.residual_scores(wide, oc, os_, ost, K=K)
+    assert_bits_equal(to_np(score), osc, "strided scores")
+    assert_bits_equal(to_np(sc2), osc, "strided scores (recomputed)")
+    oidx = oracle.topk(osc, k)
+    assert_bits_equal(to_np(idx), oidx, "strided topk")
+    assert_bits_equal(to_np(resid), oracle.residual_columns_bf16(wide, oc, os_, ost, oidx, K=K),
+                      "strided resid")
+    assert nvq.device_status(ws) == 0
+    # stacked items, each [rows, K] inside [rows, ldx]
+    items = np.stack([wide, wide[::-1].copy(), (wide.view(np.uint16) ^ 0x8000).view(wide.dtype)
+                      if dtype == "bf16" else -wide])
+    xb = to_gpu(items)[:, :, :K]
+    cb, sb, stb, _, _ = nvq.nvfp4_quantize(xb)
+    torch.cuda.synchronize()
+    for b in range(3):
+        oc, os_, ost = oracle.quantize(items[b], K=K)
+        assert_bits_equal(to_np(stb)[b:b + 1], np.array([ost], np.float32), f"item {b} s_t")
+        assert_bits_equal(to_np(cb)[b], oc, f"item {b} codes")
+        assert_bits_equal(to_np(sb)[b], os_, f"item {b} scales")

@@ -44,6 +44,46 @@ def test_residual_scores_follow_chunked_sequential_fp32_order():
     assert np.array_equal(gb, oracle.residual_scores(xf, *oracle.quantize(xf)))
 
 
+def test_residual_scores_chunk128_order_pinned_by_cumsum():
+    # the plainer order: one sequential fp32 sum per 128-row chunk, chunks in order
+    x = _x(3, 300, 64)
+    codes, scales, st = oracle.quantize(x)
+    r = np.abs(x - oracle.dequantize(codes, scales, st))
+
+    def seq(a):
+        return np.cumsum(a, axis=0, dtype=np.float32)[-1]
+
+    ref = seq(np.stack([seq(r[m0:m0 + 128]) for m0 in range(0, 300, 128)]))
+    got = oracle.residual_scores(x, codes, scales, st, order="chunk128")
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("workload", ["dense", "sweep", "decode_x", "prefill_x"])
+def test_score_order_choice_selects_the_same_channels(workload):
+    """The pages fix no summation order for the residual score.  On the
+    activations of every workload, the order the library computes (16-row
+    sub-chunks inside 128-row chunks) and a plain sequential sum per 128-row
+    chunk select the same top-k channels in the same rank order, and the two
+    scores differ by no more than the fp32 summation bound."""
+    if workload == "dense":
+        x, _, k = inputs.dense_check()
+    elif workload == "sweep":
+        x, k = inputs.quant_sweep(), 64
+    elif workload == "decode_x":
+        x, k = inputs.activations(inputs.DECODE), inputs.DECODE.k
+    else:
+        x, k = inputs.activations(inputs.PREFILL), inputs.PREFILL.k
+    codes, scales, st = oracle.quantize(x)
+    a = oracle.residual_scores(x, codes, scales, st, order="sub16")
+    b = oracle.residual_scores(x, codes, scales, st, order="chunk128")
+    assert np.array_equal(oracle.topk(a, k), oracle.topk(b, k))
+    # both are fp32 sums of the same M non-negative terms: each within
+    # (M - 1) u of the exact sum (relative), u = 2^-24
+    M = x.shape[0]
+    rel = np.abs(a.astype(np.float64) - b) / np.maximum(b.astype(np.float64), 1e-300)
+    assert rel.max() <= 2 * (M - 1) * 2.0 ** -24
+
+
 def test_residual_scores_zero_on_grid_and_golden_outlier():
     x = np.zeros((3, 16), np.float32)
     x[0, 0] = 2688.0  # s_t = 1
@@ -192,6 +232,48 @@ def test_moe_rows_pick_token_and_expert():
         np.testing.assert_array_equal(got[i], one[0, [7, 0, 2]])
 
 
+# Every finite non-negative bf16 value, ascending (bit patterns 0x0000..0x7F7F).
+_BF16_POS = (np.arange(0x7F80, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _bf16_nearest(v: float) -> int:
+    """bf16 bit pattern nearest the real number v (an fp64 value), ties to the
+    even pattern, by exact rational comparison of the two bracketing bf16
+    values; beyond the largest finite value, the IEEE overflow rule (at or
+    above max + half an ulp -> infinity)."""
+    a = abs(v)
+    sign = 0x8000 if np.signbit(v) else 0
+    big = Fraction(_BF16_POS[-1]) + Fraction(2) ** 119  # max + half ulp (ulp 2^120)
+    if Fraction(a) >= big:
+        return sign | 0x7F80
+    i = int(np.searchsorted(_BF16_POS, a, side="right")) - 1  # _BF16_POS[i] <= a
+    if i == len(_BF16_POS) - 1 or _BF16_POS[i] == a:
+        return sign | i
+    lo, hi = Fraction(_BF16_POS[i]), Fraction(_BF16_POS[i + 1])
+    d_lo, d_hi = Fraction(a) - lo, hi - Fraction(a)
+    pick = i if (d_lo < d_hi or (d_lo == d_hi and i % 2 == 0)) else i + 1
+    return sign | pick
+
+
+def test_double_to_bf16_rounds_once_to_nearest_even():
+    # ties, a value a double rounding through fp32 would get wrong, subnormals,
+    # the overflow threshold, signed zero, and random fp64 values
+    cases = [0.0, -0.0, 1.0, 1.0 + 2 ** -8, 1.0 + 2 ** -8 + 2 ** -40, 1.0 + 3 * 2 ** -8,
+             -(1.0 + 2 ** -8 + 2 ** -40), 2 ** -133, 2 ** -134, 3 * 2 ** -134, 2 ** -135,
+             2 ** -126 - 2 ** -134, 2 ** -126 - 2 ** -135, 3.3895313892515355e38,
+             float(_BF16_POS[-1]) + 2 ** 119, float(_BF16_POS[-1]) + 2 ** 119 - 2 ** 80, 1e300,
+             -1e-300, 1e-50]
+    g = np.random.default_rng(17)
+    cases += list(g.standard_normal(300) * np.exp2(g.integers(-140, 128, 300)))
+    cases += list(np.float64(g.standard_normal(200).astype(np.float32)) * (1 + 2.0 ** -30))
+    for v in cases:
+        assert oracle.double_to_bf16(v) == _bf16_nearest(v), v
+    # fp32 inputs agree with torch's fp32 -> bf16 rounding (one rounding either way)
+    f = g.standard_normal(1000).astype(np.float32)
+    tb = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert all(oracle.double_to_bf16(float(a)) == int(b) for a, b in zip(f, tb))
+
+
 def test_swiglu_closed_form():
     y = np.array([[0.0, 1.0, -3.0, 2.0, 5.0, 0.5],
                   [40.0, -40.0, 1e-3, 7.0, 7.0, -2.0]])
@@ -201,8 +283,7 @@ def test_swiglu_closed_form():
         for i in range(3):
             gte, up = y[r, i], y[r, 3 + i]
             ref = gte * up / (1.0 + math.exp(-gte))
-            refb = torch.tensor([ref], dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
-            assert h[r, i] == np.uint16(refb.numpy().view(np.uint16)[0])
+            assert h[r, i] == _bf16_nearest(ref)
 
 
 def test_combine_matches_numpy():
@@ -215,8 +296,8 @@ def test_combine_matches_numpy():
     got = oracle.combine_bf16(y, pos, w)
     ref = np.einsum("tj,tjn->tn", w.astype(np.float64),
                     y.astype(np.float64)[pos.reshape(T, topk)])
-    refb = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).view(torch.int16)
-    assert np.array_equal(got, refb.numpy().view(np.uint16))
+    refb = np.array([_bf16_nearest(v) for v in ref.ravel()], np.uint16).reshape(ref.shape)
+    assert np.array_equal(got, refb)
 
 
 def _qat_case(seed=8):
