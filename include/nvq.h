@@ -108,6 +108,25 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t rows, int6
                    float* tensor_scale, float* chan_score, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* Allocation-free variant of nvfp4_quantize, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, results
+ * and host-side errors as nvfp4_quantize, without ws / ws_bytes: the scratch
+ * memory (status word, amax partials, residual chunk partials) is a static
+ * array inside the library, NVQ_QUANTIZE_NOALLOC_SCRATCH_BYTES on every GPU
+ * the library runs on, held until the process ends.  A call whose scratch
+ * need (nvfp4_quantize_workspace_bytes(batch, rows, K)) exceeds it returns
+ * NVQ_EWORKSPACE and launches nothing.  The first call on a device looks up
+ * that device's array (hipGetSymbolAddress); no call allocates.  Every call on
+ * one GPU shares the array: calls that may overlap on one GPU (other streams,
+ * other host threads) race and must be ordered by the caller.  The device
+ * status word lives in the shared array and is not reported to the caller;
+ * use nvfp4_quantize when NVQ_STATUS_NONFINITE must be read. */
+#define NVQ_QUANTIZE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int nvfp4_quantize_noalloc(const void* x, int x_dtype, int64_t batch, int64_t rows, int64_t K,
+                           int64_t ldx, const float* amax_in, uint8_t* codes, uint8_t* scales,
+                           float* tensor_scale, float* chan_score, void* stream);
+
 /* NVFP4 dequantization: y = sign * fl32(fl32(G * s_b) * s_t), written as fp32
  * (y_dtype NVQ_F32) or rounded to nearest-even bf16 (NVQ_BF16).  This is the
  * quantize-dequantize image both sides use for the weights (QUADS §2.1).

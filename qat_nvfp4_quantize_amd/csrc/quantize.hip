@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "nvq.h"
 #include "nvq_device.h"
@@ -998,11 +999,14 @@ extern "C" size_t nvfp4_quantize_workspace_bytes(int64_t batch, int64_t rows, in
                   quant_layout(nullptr, batch, rows, K, NVQ_BF16).bytes);
 }
 
-extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t rows, int64_t K,
-                              int64_t ldx, const float* amax_in, uint8_t* codes, uint8_t* scales,
-                              float* tensor_scale, float* chan_score, void* ws, size_t ws_bytes,
-                              void* stream) {
-  if (!tensor_scale || !ws || (rows != 0 && (!x || !codes || !scales))) return NVQ_EINVAL;
+namespace nvq {
+namespace {
+// Host-side argument checks of nvfp4_quantize apart from the workspace (no
+// HIP call).  ldx == 0 becomes K.
+int quantize_check_args(const void* x, int x_dtype, int64_t batch, int64_t rows, int64_t K,
+                        int64_t& ldx, const uint8_t* codes, const uint8_t* scales,
+                        const float* tensor_scale, const float* chan_score) {
+  if (!tensor_scale || (rows != 0 && (!x || !codes || !scales))) return NVQ_EINVAL;
   if (x_dtype != NVQ_F32 && x_dtype != NVQ_BF16) return NVQ_EINVAL;
   if (batch <= 0 || batch > 65535 || rows < 0 || K <= 0 || (K & 15)) return NVQ_ESHAPE;
   if (ldx == 0) ldx = K;
@@ -1010,6 +1014,20 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
   if (chan_score && batch != 1) return NVQ_ESHAPE;
   const int64_t eb = (x_dtype == NVQ_BF16) ? 2 : 4;
   if (!aligned16(x) || ((uintptr_t)codes & 7u) || (ldx * eb) % 16) return NVQ_EALIGN;
+  return NVQ_OK;
+}
+}  // namespace
+}  // namespace nvq
+
+extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t rows, int64_t K,
+                              int64_t ldx, const float* amax_in, uint8_t* codes, uint8_t* scales,
+                              float* tensor_scale, float* chan_score, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!ws) return NVQ_EINVAL;
+  if (int rc = quantize_check_args(x, x_dtype, batch, rows, K, ldx, codes, scales, tensor_scale,
+                                   chan_score))
+    return rc;
+  const int64_t eb = (x_dtype == NVQ_BF16) ? 2 : 4;
   if (!aligned256(ws)) return NVQ_EALIGN;
   QuantLayout L = quant_layout(ws, batch, rows, K, x_dtype);
   if (ws_bytes < L.bytes) return NVQ_EWORKSPACE;
@@ -1079,6 +1097,52 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
     return last_launch();
   }
   return NVQ_OK;
+}
+
+// ------------------------------------------------------------------------
+// Allocation-free variant of nvfp4_quantize.  Its scratch (status word, amax
+// partials, residual chunk partials) is a file-scope device array: every GPU
+// the library runs on holds one copy of kQuantScratchBytes until the process
+// ends, and every call on that GPU shares it.  In host code `nvq_quant_scratch`
+// names a host-side stand-in, so its device address is taken once per device
+// with hipGetSymbolAddress and only that address reaches the kernels.
+constexpr size_t kQuantScratchBytes = NVQ_QUANTIZE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char nvq_quant_scratch[kQuantScratchBytes];
+
+namespace nvq {
+namespace {
+constexpr int kScratchMaxDevices = 64;
+std::atomic<void*> g_quant_scratch[kScratchMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the
+// first call on each device; a racing second lookup stores the same value).
+int quant_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NVQ_EHIP;
+  if (dev < 0 || dev >= kScratchMaxDevices) return NVQ_EUNSUPPORTED;
+  void* p = g_quant_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(nvq_quant_scratch)) != hipSuccess || !p) return NVQ_EHIP;
+    g_quant_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return NVQ_OK;
+}
+}  // namespace
+}  // namespace nvq
+
+extern "C" int nvfp4_quantize_noalloc(const void* x, int x_dtype, int64_t batch, int64_t rows,
+                                      int64_t K, int64_t ldx, const float* amax_in, uint8_t* codes,
+                                      uint8_t* scales, float* tensor_scale, float* chan_score,
+                                      void* stream) {
+  if (int rc = quantize_check_args(x, x_dtype, batch, rows, K, ldx, codes, scales, tensor_scale,
+                                   chan_score))
+    return rc;
+  if (nvfp4_quantize_workspace_bytes(batch, rows, K) > kQuantScratchBytes) return NVQ_EWORKSPACE;
+  void* ws = nullptr;
+  if (int rc = quant_scratch(&ws)) return rc;
+  return nvfp4_quantize(x, x_dtype, batch, rows, K, ldx, amax_in, codes, scales, tensor_scale,
+                        chan_score, ws, kQuantScratchBytes, stream);
 }
 
 extern "C" int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,

@@ -65,6 +65,8 @@ _SIGS = [
     ("nvfp4_quantize_workspace_bytes", _SZ, [_I64, _I64, _I64]),
     ("nvfp4_quantize", ctypes.c_int,
      [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    ("nvfp4_quantize_noalloc", ctypes.c_int,
+     [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     ("nvfp4_dequantize", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P]),
     ("nvfp4_guidance_record", ctypes.c_int,
      [_P, ctypes.c_int, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
@@ -199,6 +201,32 @@ def nvfp4_quantize(x, amax_in=None, score=False, ws=None, out=None):
                           _stream())
     _check("nvfp4_quantize", rc)
     return codes, scales, st, sc, ws
+
+
+NVQ_QUANTIZE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def nvfp4_quantize_noalloc(x, amax_in=None, score=False, out=None):
+    """nvfp4_quantize without a workspace: the library's static per-device
+    scratch serves the call (calls on one GPU must not overlap).  Returns
+    (codes, scales, tensor_scale, score or None)."""
+    ldx = _dev_rows(x, "x")
+    batch, rows, K = (1, *x.shape) if x.dim() == 2 else tuple(x.shape)
+    lead = x.shape[:-1]
+    if out is None:
+        codes = torch.empty(*lead, K // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(*lead, K // 16, dtype=torch.uint8, device=x.device)
+        st = torch.empty(batch, dtype=torch.float32, device=x.device)
+        sc = torch.empty(K, dtype=torch.float32, device=x.device) if score else None
+    else:
+        codes, scales, st, sc = out
+    if amax_in is not None:
+        _dev(amax_in, "amax_in")
+    rc = load().nvfp4_quantize_noalloc(_ptr(x), _dtype_code(x), batch, rows, K, ldx,
+                                       _ptr(amax_in), _ptr(codes), _ptr(scales), _ptr(st),
+                                       _ptr(sc), _stream())
+    _check("nvfp4_quantize_noalloc", rc)
+    return codes, scales, st, sc
 
 
 def nvfp4_dequantize(codes, scales, tensor_scale, out_dtype=torch.float32, batch=None, out=None):
