@@ -101,6 +101,53 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4* __restrict__
   amax_store_wave<kBF16>(m, partial, nwg, status);
 }
 
+// Amax pass laid out like the quantize pass that follows it (one item, the
+// scored row tile): workgroup (bx, by) reads exactly the rows and block
+// columns that quantize workgroup (bx, by) will read, wave w its 16-row
+// sub-chunk, lane l its block column, but each wave walks its rows last to
+// first.  Workgroups go to the XCDs in the same round-robin order in both
+// launches, so the rows a quantize wave starts with are the ones its amax
+// wave read last and may still be in that XCD's L2.  Four rows in flight per
+// lane; one partial per wave.
+template <bool kBF16>
+__global__ __launch_bounds__(512) void k_amax_tiles(const void* __restrict__ xv, int64_t rows,
+                                                   int64_t K, int64_t ldx,
+                                                   uint32_t* __restrict__ partial,
+                                                   uint32_t* __restrict__ status) {
+  constexpr int kVec = kBF16 ? 2 : 4;  // 16-byte vectors per block
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t nblk = K >> 4;
+  const int64_t blk = (int64_t)blockIdx.x * kQBlocksPerWave + lane;
+  const int64_t r0 = (int64_t)blockIdx.y * kQRows + wave * kQSub;
+  const int nrows = (int)max<int64_t>(0, min<int64_t>(kQSub, rows - r0));
+  uint32_t m = 0;
+  if (blk < nblk && nrows > 0) {
+    const int64_t xrow = ldx * (kBF16 ? 2 : 4);
+    const char* base = static_cast<const char*>(xv) + (r0 * ldx + blk * 16) * (kBF16 ? 2 : 4);
+    // rows nrows-1 .. 0 in groups of four; a group's rows past the sub-chunk
+    // are clamped to its row 0 (read, folded again, harmless for a max)
+#pragma unroll 1
+    for (int top = nrows - 1; top >= 0; top -= 4) {
+      uint4 v[4][kVec];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int rr = max(top - u, 0);
+        const uint4* p = reinterpret_cast<const uint4*>(base + rr * xrow);
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) v[u][q] = p[q];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) amax_fold<kBF16>(m, v[u][q]);
+    }
+  }
+  if (kBF16) m <<= 16;
+  m = wave_max_u32(m);
+  if (lane == 0) partial[((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 8 + wave] = m;
+  if (status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;
+}
+
 // Row-strided tensor: rows of vpr vectors, ldv vectors apart (item b starts
 // at row b * rows).  Wave w of workgroup g takes rows 4 g + w, 4 g + w +
 // 4 nwg, ...; its lanes stride along the row.
@@ -944,6 +991,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint2* __restrict__ codes
 struct QuantLayout {
   int nwg;        // pass-1 workgroups per item
   int n_partial;  // pass-1 wave partials per item
+  int64_t n_partial_tiles;  // partials of the tiled pass 1 (one item, scored)
   int64_t nchunks;
   size_t bytes;
   uint32_t* status;
@@ -958,8 +1006,12 @@ QuantLayout quant_layout(void* ws, int64_t batch, int64_t rows, int64_t K, int x
   L.nwg = amax_wg_per_item(batch, vec_per_item);
   L.n_partial = L.nwg * kAmaxWaves;
   L.nchunks = (rows + kQRows - 1) / kQRows;
+  // the tiled amax pass (one item with a score, at most 1024 quantize
+  // workgroups) writes one partial per wave of the quantize grid
+  L.n_partial_tiles = (int64_t)((K / 16 + kQBlocksPerWave - 1) / kQBlocksPerWave) * L.nchunks * 8;
   WsCarve c(ws);
-  L.amax_partial = c.take<uint32_t>((size_t)batch * L.n_partial);
+  L.amax_partial = c.take<uint32_t>((size_t)std::max<int64_t>(
+      (int64_t)batch * L.n_partial, std::min<int64_t>(L.n_partial_tiles, 1024 * 8)));
   L.chunk_partial = c.take<float>((size_t)L.nchunks * K);
   L.bytes = c.off;
   L.status = c.status();
@@ -1039,7 +1091,23 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
                        tensor_scale, chan_score, K, L.status);
     return last_launch();
   }
-  if (!amax_in) {
+  const bool score = chan_score != nullptr;
+  const dim3 qgrid((unsigned)((K / 16 + kQBlocksPerWave - 1) / kQBlocksPerWave), (unsigned)L.nchunks,
+                   (unsigned)batch);
+  int n_partial = L.n_partial;
+  // The tiled amax pass pays off when the whole quantize grid is resident at
+  // once (two 512-thread workgroups per CU), so both launches place workgroup
+  // i on the same XCD at about the same time; larger grids take the flat pass.
+  const int64_t qwgs = (int64_t)qgrid.x * qgrid.y;
+  if (!amax_in && score && qwgs <= 1024 && qwgs <= 2 * device_cu_count()) {
+    n_partial = (int)L.n_partial_tiles;
+    if (bf16)
+      hipLaunchKernelGGL(k_amax_tiles<true>, dim3(qgrid.x, qgrid.y), dim3(512), 0, s, x, rows, K, ldx,
+                         L.amax_partial, L.status);
+    else
+      hipLaunchKernelGGL(k_amax_tiles<false>, dim3(qgrid.x, qgrid.y), dim3(512), 0, s, x, rows, K, ldx,
+                         L.amax_partial, L.status);
+  } else if (!amax_in) {
     dim3 grid(L.nwg, (unsigned)batch);
     const uint4* xv = static_cast<const uint4*>(x);
     if (ldx == K) {
@@ -1063,7 +1131,6 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
     hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, s, L.status);
   }
   if (int rc = last_launch()) return rc;
-  const bool score = chan_score != nullptr;
   // The flat score-free kernel walks the item as one run of blocks, so it
   // takes dense tensors only; row-strided ones go through the row tile.
   if (!score && ldx == K) {
@@ -1079,11 +1146,9 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
                          L.amax_partial, L.n_partial, amax_in, codes, scales, tensor_scale, L.status);
     return last_launch();
   }
-  dim3 grid((unsigned)((K / 16 + kQBlocksPerWave - 1) / kQBlocksPerWave), (unsigned)L.nchunks,
-            (unsigned)batch);
 #define NVQ_LAUNCH_Q(B, S)                                                                    \
-  hipLaunchKernelGGL((k_quantize<B, S>), grid, dim3(512), 0, s, x, rows, K, ldx, L.amax_partial, \
-                     L.n_partial, amax_in, codes, scales, tensor_scale, L.chunk_partial, L.status)
+  hipLaunchKernelGGL((k_quantize<B, S>), qgrid, dim3(512), 0, s, x, rows, K, ldx, L.amax_partial, \
+                     n_partial, amax_in, codes, scales, tensor_scale, L.chunk_partial, L.status)
   if (bf16) {
     if (score) NVQ_LAUNCH_Q(true, true); else NVQ_LAUNCH_Q(true, false);
   } else {
