@@ -249,10 +249,12 @@ class MoeLeg:
             w_cm=self.wcm[proj], h_amax=self.h_amax if epi == nvq.NVQ_EPI_SWIGLU else None)
 
     def step(self, timer_, comp=True, path=0):
-        """path 0: the library's choice (exact fp16 dequantization); 2: the
-        FP8 block-product path, timed separately for the comparison."""
+        """path 0: the library's choice (exact fp16 dequantization, 128-row
+        tiles); 2: the FP8 block-product path; 3: the 256-row tiles; 2 and 3
+        are timed separately for the comparison."""
         nvq, s = self.nvq, self.s
-        tag = ("" if comp else "_k0") + ("_fp8blk" if path == nvq.NVQ_GEMM_FP8_BLOCK else "")
+        tag = ("" if comp else "_k0") + {nvq.NVQ_GEMM_FP8_BLOCK: "_fp8blk",
+                                          nvq.NVQ_GEMM_DEQ16_WIDE: "_wide"}.get(path, "")
         timer = lambda label, fn: timer_(self.name + "/" + label, fn)
         r = timer("route", lambda: nvq.nvq_moe_route(self.logits, s.topk))
         self.ids, self.w = r
@@ -373,6 +375,12 @@ class MoeLeg:
                                      "gemm_tflops": round(tf8, 1),
                                      "frac_fp8_mfma_peak": round(tf8 / FP8_PEAK_TFLOPS, 4),
                                      "time_vs_chosen_path": round((g8 + d8) / (gu + dn), 3)}
+        if "gemm_gu_wide" in timer.total:
+            gw, dw_ = timer.avg_ms("gemm_gu_wide"), timer.avg_ms("gemm_dn_wide")
+            tfw = (self.flops_gu + self.flops_dn) / ((gw + dw_) * 1e-3) / 1e12
+            out["path_deq16_wide"] = {"gemm_gu_ms": round(gw, 4), "gemm_dn_ms": round(dw_, 4),
+                                      "gemm_tflops": round(tfw, 1),
+                                      "time_vs_chosen_path": round((gw + dw_) / (gu + dn), 3)}
         if hasattr(self, "graph_ms"):
             out["layer_ms_graph"] = round(self.graph_ms, 4)
         return out
@@ -768,6 +776,9 @@ def main():
                 leg.step(timer, comp=False)
             for _ in range(2):
                 leg.step(timer, path=_nvq.NVQ_GEMM_FP8_BLOCK)
+            if leg.name == "moe_prefill":
+                for _ in range(2):
+                    leg.step(timer, path=_nvq.NVQ_GEMM_DEQ16_WIDE)
         if leg.name == "qat":
             for _ in range(3):
                 leg.symmetric(timer)

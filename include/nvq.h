@@ -281,12 +281,15 @@ int nvq_moe_combine_backward(const uint16_t* dout, const uint16_t* y, const int3
  * NVQ_EPI_SWIGLU writes h = bf16(silu(Y[:, :N/2]) * Y[:, N/2:]) [rows, N/2]
  * (out_f32, if given, still receives the full pre-activation Y).
  * Path NVQ_GEMM_DEQ16 (what NVQ_GEMM_AUTO selects) dequantizes each NVFP4 tile
- * exactly to fp16 and feeds fp16 MFMA; NVQ_GEMM_FP8_BLOCK runs one FP8 MFMA per
+ * exactly to fp16 and feeds fp16 MFMA, in 128-row tiles; NVQ_GEMM_DEQ16_WIDE
+ * is the same arithmetic in 256-row tiles with both operands dequantized once
+ * per workgroup (an evaluated alternative; slower here).  NVQ_GEMM_FP8_BLOCK
+ * runs one FP8 MFMA per
  * 16-element block on the raw E2M1 magnitudes and applies both block scales to
  * the block product in fp32 (the evaluated alternative; same result to
  * rounding, slower).  K % 128 == 0; k % 8 == 0. */
 enum { NVQ_EPI_NONE = 0, NVQ_EPI_SWIGLU = 1 };
-enum { NVQ_GEMM_AUTO = 0, NVQ_GEMM_DEQ16 = 1, NVQ_GEMM_FP8_BLOCK = 2 };
+enum { NVQ_GEMM_AUTO = 0, NVQ_GEMM_DEQ16 = 1, NVQ_GEMM_FP8_BLOCK = 2, NVQ_GEMM_DEQ16_WIDE = 3 };
 
 typedef struct nvq_moe_gemm_args {
   size_t struct_size;            /* sizeof(nvq_moe_gemm_args) */

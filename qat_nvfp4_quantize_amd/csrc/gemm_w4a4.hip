@@ -305,23 +305,24 @@ struct TileCtx {
   int e, nt;
   int64_t row0, row_end;
 };
+template <int kGM = kGroupM>
 __device__ __forceinline__ TileCtx tile_of_block(const GemmParams& p) {
   TileCtx c;
   c.valid = false;
   const int n_mt = min(*p.ntiles, p.max_tiles);
-  const int n_groups = (n_mt + kGroupM - 1) / kGroupM;
-  const int total = n_groups * kGroupM * p.n_tiles_n;
+  const int n_groups = (n_mt + kGM - 1) / kGM;
+  const int total = n_groups * kGM * p.n_tiles_n;
   const int per = (total + 7) / 8;
   const int slot = blockIdx.x >> 3;
   if (slot >= per) return c;
   const int logical = (blockIdx.x & 7) * per + slot;
   if (logical >= total) return c;
-  const int group_span = kGroupM * p.n_tiles_n;
+  const int group_span = kGM * p.n_tiles_n;
   const int grp = logical / group_span, rem = logical - grp * group_span;
-  const int mt = kGroupM * grp + (rem % kGroupM);
+  const int mt = kGM * grp + (rem % kGM);
   if (mt >= n_mt) return c;
   c.valid = true;
-  c.nt = rem / kGroupM;
+  c.nt = rem / kGM;
   c.e = p.tiles[2 * mt];
   c.row0 = p.tiles[2 * mt + 1];
   c.row_end = p.off[c.e + 1];
@@ -598,6 +599,242 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
   epilogue<kSwiglu>(p, c, acc);
 }
 
+// ------------------------------------------------ path DEQ16, wide tile --
+// For experts with many rows: workgroup = 8 waves (two per SIMD) over a
+// 256-row x 256-column tile; wave w owns rows 128 (w / 4) .. + 128 and
+// columns 64 (w % 4) .. + 64 (4 x 2 MFMA tiles, 128 accumulator registers,
+// as in the 128-row kernel).  K advances 64 elements per step.  Both operands
+// are dequantized once per workgroup into a double-buffered fp16 LDS tile:
+// thread t dequantizes half of A row t / 2 and half of B row t / 2 (one code
+// uint4 and two scale bytes each), so every weight element is dequantized
+// once per 256 rows, where the 128-row kernel dequantizes it once per wave
+// of 128 rows.  The raw FP4 stages are loaded two steps ahead; one barrier
+// per step.  LDS rows are 144 bytes (64 fp16 + 16 pad).  The compensation
+// runs as bf16 steps of 64 channels through the same tiles after the
+// tensor-scale multiply, as in the 128-row kernel.
+constexpr int W_THR = 512;
+constexpr int W_BM = 256;
+constexpr int W_SE = 64;
+constexpr int W_PITCH = 144;
+constexpr int kGroupMW = 4;  // 256-row tiles per group of the XCD-aware order
+
+struct WStage {
+  uint4 a;
+  uint32_t as;  // two scale bytes in the low half
+  uint4 b;
+  uint32_t bs;
+};
+
+template <int kSwiglu>
+__global__ __launch_bounds__(W_THR, 1) void k_moe_gemm_deq16w(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][W_BM][W_PITCH];  // [buf][A, B][row][byte]
+  const TileCtx c = tile_of_block<kGroupMW>(p);
+  if (!c.valid) return;
+  const int64_t K = p.K, N = p.N;
+  const int64_t Kh = K >> 1, Kb = K >> 4;
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int wr = wave >> 2, wc = wave & 3;  // wave's 128-row half and 64-column quarter
+
+  // loader: row lr = t / 2 of A and of B, half hf = t % 2 of each step
+  // (elements 32 hf .. 32 hf + 31); rows past the ends are clamped (loaded,
+  // never stored)
+  const int lr = t >> 1, hf = t & 1;
+  const int64_t a_tok = a_source_row(p, min<int64_t>(c.row0 + lr, c.row_end - 1));
+  const uint8_t* a_src = p.a_codes + a_tok * Kh + 16 * hf;
+  const uint8_t* a_ssrc = p.a_scales + a_tok * Kb + 2 * hf;
+  const int64_t bn = min<int64_t>(b_row_to_n(lr, c.nt, kSwiglu, N), N - 1);
+  const uint8_t* b_src = p.w_codes + ((int64_t)c.e * N + bn) * Kh + 16 * hf;
+  const uint8_t* b_ssrc = p.w_scales + ((int64_t)c.e * N + bn) * Kb + 2 * hf;
+  const int nst = (int)(K / W_SE);  // even: K % 128 == 0
+
+  auto gload = [&](WStage& S, int step) {
+    const int64_t sc = min(step, nst - 1);  // past the end: a valid step, zero-scaled later
+    S.a = *reinterpret_cast<const uint4*>(a_src + sc * 32);
+    S.as = *reinterpret_cast<const uint16_t*>(a_ssrc + sc * 4);
+    S.b = *reinterpret_cast<const uint4*>(b_src + sc * 32);
+    S.bs = *reinterpret_cast<const uint16_t*>(b_ssrc + sc * 4);
+  };
+  auto dw = [](const uint4& v, int d) { return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w; };
+  // this thread's halves of A and B rows lr -> exact fp16 in buffer buf;
+  // live == false (a step past K) writes zeros
+  auto stage_store = [&](const WStage& S, int buf, bool live) {
+    uint8_t* da = &lds[buf][0][lr][64 * hf];
+    uint8_t* db = &lds[buf][1][lr][64 * hf];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t pa = live ? scale_pair(S.as, d >> 1) : 0u;
+      const uint32_t pb = live ? scale_pair(S.bs, d >> 1) : 0u;
+      *reinterpret_cast<half8_t*>(da + 16 * d) = dequant8(dw(S.a, d), pa);
+      *reinterpret_cast<half8_t*>(db + 16 * d) = dequant8(dw(S.b, d), pb);
+    }
+  };
+
+  floatx16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // one step: 4 sub-steps of 16 elements; lane half h takes elements
+  // 16 d + 8 h .. + 7 of A rows 128 wr + 32 i + l32 and B rows
+  // 64 wc + 32 j + l32
+  auto mfma_step = [&](int buf) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      half8_t af[4], bf[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const half8_t*>(&lds[buf][0][128 * wr + 32 * i + l32][32 * d + 16 * h]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const half8_t*>(&lds[buf][1][64 * wc + 32 * j + l32][32 * d + 16 * h]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  WStage R0, R1;
+  gload(R0, 0);
+  gload(R1, 1);
+  stage_store(R0, 0, true);
+  gload(R0, 2);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    stage_store(R1, 1, st + 1 < nst);
+    gload(R1, st + 3);
+    mfma_step(0);
+    __syncthreads();
+    stage_store(R0, 0, st + 2 < nst);
+    gload(R0, st + 4);
+    mfma_step(1);
+    __syncthreads();
+  }
+
+  // acc *= s_tA, then the compensation: bf16 steps of 64 channels, the
+  // residual rows (A side) and packed weight columns (B side) copied into
+  // buffer 0 (thread: channels 32 hf .. + 31 of row lr); channels past k
+  // read as zero
+  const float sta = *p.a_st;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] *= sta;
+  if (p.k > 0) {
+    auto keep = [](bool live, uint4 v) {
+      const uint32_t m = live ? 0xFFFFFFFFu : 0u;
+      return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+    };
+    const uint16_t* r_row = p.a_resid + a_tok * p.k;
+    const uint16_t* w_row = p.wcomp + ((int64_t)c.e * N + bn) * p.kpad;
+    for (int kc = 0; kc < p.k; kc += W_SE) {
+      const int rem = p.k - kc;  // channels left, uniform
+      uint4 ra[4], wb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ch = 32 * hf + 8 * q;
+        ra[q] = *reinterpret_cast<const uint4*>(r_row + min(kc + ch, p.k - 8));
+        wb[q] = *reinterpret_cast<const uint4*>(w_row + min(kc + ch, p.kpad - 8));
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ch = 32 * hf + 8 * q;
+        *reinterpret_cast<uint4*>(&lds[0][0][lr][2 * ch]) = keep(ch < rem, ra[q]);
+        *reinterpret_cast<uint4*>(&lds[0][1][lr][2 * ch]) = keep(ch < rem, wb[q]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        if (16 * d >= rem) break;
+        bf16x8_t af[4], bf[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[i] = *reinterpret_cast<const bf16x8_t*>(&lds[0][0][128 * wr + 32 * i + l32][32 * d + 16 * h]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bf[j] = *reinterpret_cast<const bf16x8_t*>(&lds[0][1][64 * wc + 32 * j + l32][32 * d + 16 * h]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      }
+      __syncthreads();
+    }
+  }
+
+  // epilogue: scale by s_tW and store.  acc[i][j][v]: row 128 wr + 32 i +
+  // 8 (v / 4) + 4 h + v % 4, B row 64 wc + 32 j + l32 (with SwiGLU j = 0 is
+  // the gate and j = 1 the up row of output column 32 wc + l32).
+  const float stw = p.w_st[c.e];
+  const int64_t rbase = c.row0 + 128 * wr;
+  const bool rows_full = rbase + 128 <= c.row_end;
+  if (!kSwiglu) {
+    const int64_t nbase = (int64_t)c.nt * BN + WN * wc;
+    auto emit = [&](bool check) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t pr = rbase + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (check && pr >= c.row_end) continue;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int64_t n = nbase + 32 * j + l32;
+            if (check && n >= N) continue;
+            const float y = acc[i][j][v] * stw;
+            if (p.out_f32) p.out_f32[pr * N + n] = y;
+            if (p.out_bf16) p.out_bf16[pr * N + n] = (uint16_t)f32_to_bf16_rne(y);
+          }
+        }
+    };
+    if (rows_full && nbase + WN <= N)
+      emit(false);
+    else
+      emit(true);
+  } else {
+    const int64_t I = N >> 1;
+    const int64_t ng = (int64_t)c.nt * (BN / 2) + 32 * wc + l32;
+    uint32_t hmax = 0;  // largest |h| stored by this lane, as bf16 bits
+    auto emit = [&](bool check) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t pr = rbase + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (check && (pr >= c.row_end || ng >= I)) continue;
+          const float g = acc[i][0][v] * stw;
+          const float u = acc[i][1][v] * stw;
+          if (p.out_f32) {
+            p.out_f32[pr * N + ng] = g;
+            p.out_f32[pr * N + I + ng] = u;
+          }
+          // silu(g) u; the result is rounded to bf16, so an rcp suffices
+          const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+          const uint32_t hb = f32_to_bf16_rne(hv);
+          if (p.out_bf16) p.out_bf16[pr * I + ng] = (uint16_t)hb;
+          hmax = max(hmax, hb & 0x7FFFu);
+        }
+    };
+    if (rows_full && (int64_t)c.nt * (BN / 2) + 32 * (wc + 1) <= I)
+      emit(false);
+    else
+      emit(true);
+    if (p.h_amax) {
+      const uint32_t m = wave_max_u32(hmax);
+      if (lane == 0 && m != 0u) atomicMax(p.h_amax, m << 16);
+    }
+  }
+}
+
 // -------------------------------------------------------- path FP8_BLOCK --
 // E2M1 magnitude index -> FP8 E4M3 byte (0, 0.5, 1, 1.5, 2, 3, 4, 6), as two
 // byte-select tables for v_perm.
@@ -810,7 +1047,8 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   if (a->rows != 0 && (!a->a_codes || !a->a_scales || !a->a_tensor_scale)) return NVQ_EINVAL;
   if (a->rows != 0 && !a->out_bf16 && !a->out_f32) return NVQ_EINVAL;
   if (a->epilogue != NVQ_EPI_NONE && a->epilogue != NVQ_EPI_SWIGLU) return NVQ_EINVAL;
-  if (a->path != NVQ_GEMM_AUTO && a->path != NVQ_GEMM_DEQ16 && a->path != NVQ_GEMM_FP8_BLOCK)
+  if (a->path != NVQ_GEMM_AUTO && a->path != NVQ_GEMM_DEQ16 && a->path != NVQ_GEMM_FP8_BLOCK &&
+      a->path != NVQ_GEMM_DEQ16_WIDE)
     return NVQ_EINVAL;
   if (a->rows < 0 || a->E < 1 || a->E > 1024 || a->N <= 0 || a->K <= 0) return NVQ_ESHAPE;
   if (a->K % 128 != 0) return NVQ_ESHAPE;  // K steps of 32 elements; 128 keeps rows 64-byte aligned
@@ -831,8 +1069,15 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
     hipLaunchKernelGGL(k_clear_word, dim3(1), dim3(1), 0, s, h_amax);  // amax of no rows: 0
     return last_launch();
   }
-  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, a->expert_offsets, (int)a->E, BM, L.tiles,
-                     L.ntiles, L.max_tiles, h_amax);
+  // Tile shape: 128-row tiles unless the 256-row kernel is asked for (it
+  // measured slower on every layer here, also where experts average 2048
+  // rows, so AUTO does not take it).
+  const bool fp8 = a->path == NVQ_GEMM_FP8_BLOCK;
+  const bool wide = a->path == NVQ_GEMM_DEQ16_WIDE;
+  const int bm = wide ? W_BM : BM;
+  const int max_tiles = wide ? (int)((a->rows + W_BM - 1) / W_BM + a->E) : L.max_tiles;
+  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, a->expert_offsets, (int)a->E, bm, L.tiles,
+                     L.ntiles, max_tiles, h_amax);
   if (int rc = last_launch()) return rc;
   GemmParams p;
   p.rows = a->rows; p.K = a->K; p.N = a->N; p.E = a->E; p.a_rows = a->a_rows;
@@ -853,17 +1098,23 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   }
   p.w_codes = a->w_codes; p.w_scales = a->w_scales; p.w_st = a->w_tensor_scale;
   p.out_bf16 = a->out_bf16; p.out_f32 = a->out_f32;
-  p.tiles = L.tiles; p.ntiles = L.ntiles; p.max_tiles = L.max_tiles;
+  p.tiles = L.tiles; p.ntiles = L.ntiles; p.max_tiles = max_tiles;
   p.h_amax = h_amax;
   const bool swiglu = a->epilogue == NVQ_EPI_SWIGLU;
   p.swiglu = swiglu ? 1 : 0;
-  p.bm = BM;
+  p.bm = bm;
   p.n_tiles_n = swiglu ? (int)((a->N / 2 + BN / 2 - 1) / (BN / 2)) : (int)((a->N + BN - 1) / BN);
-  const int n_groups = (L.max_tiles + kGroupM - 1) / kGroupM;
-  const int64_t G0 = (int64_t)n_groups * kGroupM * p.n_tiles_n;
+  const int gm = wide ? kGroupMW : kGroupM;
+  const int n_groups = (max_tiles + gm - 1) / gm;
+  const int64_t G0 = (int64_t)n_groups * gm * p.n_tiles_n;
   const int64_t G = (G0 + 7) / 8 * 8;
-  const bool fp8 = a->path == NVQ_GEMM_FP8_BLOCK;
-  if (fp8) {
+  if (G > 0x7FFFFFFF) return NVQ_ESHAPE;
+  if (wide) {
+    if (swiglu)
+      hipLaunchKernelGGL(k_moe_gemm_deq16w<1>, dim3((unsigned)G), dim3(W_THR), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_moe_gemm_deq16w<0>, dim3((unsigned)G), dim3(W_THR), 0, s, p);
+  } else if (fp8) {
     if (swiglu)
       hipLaunchKernelGGL(k_moe_gemm_fp8blk<1>, dim3((unsigned)G), dim3(NTHR), 0, s, p);
     else

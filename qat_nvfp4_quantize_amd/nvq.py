@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libnvq.so")
 
 NVQ_F32, NVQ_BF16 = 0, 1
 NVQ_EPI_NONE, NVQ_EPI_SWIGLU = 0, 1
-NVQ_GEMM_AUTO, NVQ_GEMM_DEQ16, NVQ_GEMM_FP8_BLOCK = 0, 1, 2
+NVQ_GEMM_AUTO, NVQ_GEMM_DEQ16, NVQ_GEMM_FP8_BLOCK, NVQ_GEMM_DEQ16_WIDE = 0, 1, 2, 3
 NVQ_QAT_FWD, NVQ_QAT_DGRAD, NVQ_QAT_WGRAD = 0, 1, 2
 NVQ_STATUS_NONFINITE, NVQ_STATUS_BAD_EXPERT = 1, 2
 NVQ_GUIDE_MANTISSA, NVQ_GUIDE_DIRECTION = 0, 1

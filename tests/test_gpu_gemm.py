@@ -35,12 +35,20 @@ def _w_deq(codes, scales, st):
     return oracle.dequantize(codes, scales, st).astype(np.float64)
 
 
-@pytest.mark.parametrize("path", ["deq16", "fp8_block"])
+def _path(name):
+    """deq16: exact fp16 dequantization, 128-row tiles; deq16w: the same in
+    256-row tiles; fp8_block: FP8 block products scaled in fp32."""
+    nvq = _nvq()
+    return {"deq16": nvq.NVQ_GEMM_DEQ16, "deq16w": nvq.NVQ_GEMM_DEQ16_WIDE,
+            "fp8_block": nvq.NVQ_GEMM_FP8_BLOCK}[name]
+
+
+@pytest.mark.parametrize("path", ["deq16", "deq16w", "fp8_block"])
 def test_dense_check_workload(path):
     import torch
 
     nvq = _nvq()
-    gp = nvq.NVQ_GEMM_DEQ16 if path == "deq16" else nvq.NVQ_GEMM_FP8_BLOCK
+    gp = _path(path)
     x, w, k = inputs.dense_check()
     xg, wg = to_gpu(x), to_gpu(w)
     qa = nvq.nvfp4_quantize(xg, score=True)
@@ -93,15 +101,15 @@ class MoeRun:
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("path", ["deq16", "fp8_block"])
+@pytest.mark.parametrize("path", ["deq16", "deq16w", "fp8_block"])
 @pytest.mark.parametrize("shape", ["small", "small_ragged"])
 def test_small_moe_layer_stagewise(shape, path):
-    """Both GEMM paths (exact fp16 dequantization; FP8 block products scaled
-    in fp32) against the same oracle."""
+    """Every GEMM path (exact fp16 dequantization in 128- and 256-row tiles;
+    FP8 block products scaled in fp32) against the same oracle."""
     import torch
 
     nvq = _nvq()
-    gp = nvq.NVQ_GEMM_DEQ16 if path == "deq16" else nvq.NVQ_GEMM_FP8_BLOCK
+    gp = _path(path)
     s = inputs.small_moe() if shape == "small" else inputs.small_moe(wid=101, T=77, E=5, topk=3, k=24)
     run = MoeRun(s, gp)
     x = run.x
@@ -207,23 +215,25 @@ def test_decode_layer_gate_up_sampled():
         check_tol(y1[sel], ref[sel], xf[row_tok[sel]], _w_deq(wc[i], wsc[i], wst[i]), f"decode e={e}")
 
 
-@pytest.mark.parametrize("path", ["deq16", "fp8_block"])
+@pytest.mark.parametrize("path", ["deq16", "deq16w", "fp8_block"])
 @pytest.mark.parametrize("K,N,k,epi", [(128, 160, 8, "none"), (384, 384, 128, "none"),
-                                       (384, 192, 0, "swiglu"), (128, 208, 128, "swiglu")])
+                                       (384, 192, 0, "swiglu"), (128, 208, 128, "swiglu"),
+                                       (256, 512, 72, "swiglu"), (256, 320, 200, "none")])
 def test_grouped_gemm_edge_shapes(K, N, k, epi, path):
     """Direct grouped-GEMM calls on shapes the layer tests do not reach: an odd
     number of 128-element K steps (K = 384), partial column tiles (N = 160,
-    208, 384; SwiGLU halves of 96 and 104), k = K, k = 0, experts with no
-    rows, one expert with more rows than one row tile, fp32 and bf16 outputs,
-    and rows read through a_row with a divisor."""
+    208, 320, 384; SwiGLU halves of 96 and 104), k = K, k = 0, k not a
+    multiple of 64, experts with no rows, one expert with more rows than one
+    256-row tile and one with more than one 128-row tile, fp32 and bf16
+    outputs, and rows read through a_row with a divisor."""
     import torch
 
     nvq = _nvq()
-    gp = nvq.NVQ_GEMM_DEQ16 if path == "deq16" else nvq.NVQ_GEMM_FP8_BLOCK
+    gp = _path(path)
     swiglu = epi == "swiglu"
     g = np.random.default_rng(K * 1000 + N + k)
-    E, T, topk = 5, 70, 3
-    counts = np.array([0, 150, 3, 0, 57])  # P = 210 sorted rows
+    E, T, topk = 5, 140, 3
+    counts = np.array([0, 300, 3, 0, 57])  # P = 360 sorted rows of 420 pairs
     P = int(counts.sum())
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     pair = g.permutation(T * topk)[:P].astype(np.int32)  # sorted pair ids; token = pair // topk
