@@ -621,13 +621,24 @@ __global__ __launch_bounds__(256, 2) void k_qat_fwd2(QatParams p) {
   auto st_f32 = [&](int64_t o, float y) { p.out_f32[o] = y; };
   auto st_bf16 = [&](int64_t o, float y) { p.out_bf16[o] = (uint16_t)f32_to_bf16_rne(y); };
   auto st_both = [&](int64_t o, float y) { st_f32(o, y); st_bf16(o, y); };
-  const bool full = row0 + FBM <= row_end && (int64_t)nt * FBN + FWN * (wave + 1) <= N;
-  if (p.out_f32 && p.out_bf16)
+  const bool cols_full = (int64_t)nt * FBN + FWN * (wave + 1) <= N;
+  const bool full = row0 + FBM <= row_end && cols_full;
+  // bf16 rows as 16-byte pieces through LDS when the wave's 64 columns are
+  // inside the output (the LDS tiles are free after the barrier)
+  const bool bf16_lds = p.out_bf16 && (N % 8 == 0) && ((uintptr_t)p.out_bf16 % 16 == 0) && cols_full;
+  if (p.out_f32 && p.out_bf16 && !bf16_lds)
     full ? emit(st_both, false) : emit(st_both, true);
   else if (p.out_f32)
     full ? emit(st_f32, false) : emit(st_f32, true);
-  else
+  else if (!bf16_lds)
     full ? emit(st_bf16, false) : emit(st_bf16, true);
+  if (p.out_bf16) {
+    __syncthreads();  // every wave is past its last LDS read
+    if (bf16_lds)
+      store_tile_bf16_lds(acc, stw, reinterpret_cast<uint8_t*>(&lds[0][0]) + 16384 * wave,
+                          p.out_bf16 + row0 * N + (int64_t)nt * FBN + FWN * wave, N,
+                          (int)min<int64_t>(FBM, row_end - row0));
+  }
 }
 
 // ------------------------------------------------ input gradient, 2 WG/CU --

@@ -87,6 +87,7 @@ struct GemmParams {
   int swiglu;             // 1: gate/up fused weight, epilogue h = silu(gate) * up
   int bm;                 // row tile of the tile table
   uint32_t* h_amax;       // SwiGLU: max |h| over the stored bf16 h, as fp32 bits; or NULL
+  int bf16_rows16;        // out_bf16 rows may be written in 16-byte pieces (N % 8 == 0, aligned)
 };
 
 // Tile table: expert e's rows [off[e], off[e+1]) split into BM-row tiles.
@@ -415,10 +416,11 @@ __device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c
 
 // Scale by s_tW and store.  acc[i][j][v]: row 32i + 8(v/4) + 4h + v%4, local
 // column 64 wave + 32 j + l32; with SwiGLU fragment 0 is the gate and
-// fragment 1 the up column of the same output column.
+// fragment 1 the up column of the same output column.  lds: the kernel's
+// LDS tiles, no longer read (a 16 KB region per wave for the bf16 stores).
 template <int kSwiglu>
 __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c,
-                                         const floatx16_t (&acc)[4][2]) {
+                                         const floatx16_t (&acc)[4][2], uint8_t* lds) {
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, l32 = lane & 31, h = lane >> 5;
   const int64_t N = p.N;
   const float stw = p.w_st[c.e];
@@ -426,7 +428,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c,
   // guards become exec-mask branches whose waits serialize the stores.
   const bool rows_full = c.row0 + BM <= c.row_end;
   if (!kSwiglu) {
-    auto emit = [&](bool check) {
+    const bool cols_full = (int64_t)c.nt * BN + WN * (wave + 1) <= N;
+    // bf16 through LDS when the wave's 64 columns are inside the output
+    const bool bf16_lds = p.out_bf16 && p.bf16_rows16 && cols_full;
+    auto emit = [&](bool check, bool f32, bool bf16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -438,15 +443,21 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c,
             const int64_t n = (int64_t)c.nt * BN + WN * wave + 32 * j + l32;
             if (check && n >= N) continue;
             const float y = acc[i][j][v] * stw;
-            if (p.out_f32) p.out_f32[pr * N + n] = y;
-            if (p.out_bf16) p.out_bf16[pr * N + n] = (uint16_t)f32_to_bf16_rne(y);
+            if (f32) p.out_f32[pr * N + n] = y;
+            if (bf16) p.out_bf16[pr * N + n] = (uint16_t)f32_to_bf16_rne(y);
           }
         }
     };
-    if (rows_full && (int64_t)c.nt * BN + WN * (wave + 1) <= N)
-      emit(false);
-    else
-      emit(true);
+    const bool f32 = p.out_f32 != nullptr, bf16_direct = p.out_bf16 && !bf16_lds;
+    if (f32 || bf16_direct) {
+      if (rows_full && cols_full)
+        emit(false, f32, bf16_direct);
+      else
+        emit(true, f32, bf16_direct);
+    }
+    if (bf16_lds)
+      store_tile_bf16_lds(acc, stw, lds + 16384 * wave, p.out_bf16 + c.row0 * N + (int64_t)c.nt * BN + WN * wave,
+                          N, (int)min<int64_t>(BM, c.row_end - c.row0));
   } else {
     const int64_t I = N >> 1;
     const int64_t ng = (int64_t)c.nt * (BN / 2) + 32 * wave + l32;
@@ -596,7 +607,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
     gload(X1, st + 3);
   }
   comp_phase(p, c, acc, lds[0], a_tok, b_n);
-  epilogue<kSwiglu>(p, c, acc);
+  epilogue<kSwiglu>(p, c, acc, &lds[0][0][0]);
 }
 
 // ------------------------------------------------ path DEQ16, wide tile --
@@ -999,7 +1010,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_moe_gemm_fp8blk(GemmParams p) {
     gload(X1, st + 3);
   }
   comp_phase(p, c, acc, lds[0], a_tok, b_n);
-  epilogue<kSwiglu>(p, c, acc);
+  epilogue<kSwiglu>(p, c, acc, &lds[0][0][0]);
 }
 
 struct MoeLayout {
@@ -1098,6 +1109,7 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   }
   p.w_codes = a->w_codes; p.w_scales = a->w_scales; p.w_st = a->w_tensor_scale;
   p.out_bf16 = a->out_bf16; p.out_f32 = a->out_f32;
+  p.bf16_rows16 = (a->N % 8 == 0 && aligned16(a->out_bf16)) ? 1 : 0;
   p.tiles = L.tiles; p.ntiles = L.ntiles; p.max_tiles = max_tiles;
   p.h_amax = h_amax;
   const bool swiglu = a->epilogue == NVQ_EPI_SWIGLU;

@@ -95,4 +95,51 @@ __device__ __forceinline__ uint32_t e2m1_index_exact(float ax, double S) {
   return i;
 }
 
+// ------------------------------------------------------- tile stores --
+// Stores a wave's 128 x 64 outputs bf16(acc * scale) as 16-byte row pieces
+// through LDS.  acc[i][j][v] is row 32 i + 8 (v / 4) + 4 h + v % 4, column
+// 32 j + l32 of the wave tile, so a store straight from the accumulators
+// writes 2 bytes per lane (128 store instructions).  Here adjacent lanes
+// first trade one value (a DPP swap), so each lane holds a bf16 pair of one
+// row and writes it to the wave's LDS region (128 rows x 128 bytes, 16-byte
+// chunk q of row r at slot q ^ 4 (r & 1), which keeps the two rows of a write
+// instruction in different banks); then each lane reads 16-byte row pieces
+// and stores them (16 store instructions).  Rows at or past nrows are not
+// stored.  region: this wave's 16 KB of LDS, free of other use.
+template <class Acc>
+__device__ __forceinline__ void store_tile_bf16_lds(const Acc (&acc)[4][2], float scale,
+                                                    uint8_t* region, uint16_t* out, int64_t ld,
+                                                    int nrows) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+  const bool odd = (l32 & 1) != 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        // rows r, r + 1 of column c: the even lane keeps row r and sends row
+        // r + 1 to its odd neighbour, which keeps row r + 1
+        const float a = acc[i][j][v] * scale, b = acc[i][j][v + 1] * scale;
+        const float send = odd ? a : b;
+        const float recv = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(send), 0xB1, 0xF, 0xF, false));
+        const float lo = odd ? recv : a, hi = odd ? b : recv;
+        const int row = 32 * i + 8 * (v >> 2) + 4 * h + (v & 3) + (odd ? 1 : 0);
+        const int col = 32 * j + l32 - (odd ? 1 : 0);  // even column of the pair
+        const int slot = (col >> 3) ^ ((row & 1) << 2);
+        *reinterpret_cast<uint32_t*>(region + row * 128 + slot * 16 + (col & 7) * 2) =
+            f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+      }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int row = (lane >> 3) + 8 * m, q = lane & 7;
+    if (row >= nrows) continue;
+    const uint4 v4 = *reinterpret_cast<const uint4*>(region + row * 128 + ((q ^ ((row & 1) << 2)) << 4));
+    *reinterpret_cast<uint4*>(out + (int64_t)row * ld + 8 * q) = v4;
+  }
+}
+
 }  // namespace nvq
