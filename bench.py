@@ -235,6 +235,13 @@ class MoeLeg:
         # the quantization of h (which then skips its own amax pass)
         self.h_amax = torch.zeros(1, dtype=f32, device=dev)
         self.y2 = torch.empty(P, H, dtype=bf, device=dev)
+        # the layer output (the next layer's input) and its max |x|, recorded
+        # by the combine for that input's quantization
+        self.out = torch.empty(s.T, H, dtype=bf, device=dev)
+        self.out_amax = torch.zeros(1, dtype=f32, device=dev)
+        self.qnext = (torch.empty(s.T, H // 2, dtype=u8, device=dev),
+                      torch.empty(s.T, H // 16, dtype=u8, device=dev),
+                      torch.empty(1, dtype=f32, device=dev), torch.empty(H, dtype=f32, device=dev))
         self.flops_gu = 2.0 * P * H * 2 * I
         self.flops_dn = 2.0 * P * I * H
         self.flops_comp = 2.0 * P * k * 2 * I + 2.0 * P * k * H
@@ -270,7 +277,39 @@ class MoeLeg:
             self.h, self.qh[0], self.qh[1], self.qh[2], s.k, scores=self.qh[3], ws=self.ws_t2))
         timer("gemm_dn" + tag, lambda: self.gemm("dn", self.qh, s.P, None, r2, idx2, (self.y2, None),
                                                   nvq.NVQ_EPI_NONE, comp, path))
-        timer("combine", lambda: nvq.nvq_moe_combine(self.y2, self.pos, self.w))
+        timer("combine", lambda: nvq.nvq_moe_combine(self.y2, self.pos, self.w, out=self.out))
+
+    def fused_combine(self, timer_):
+        """The down projection with the layer's combine fused into its
+        epilogue (outside the timed steps; same inputs as the step's down
+        projection), against the step's separate down GEMM + combine."""
+        nvq, s = self.nvq, self.s
+        timer = lambda label, fn: timer_(self.name + "/" + label, fn)
+        if not hasattr(self, "ws_comb"):
+            L = nvq.load()
+            self.ws_comb = nvq.workspace(L.moe_gemm_workspace_bytes_comb(s.P, s.E, s.H, s.k, s.T),
+                                         self.y2.device)
+        idx2, r2, _ = nvq.residual_topk_channels(self.h, self.qh[0], self.qh[1], self.qh[2], s.k,
+                                                 scores=self.qh[3], ws=self.ws_t2)
+        codes, scales, st = self.qw["dn"]
+        timer("gemm_dn_fused_combine", lambda: nvq.moe_grouped_gemm_w4a4_comp(
+            self.qh[0], self.qh[1], self.qh[2], codes, scales, st, self.off, rows=s.P,
+            a_resid=r2, comp_idx=idx2, ws=self.ws_comb, out=(self.y2, None), w_cm=self.wcm["dn"],
+            comb=(self.sp, self.pos, self.w, self.out)))
+
+    def next_input(self, timer_):
+        """The layer output quantized as the next layer's input (outside the
+        timed steps), two ways: the combine records max |x| and the
+        quantization takes it as amax_in (one pass fewer over x), or the plain
+        combine and the quantization's own amax pass.  Same record."""
+        nvq = self.nvq
+        timer = lambda label, fn: timer_(self.name + "/" + label, fn)
+        timer("combine_with_amax", lambda: nvq.nvq_moe_combine(self.y2, self.pos, self.w, out=self.out,
+                                                               out_amax=self.out_amax))
+        timer("quant_next_x_combine_amax", lambda: nvq.nvfp4_quantize(
+            self.out, amax_in=self.out_amax, score=True, ws=self.ws_q1, out=self.qnext))
+        timer("quant_next_x_own_amax", lambda: nvq.nvfp4_quantize(
+            self.out, score=True, ws=self.ws_q1, out=self.qnext))
 
     def cpu_baseline(self, max_rows=64):
         """The oracle's W4A4 grouped GEMM with compensation (fp64, exhaustive
@@ -381,6 +420,17 @@ class MoeLeg:
             out["path_deq16_wide"] = {"gemm_gu_ms": round(gw, 4), "gemm_dn_ms": round(dw_, 4),
                                       "gemm_tflops": round(tfw, 1),
                                       "time_vs_chosen_path": round((gw + dw_) / (gu + dn), 3)}
+        if "gemm_dn_fused_combine" in timer.total:
+            fz = timer.avg_ms("gemm_dn_fused_combine")
+            out["fused_combine"] = {"gemm_dn_with_combine_ms": round(fz, 4),
+                                    "separate_gemm_dn_plus_combine_ms": round(dn + timer.avg_ms("combine"), 4),
+                                    "time_vs_separate": round(fz / (dn + timer.avg_ms("combine")), 3)}
+        if "quant_next_x_combine_amax" in timer.total:
+            ca, qa = timer.avg_ms("combine_with_amax"), timer.avg_ms("quant_next_x_combine_amax")
+            c0, q0 = timer.avg_ms("combine"), timer.avg_ms("quant_next_x_own_amax")
+            out["next_input_amax"] = {"combine_with_amax_ms": round(ca, 4), "quant_with_amax_in_ms": round(qa, 4),
+                                      "combine_ms": round(c0, 4), "quant_own_amax_ms": round(q0, 4),
+                                      "pair_vs_plain": round((ca + qa) / (c0 + q0), 3)}
         if hasattr(self, "graph_ms"):
             out["layer_ms_graph"] = round(self.graph_ms, 4)
         return out
@@ -779,6 +829,10 @@ def main():
             if leg.name == "moe_prefill":
                 for _ in range(2):
                     leg.step(timer, path=_nvq.NVQ_GEMM_DEQ16_WIDE)
+            for _ in range(5):
+                leg.next_input(timer)
+            for _ in range(3):
+                leg.fused_combine(timer)
         if leg.name == "qat":
             for _ in range(3):
                 leg.symmetric(timer)

@@ -231,9 +231,15 @@ int nvq_moe_permute(const int32_t* ids, int64_t T, int64_t topk, int64_t E,
 
 /* out[t, n] = bf16( sum_j w[t, j] * y[pos[t*topk + j], n] ), j ascending, fp32
  * accumulation.  y [P, N] bf16 in sorted-pair order; a pair the permutation
- * dropped (pos < 0) is left out of the sum.  N % 8 == 0. */
+ * dropped (pos < 0) is left out of the sum.  N % 8 == 0.
+ * out_amax: nullable device fp32 word (4-byte aligned) that receives max |out|
+ * over the stored bf16 values (0 for no tokens); the call clears it first.
+ * When out is the next layer's input (QUADS §2.1: activations are quantized
+ * online at every forward), passing it as amax_in to nvfp4_quantize replaces
+ * that call's amax pass with an identical result.  Calls sharing the word
+ * must be ordered on one stream. */
 int nvq_moe_combine(const uint16_t* y, const int32_t* pos, const float* weights, int64_t T,
-                    int64_t topk, int64_t N, uint16_t* out, void* stream);
+                    int64_t topk, int64_t N, uint16_t* out, float* out_amax, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Chained backward of the MoE layer's glue (QUADS §2.2-A: the trainer's
@@ -329,6 +335,23 @@ typedef struct nvq_moe_gemm_args {
    * does not depend on order).  NULL: not computed.  NVQ_EINVAL with another
    * epilogue.  Calls sharing the word must be ordered on one stream. */
   float* h_amax;
+  /* Optional, read only when struct_size covers them: the layer's combine
+   * fused into this call (NVQ_EPI_NONE, path DEQ16 or AUTO; out_bf16 needed):
+   * comb_out[t, n] = bf16( sum_j comb_weights[t, j] * out_bf16[comb_pos[t*topk
+   * + j], n] ), j ascending, fp32 -- the same values as nvq_moe_combine on this
+   * call's bf16 output, bit for bit (QUADS §2.2-B asks for the correction in
+   * fused kernels).  comb_pair [rows] is the sorted pair id of each row (token
+   * = pair / comb_topk), comb_pos [comb_T, comb_topk] the permutation's inverse
+   * map (pos < 0: dropped pair), comb_weights [comb_T, comb_topk].  Each output
+   * row piece is written by the last workgroup to finish a row of that token
+   * (arrival counters in the workspace; moe_gemm_workspace_bytes_comb).
+   * comb_out NULL: no combine. */
+  const int32_t* comb_pair;
+  const int32_t* comb_pos;
+  const float* comb_weights;
+  int64_t comb_T;
+  int32_t comb_topk;
+  uint16_t* comb_out;
 } nvq_moe_gemm_args;
 
 /* Channel-major copy of an NVFP4 weight record (same codes and scales, other
@@ -347,8 +370,10 @@ typedef struct nvq_moe_gemm_args {
 int nvfp4_channel_major(const uint8_t* codes, const uint8_t* scales, int64_t batch, int64_t N,
                         int64_t K, uint8_t* codes_cm, uint8_t* scales_cm, void* stream);
 
-/* Workspace: tile table plus the packed compensation weights [E, N, k16] bf16. */
+/* Workspace: tile table plus the packed compensation weights [E, N, k16] bf16;
+ * the _comb variant also holds the fused combine's arrival counters (T tokens). */
 size_t moe_gemm_workspace_bytes(int64_t rows, int64_t E, int64_t N, int32_t k);
+size_t moe_gemm_workspace_bytes_comb(int64_t rows, int64_t E, int64_t N, int32_t k, int64_t T);
 int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */

@@ -88,7 +88,30 @@ struct GemmParams {
   int bm;                 // row tile of the tile table
   uint32_t* h_amax;       // SwiGLU: max |h| over the stored bf16 h, as fp32 bits; or NULL
   int bf16_rows16;        // out_bf16 rows may be written in 16-byte pieces (N % 8 == 0, aligned)
+  // fused combine (NULL comb_out: none)
+  const int32_t* comb_pair;
+  const int32_t* comb_pos;
+  const float* comb_w;
+  int comb_topk;
+  uint16_t* comb_out;
+  uint32_t* comb_cnt;     // [T, n_tiles_n] arrival counters, zero at launch
 };
+
+// Before a GEMM with the fused combine: clears the arrival counters, and
+// writes the output row of every token none of whose pairs has a row (all
+// dropped by the permutation): its combine is the empty sum, 0.
+__global__ __launch_bounds__(256) void k_comb_prep(uint32_t* __restrict__ cnt, int64_t n_cnt,
+                                                  const int32_t* __restrict__ pos, int64_t T, int topk,
+                                                  uint16_t* __restrict__ out, int64_t N) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_cnt; i += stride) cnt[i] = 0u;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < T; t += stride) {
+    bool any = false;
+    for (int j = 0; j < topk; ++j) any = any || pos[t * topk + j] >= 0;
+    if (any) continue;
+    for (int64_t c = 0; c < N; c += 8) *reinterpret_cast<uint4*>(out + t * N + c) = make_uint4(0, 0, 0, 0);
+  }
+}
 
 // Tile table: expert e's rows [off[e], off[e+1]) split into BM-row tiles.
 // Also clears the h amax word, ahead of the GEMM on the same stream.
@@ -414,6 +437,69 @@ __device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c
   }
 }
 
+// acc + w * y with two roundings (no fused multiply-add), as the separate
+// combine computes it.
+__device__ __forceinline__ float mul_add_unfused(float acc, float w, float y) {
+#pragma clang fp contract(off)
+  return acc + w * y;
+}
+
+// The layer's combine fused after the down projection's stores (the
+// "last workgroup" pattern): every workgroup makes its output rows visible
+// device-wide (__threadfence), then counts, for each of its rows, one arrival
+// of that row's token at this column tile.  The workgroup whose arrival
+// completes a token's count (the number of its pairs the permutation kept)
+// sums the token's pair rows over this column tile, j ascending, in fp32, as
+// nvq_moe_combine does on the same bf16 rows: the result does not depend on
+// which workgroup is last.  lds: the kernel's LDS tiles, free by now.
+__device__ __forceinline__ void fused_combine(const GemmParams& p, const TileCtx& c, uint8_t* lds) {
+  const int t = threadIdx.x;
+  int32_t* s_list = reinterpret_cast<int32_t*>(lds);      // tokens completed here (<= BM)
+  int32_t* s_n = reinterpret_cast<int32_t*>(lds + 4 * BM);
+  __threadfence();  // this thread's output rows are visible to every workgroup
+  __syncthreads();  // ... and every thread of this workgroup is past its stores
+  if (t == 0) *s_n = 0;
+  __syncthreads();
+  const int topk = p.comb_topk;
+  if (t < BM && c.row0 + t < c.row_end) {
+    const int64_t tok = p.comb_pair[c.row0 + t] / topk;
+    int nvalid = 0;
+    for (int j = 0; j < topk; ++j) nvalid += p.comb_pos[tok * topk + j] >= 0 ? 1 : 0;
+    const uint32_t before = atomicAdd(&p.comb_cnt[tok * p.n_tiles_n + c.nt], 1u);
+    if (before + 1u == (uint32_t)nvalid) s_list[atomicAdd(s_n, 1)] = (int32_t)tok;
+  }
+  __syncthreads();
+  const int nlast = *s_n;
+  if (nlast == 0) return;
+  __threadfence();  // the other workgroups' rows of these tokens are visible here
+  const int64_t N = p.N;
+  constexpr int kVecs = BN / 8;  // 8-column pieces of a column tile
+  for (int idx = t; idx < nlast * kVecs; idx += NTHR) {
+    const int64_t tok = s_list[idx / kVecs];
+    const int64_t col = (int64_t)c.nt * BN + 8 * (idx % kVecs);
+    if (col >= N) continue;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < topk; ++j) {
+      const int32_t pj = p.comb_pos[tok * topk + j];
+      if (pj < 0) continue;
+      const float wj = p.comb_w[tok * topk + j];
+      const uint4 q = *reinterpret_cast<const uint4*>(p.out_bf16 + (int64_t)pj * N + col);
+      const uint32_t q4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int h2 = 0; h2 < 4; ++h2) {
+        acc[2 * h2] = mul_add_unfused(acc[2 * h2], wj, bf16_lo(q4[h2]));
+        acc[2 * h2 + 1] = mul_add_unfused(acc[2 * h2 + 1], wj, bf16_hi(q4[h2]));
+      }
+    }
+    uint4 o;
+    o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+    o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+    o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(p.comb_out + tok * N + col) = o;
+  }
+}
+
 // Scale by s_tW and store.  acc[i][j][v]: row 32i + 8(v/4) + 4h + v%4, local
 // column 64 wave + 32 j + l32; with SwiGLU fragment 0 is the gate and
 // fragment 1 the up column of the same output column.  lds: the kernel's
@@ -458,6 +544,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c,
     if (bf16_lds)
       store_tile_bf16_lds(acc, stw, lds + 16384 * wave, p.out_bf16 + c.row0 * N + (int64_t)c.nt * BN + WN * wave,
                           N, (int)min<int64_t>(BM, c.row_end - c.row0));
+    if (p.comb_out) fused_combine(p, c, lds);
   } else {
     const int64_t I = N >> 1;
     const int64_t ng = (int64_t)c.nt * (BN / 2) + 32 * wave + l32;
@@ -1019,10 +1106,12 @@ struct MoeLayout {
   int32_t* tiles;
   int32_t* ntiles;
   uint16_t* wcomp;
+  int64_t n_cnt;
+  uint32_t* cnt;
   size_t bytes;
 };
 
-MoeLayout moe_layout(void* ws, int64_t rows, int64_t E, int64_t N, int64_t k) {
+MoeLayout moe_layout(void* ws, int64_t rows, int64_t E, int64_t N, int64_t k, int64_t comb_T = 0) {
   MoeLayout L;
   L.max_tiles = (int)((rows + BM - 1) / BM + E);
   L.kpad = (int)((k + 15) / 16 * 16);
@@ -1030,6 +1119,8 @@ MoeLayout moe_layout(void* ws, int64_t rows, int64_t E, int64_t N, int64_t k) {
   L.tiles = c.take<int32_t>((size_t)L.max_tiles * 2);
   L.ntiles = c.take<int32_t>(1);
   L.wcomp = c.take<uint16_t>((size_t)(E * N * L.kpad));
+  L.n_cnt = comb_T * ((N + BN - 1) / BN);
+  L.cnt = L.n_cnt > 0 ? c.take<uint32_t>((size_t)L.n_cnt) : nullptr;
   L.bytes = c.off;
   return L;
 }
@@ -1042,6 +1133,12 @@ using namespace nvq;
 extern "C" size_t moe_gemm_workspace_bytes(int64_t rows, int64_t E, int64_t N, int32_t k) {
   if (rows < 0 || E < 1 || N < 1 || k < 0) return kAlign;
   return moe_layout(nullptr, rows, E, N, k).bytes;
+}
+
+extern "C" size_t moe_gemm_workspace_bytes_comb(int64_t rows, int64_t E, int64_t N, int32_t k,
+                                                int64_t T) {
+  if (rows < 0 || E < 1 || N < 1 || k < 0 || T < 0) return kAlign;
+  return moe_layout(nullptr, rows, E, N, k, T).bytes;
 }
 
 extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stream) {
@@ -1072,9 +1169,23 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
       ((uintptr_t)a->a_scales & 7u) || ((uintptr_t)a->w_scales & 7u))
     return NVQ_EALIGN;
   if (!aligned256(a->ws)) return NVQ_EALIGN;
-  MoeLayout L = moe_layout(a->ws, a->rows, a->E, a->N, a->k);
+  const bool has_comb_fields = a->struct_size >= offsetof(nvq_moe_gemm_args, comb_out) + sizeof(void*);
+  const bool comb = has_comb_fields && a->comb_out;
+  if (comb) {
+    if (a->epilogue != NVQ_EPI_NONE || a->path == NVQ_GEMM_DEQ16_WIDE || !a->out_bf16) return NVQ_EINVAL;
+    if (!a->comb_pos || !a->comb_weights || (a->rows != 0 && !a->comb_pair)) return NVQ_EINVAL;
+    if (a->comb_topk < 1 || a->comb_T < 0 || (a->N & 7)) return NVQ_ESHAPE;
+    if (!aligned16(a->comb_out) || !aligned16(a->out_bf16)) return NVQ_EALIGN;
+  }
+  MoeLayout L = moe_layout(a->ws, a->rows, a->E, a->N, a->k, comb ? a->comb_T : 0);
   if (a->ws_bytes < L.bytes) return NVQ_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (comb && a->comb_T > 0) {  // counters start at zero (a kernel, not a memset: capture-safe)
+    const int64_t nb = std::min<int64_t>((std::max(L.n_cnt, a->comb_T) + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_comb_prep, dim3((unsigned)nb), dim3(256), 0, s, L.cnt, L.n_cnt, a->comb_pos,
+                       a->comb_T, (int)a->comb_topk, a->comb_out, a->N);
+    if (int rc = last_launch()) return rc;
+  }
   if (a->rows == 0) {
     if (!h_amax) return NVQ_OK;
     hipLaunchKernelGGL(k_clear_word, dim3(1), dim3(1), 0, s, h_amax);  // amax of no rows: 0
@@ -1110,6 +1221,12 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   p.w_codes = a->w_codes; p.w_scales = a->w_scales; p.w_st = a->w_tensor_scale;
   p.out_bf16 = a->out_bf16; p.out_f32 = a->out_f32;
   p.bf16_rows16 = (a->N % 8 == 0 && aligned16(a->out_bf16)) ? 1 : 0;
+  p.comb_pair = comb ? a->comb_pair : nullptr;
+  p.comb_pos = comb ? a->comb_pos : nullptr;
+  p.comb_w = comb ? a->comb_weights : nullptr;
+  p.comb_topk = comb ? a->comb_topk : 0;
+  p.comb_out = comb ? a->comb_out : nullptr;
+  p.comb_cnt = L.cnt;
   p.tiles = L.tiles; p.ntiles = L.ntiles; p.max_tiles = max_tiles;
   p.h_amax = h_amax;
   const bool swiglu = a->epilogue == NVQ_EPI_SWIGLU;

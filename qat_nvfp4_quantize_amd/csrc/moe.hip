@@ -203,19 +203,48 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__
   }
 }
 
+// max |value| of the 8 bf16 of a packed uint4, as 16-bit magnitude bits
+__device__ __forceinline__ uint32_t absmax8_bf16(uint4 o) {
+  const uint32_t a = max(o.x & 0x7FFFu, (o.x >> 16) & 0x7FFFu), b = max(o.y & 0x7FFFu, (o.y >> 16) & 0x7FFFu);
+  const uint32_t c = max(o.z & 0x7FFFu, (o.z >> 16) & 0x7FFFu), d = max(o.w & 0x7FFFu, (o.w >> 16) & 0x7FFFu);
+  return max(max(a, b), max(c, d));
+}
+
+// The largest stored |out| of a 256-thread workgroup into *amax (fp32 bits
+// of a non-negative value order as the values).  DPP wave maxima, the four
+// of them combined by thread 0, which issues the atomic only when its value
+// exceeds the word's current one: the combine launches one workgroup per
+// token (and per 256 vectors), and one atomic each on a single word would
+// serialize.  Every thread takes part (threads with nothing stored pass 0).
+__device__ __forceinline__ void block_amax_out(uint32_t m16, uint32_t* amax) {
+  __shared__ uint32_t s_wmax[4];
+  const uint32_t m = wave_max_u32(m16);
+  if ((threadIdx.x & 63) == 0) s_wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t b = max(max(s_wmax[0], s_wmax[1]), max(s_wmax[2], s_wmax[3])) << 16;
+    if (b != 0u && b > __hip_atomic_load(amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(amax, b);
+  }
+}
+
 // out[t, n..n+8) = bf16(sum_j w[t,j] * y[pos[t,j], n..n+8)), fp32, j ascending,
 // for topk <= kMaxK: every pair's row segment is loaded before the first add,
 // so all topk loads are in flight together (a dropped pair, pos < 0, reads
 // the token's own output row instead, always valid memory, and is skipped in
-// the sum).  The token comes from the grid's y index.
+// the sum).  The token comes from the grid's y index.  amax (nullable):
+// receives max |out| over the stored bf16 values.
 template <int kMaxK>
 __global__ __launch_bounds__(256) void k_combine_n(const uint16_t* __restrict__ y,
                                                   const int32_t* __restrict__ pos,
                                                   const float* __restrict__ w, int topk,
-                                                  int64_t N, uint16_t* __restrict__ out) {
+                                                  int64_t N, uint16_t* __restrict__ out,
+                                                  uint32_t* __restrict__ amax) {
   const int64_t nvec = N / 8;
-  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (v >= nvec) return;
+  const int64_t v0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool live = v0 < nvec;
+  if (!live && !amax) return;
+  const int64_t v = live ? v0 : nvec - 1;  // idle lanes read a valid vector, store nothing
   const int64_t t = blockIdx.y;
   int32_t pj[kMaxK];
   uint4 q[kMaxK];
@@ -242,17 +271,21 @@ __global__ __launch_bounds__(256) void k_combine_n(const uint16_t* __restrict__ 
   o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
   o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
   o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
-  reinterpret_cast<uint4*>(out + t * N)[v] = o;
+  if (live) reinterpret_cast<uint4*>(out + t * N)[v] = o;
+  if (amax) block_amax_out(live ? absmax8_bf16(o) : 0u, amax);
 }
 
 // General topk: one pair at a time.
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
                                                 const int32_t* __restrict__ pos,
                                                 const float* __restrict__ w, int64_t T, int topk,
-                                                int64_t N, uint16_t* __restrict__ out) {
+                                                int64_t N, uint16_t* __restrict__ out,
+                                                uint32_t* __restrict__ amax) {
   const int64_t nvec = N / 8;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= T * nvec) return;
+  const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool live = i0 < T * nvec;
+  if (!live && !amax) return;
+  const int64_t i = live ? i0 : T * nvec - 1;
   const int64_t t = i / nvec, v = i - t * nvec;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int j = 0; j < topk; ++j) {
@@ -272,7 +305,8 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
   o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
   o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
   o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
-  reinterpret_cast<uint4*>(out + t * N)[v] = o;
+  if (live) reinterpret_cast<uint4*>(out + t * N)[v] = o;
+  if (amax) block_amax_out(live ? absmax8_bf16(o) : 0u, amax);
 }
 
 // ------------------------------------------------ chained backward glue --
@@ -452,19 +486,25 @@ extern "C" int nvq_moe_permute(const int32_t* ids, int64_t T, int64_t topk, int6
 }
 
 extern "C" int nvq_moe_combine(const uint16_t* y, const int32_t* pos, const float* weights,
-                               int64_t T, int64_t topk, int64_t N, uint16_t* out, void* stream) {
+                               int64_t T, int64_t topk, int64_t N, uint16_t* out, float* out_amax,
+                               void* stream) {
   if (T != 0 && (!y || !pos || !weights || !out)) return NVQ_EINVAL;
   if (T < 0 || topk < 1 || N <= 0 || (N & 7)) return NVQ_ESHAPE;
-  if (!aligned16(y) || !aligned16(out)) return NVQ_EALIGN;
+  if (!aligned16(y) || !aligned16(out) || ((uintptr_t)out_amax & 3u)) return NVQ_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* amax = reinterpret_cast<uint32_t*>(out_amax);
+  if (amax) {  // the maximum of no values is 0
+    if (int rc = clear_status(amax, s)) return rc;
+  }
   const int64_t n = T * (N / 8);
   if (n == 0) return NVQ_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (topk <= 8 && T <= 65535 && (N / 8 + 255) / 256 <= 0x7FFFFFFF) {
     const dim3 grid((unsigned)((N / 8 + 255) / 256), (unsigned)T);
-    hipLaunchKernelGGL(k_combine_n<8>, grid, dim3(256), 0, s, y, pos, weights, (int)topk, N, out);
+    hipLaunchKernelGGL(k_combine_n<8>, grid, dim3(256), 0, s, y, pos, weights, (int)topk, N, out,
+                       amax);
   } else {
     hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, pos,
-                       weights, T, (int)topk, N, out);
+                       weights, T, (int)topk, N, out, amax);
   }
   return last_launch();
 }

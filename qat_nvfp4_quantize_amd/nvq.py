@@ -45,7 +45,8 @@ class MoeGemmArgs(ctypes.Structure):
         ("k", _I32), ("w_codes", _P), ("w_scales", _P), ("w_tensor_scale", _P),
         ("epilogue", _I32), ("path", _I32), ("out_bf16", _P), ("out_f32", _P),
         ("ws", _P), ("ws_bytes", _SZ), ("a_row_div", _I32), ("w_codes_cm", _P),
-        ("w_scales_cm", _P), ("h_amax", _P),
+        ("w_scales_cm", _P), ("h_amax", _P), ("comb_pair", _P), ("comb_pos", _P),
+        ("comb_weights", _P), ("comb_T", _I64), ("comb_topk", _I32), ("comb_out", _P),
     ]
 
 
@@ -78,12 +79,13 @@ _SIGS = [
     ("nvq_moe_route", ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     ("nvq_moe_permute_workspace_bytes", _SZ, [_I64, _I64, _I64]),
     ("nvq_moe_permute", ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
-    ("nvq_moe_combine", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    ("nvq_moe_combine", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P]),
     ("nvq_swiglu_forward", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _P, _P]),
     ("nvq_swiglu_backward", ctypes.c_int, [_P, ctypes.c_int, _P, _I64, _I64, _P, _P]),
     ("nvq_moe_combine_backward", ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P]),
     ("nvfp4_channel_major", ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P]),
     ("moe_gemm_workspace_bytes", _SZ, [_I64, _I64, _I64, _I32]),
+    ("moe_gemm_workspace_bytes_comb", _SZ, [_I64, _I64, _I64, _I32, _I64]),
     ("moe_grouped_gemm_w4a4_comp", ctypes.c_int, [ctypes.POINTER(MoeGemmArgs), _P]),
     ("qat_gemm_workspace_bytes", _SZ, [_I64, _I64]),
     ("qat_fakequant_gemm_w4a16", ctypes.c_int, [ctypes.POINTER(QatGemmArgs), _P]),
@@ -328,14 +330,15 @@ def nvq_moe_permute(ids, E, ws=None):
     return sp, off, pos, ws
 
 
-def nvq_moe_combine(y, pos, weights, out=None):
+def nvq_moe_combine(y, pos, weights, out=None, out_amax=None):
+    """out bf16 [T, N]; out_amax (optional fp32 [1] on the GPU) receives max |out|."""
     _dev(y, "y")
     T, topk = weights.shape
     N = y.shape[1]
     if out is None:
         out = torch.empty(T, N, dtype=torch.bfloat16, device=y.device)
     _check("nvq_moe_combine", load().nvq_moe_combine(_ptr(y), _ptr(pos), _ptr(weights), T, topk,
-                                                     N, _ptr(out), _stream()))
+                                                     N, _ptr(out), _ptr(out_amax), _stream()))
     return out
 
 
@@ -400,9 +403,11 @@ def moe_grouped_gemm_w4a4_comp(a_codes, a_scales, a_tensor_scale, w_codes, w_sca
                                w_tensor_scale, expert_offsets, rows, a_row=None, a_resid=None,
                                comp_idx=None, epilogue=NVQ_EPI_NONE, path=NVQ_GEMM_AUTO,
                                want_bf16=True, want_f32=False, ws=None, a_row_div=0, out=None,
-                               w_cm=None, h_amax=None):
+                               w_cm=None, h_amax=None, comb=None):
     """Returns (out_bf16 or None, out_f32 or None).  w_cm: optional
-    (codes_cm, scales_cm) from nvfp4_channel_major for the compensation gather."""
+    (codes_cm, scales_cm) from nvfp4_channel_major for the compensation gather.
+    comb: optional (sorted_pair, pos, weights, out) -- the layer's combine fused
+    into this call, written to out bf16 [T, N]."""
     L = load()
     E, N, Kh = w_codes.shape
     K = Kh * 2
@@ -415,7 +420,10 @@ def moe_grouped_gemm_w4a4_comp(a_codes, a_scales, a_tensor_scale, w_codes, w_sca
         ob = torch.empty(rows, n_out, dtype=torch.bfloat16, device=dev) if want_bf16 else None
         of = torch.empty(rows, N, dtype=torch.float32, device=dev) if want_f32 else None
     if ws is None:
-        ws = workspace(L.moe_gemm_workspace_bytes(rows, E, N, k), dev)
+        if comb is None:
+            ws = workspace(L.moe_gemm_workspace_bytes(rows, E, N, k), dev)
+        else:
+            ws = workspace(L.moe_gemm_workspace_bytes_comb(rows, E, N, k, comb[2].shape[0]), dev)
     a = MoeGemmArgs()
     a.struct_size = ctypes.sizeof(MoeGemmArgs)
     a.rows, a.K, a.N, a.E = rows, K, N, E
@@ -434,6 +442,11 @@ def moe_grouped_gemm_w4a4_comp(a_codes, a_scales, a_tensor_scale, w_codes, w_sca
     if w_cm is not None:
         a.w_codes_cm, a.w_scales_cm = _ptr(w_cm[0]), _ptr(w_cm[1])
     a.h_amax = _ptr(h_amax)
+    if comb is not None:
+        sp, pos, wts, cout = comb
+        a.comb_pair, a.comb_pos, a.comb_weights = _ptr(sp), _ptr(pos), _ptr(wts)
+        a.comb_T, a.comb_topk = wts.shape[0], wts.shape[1]
+        a.comb_out = _ptr(cout)
     _check("moe_grouped_gemm_w4a4_comp", L.moe_grouped_gemm_w4a4_comp(ctypes.byref(a), _stream()))
     return ob, of
 

@@ -88,7 +88,8 @@ def test_host_side_validation_launches_nothing():
     # route: topk > E, E too large
     assert L.nvq_moe_route(fake, 4, 8, 9, fake, fake, None) == -2
     assert L.nvq_moe_route(fake, 4, 2048, 8, fake, fake, None) == -2
-    assert L.nvq_moe_combine(fake, fake, fake, 4, 2, 12, fake, None) == -2
+    assert L.nvq_moe_combine(fake, fake, fake, 4, 2, 12, fake, None, None) == -2
+    assert L.nvq_moe_combine(fake, fake, fake, 4, 2, 16, fake, P(0x1002), None) == -3
     assert L.nvfp4_dequantize(fake, fake, fake, 1, 4, 24, fake, 0, None) == -2
 
 

@@ -464,6 +464,68 @@ def test_prefill_gate_up_full_size_sampled():
                    oidx1, w, q, "gate/up")
 
 
+def _check_fused_combine(nvq, s, logits, qh, idx2, r2, q, cm, ooff):
+    """The down projection with the layer's combine fused (bf16 output only,
+    as the benchmark runs it): the fused output equals nvq_moe_combine on the
+    same call's bf16 rows, bit for bit, on two calls in a row."""
+    import torch
+
+    oids, ow = oracle.route(logits, s.topk)
+    osp, _, opos = oracle.permute(oids, s.E)
+    spg, posg, wg = to_gpu(osp), to_gpu(opos), to_gpu(ow)
+    for rep in range(2):
+        cout = torch.empty(s.T, s.H, dtype=torch.bfloat16, device="cuda")
+        ob, _ = nvq.moe_grouped_gemm_w4a4_comp(qh[0], qh[1], qh[2], q[0], q[1], q[2], to_gpu(ooff),
+                                               rows=s.P, a_resid=r2.contiguous(), comp_idx=idx2,
+                                               w_cm=cm, comb=(spg, posg, wg, cout))
+        ref = nvq.nvq_moe_combine(ob, posg, wg)
+        torch.cuda.synchronize()
+        assert_bits_equal(to_np(cout), to_np(ref), f"fused combine, call {rep}")
+        log(f"[gemm] fused combine {s.T}x{s.H} equals the separate combine (call {rep})")
+
+
+@pytest.mark.parametrize("path", ["deq16", "fp8_block"])
+@pytest.mark.parametrize("k", [0, 24])
+def test_fused_combine_small_with_dropped_pairs(path, k):
+    """The combine fused into the down projection on a small layer whose
+    permutation dropped pairs (a bad expert id), including a token whose pairs
+    were all dropped (its output is the empty sum, 0), a partial column tile
+    (N = 384) and an expert with more rows than one tile: bit-equal to
+    nvq_moe_combine on the call's own bf16 output, also on a second call."""
+    import torch
+
+    nvq = _nvq()
+    g = np.random.default_rng(2024 + k)
+    E, T, topk, K, N = 6, 150, 3, 256, 384
+    # tokens 0..39 all route to expert 1 first, so it gets more than 128 rows
+    ids = np.stack([g.permutation(E)[:topk] if t >= 40 else
+                    np.concatenate([[1], g.permutation([e for e in range(E) if e != 1])[:topk - 1]])
+                    for t in range(T)]).astype(np.int32)
+    ids[g.random((T, topk)) < 0.06] = E + 2
+    ids[7, :] = E + 2  # token 7: every pair dropped
+    sp, off, pos, _ = nvq.nvq_moe_permute(to_gpu(ids), E)
+    P = int(to_np(off)[-1])
+    wts = to_gpu(g.random((T, topk)).astype(np.float32))
+    x = (g.standard_normal((P, K)) * np.exp(g.standard_normal((1, K)))).astype(np.float32)
+    xg = to_gpu(x)
+    qa = nvq.nvfp4_quantize(xg, score=True)
+    qw = nvq.nvfp4_quantize(to_gpu((g.standard_normal((E, N, K)) * 0.05).astype(np.float32)))
+    resid, idx = None, None
+    if k > 0:
+        idx, resid, _ = nvq.residual_topk_channels(xg, *qa[:3], k, scores=qa[3])
+        resid = resid.contiguous()
+    log(f"[gemm] fused combine small k={k} {path} P={P}")
+    for rep in range(2):
+        cout = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
+        ob, _ = nvq.moe_grouped_gemm_w4a4_comp(qa[0], qa[1], qa[2], qw[0], qw[1], qw[2], off, rows=P,
+                                               a_resid=resid, comp_idx=idx, path=_path(path),
+                                               comb=(sp, pos, wts, cout))
+        ref = nvq.nvq_moe_combine(ob, pos, wts)
+        torch.cuda.synchronize()
+        assert_bits_equal(to_np(cout), to_np(ref), f"fused combine call {rep}")
+        assert not to_np(cout)[7].any(), "token with every pair dropped"
+
+
 def test_prefill_down_full_size_sampled():
     """Full-size prefill down projection (K=1536, N=4096, k=128, P=262144 rows)
     in the benchmark's launch configuration, on an independently drawn H of the
@@ -490,6 +552,7 @@ def test_prefill_down_full_size_sampled():
     rows = _sample_rows(ooff, every=1499)
     row_e = np.searchsorted(ooff, rows, side="right") - 1
     _check_sampled(nvq, s, to_np(y2)[rows], rows, rows.astype(np.int32), row_e, oqh, hb, oidx2, w, q, "down")
+    _check_fused_combine(nvq, s, logits, qh, idx2, r2, q, cm, ooff)
 
 
 def test_decode_down_full_size_sampled():
@@ -519,3 +582,4 @@ def test_decode_down_full_size_sampled():
     row_e = np.searchsorted(ooff, rows, side="right") - 1
     _check_sampled(nvq, s, to_np(y2)[rows], rows, rows.astype(np.int32), row_e, oqh, hb, oidx2, w, q,
                    "decode down")
+    _check_fused_combine(nvq, s, inputs.logits(s), qh, idx2, r2, q, cm, ooff)

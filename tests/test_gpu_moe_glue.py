@@ -114,3 +114,36 @@ def test_combine_with_dropped_pairs(topk, N):
     ref = oracle.combine_bf16(inputs.bf16_bits_to_f32(y), opos, w)
     np.testing.assert_allclose(inputs.bf16_bits_to_f32(to_np(out)), inputs.bf16_bits_to_f32(ref),
                                rtol=2 ** -7, atol=1e-6)
+
+
+@pytest.mark.parametrize("topk,N,T", [(8, 2048, 333), (9, 80, 50), (2, 16, 1)])
+def test_combine_records_the_amax_of_its_output(topk, N, T):
+    """out_amax = max |out| over the stored bf16 output (both combine
+    kernels, ragged last vectors), and quantizing out with it as amax_in gives
+    the same record and scores as quantizing with its own amax pass."""
+    import torch
+
+    nvq = _nvq()
+    g = np.random.default_rng(topk * 7 + N + T)
+    E = 16
+    ids = np.stack([g.permutation(E)[:topk] for _ in range(T)]).astype(np.int32)
+    sp, off, pos, _ = nvq.nvq_moe_permute(to_gpu(ids), E)
+    P = int(to_np(off)[-1])
+    y = inputs.to_bf16_bits((g.standard_t(3, (P, N)) * 3).astype(np.float32))
+    w = g.random((T, topk)).astype(np.float32)
+    amax = torch.full((1,), 123.0, dtype=torch.float32, device="cuda")  # overwritten
+    out = nvq.nvq_moe_combine(to_gpu(y), pos, to_gpu(w), out_amax=amax)
+    q_own = nvq.nvfp4_quantize(out, score=True)
+    q_in = nvq.nvfp4_quantize(out, amax_in=amax, score=True)
+    torch.cuda.synchronize()
+    outf = inputs.bf16_bits_to_f32(to_np(out))
+    assert float(to_np(amax)[0]) == float(np.abs(outf).max())
+    for a, b, what in zip(q_own[:4], q_in[:4], ("codes", "scales", "s_t", "scores")):
+        assert_bits_equal(to_np(b), to_np(a), f"quantize with the combine's amax: {what}")
+    # no tokens: the maximum of nothing is 0
+    empty = nvq.nvq_moe_combine(torch.empty(0, N, dtype=torch.bfloat16, device="cuda"),
+                                torch.empty(0, dtype=torch.int32, device="cuda"),
+                                torch.empty(0, topk, dtype=torch.float32, device="cuda"),
+                                out_amax=amax)
+    torch.cuda.synchronize()
+    assert empty.shape == (0, N) and float(to_np(amax)[0]) == 0.0
