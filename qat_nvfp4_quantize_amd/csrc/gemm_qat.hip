@@ -575,8 +575,11 @@ __global__ __launch_bounds__(256, 2) void k_qat_fwd2(QatParams p) {
   // Pipeline over step pairs: each step first issues the A tile (into the
   // other LDS buffer) and the B stage of the next step, runs its MFMAs, then
   // waits for every load of this thread and meets the other waves at a
-  // barrier, so a load has one step of MFMA work to land.  An odd step count
-  // ends with one more step outside the loop.
+  // barrier, so a load has one step of MFMA work to land.  The scheduling
+  // barriers keep the loads ahead of the MFMAs (the compiler otherwise sinks
+  // them to the wait).  A load past the last step re-reads the last one
+  // into the idle buffer; it has landed by the loop's final wait.  An odd
+  // step count ends with one more step outside the loop.
   QStage X0, X1;
   a_load(0, 0);
   b_load(X0, 0);
@@ -587,13 +590,13 @@ __global__ __launch_bounds__(256, 2) void k_qat_fwd2(QatParams p) {
     const int st = 2 * it;
     a_load(1, st + 1);
     b_load(X1, st + 1);
+    __builtin_amdgcn_sched_barrier(0);
     mfma_step(X0, 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (st + 2 < nst) {
-      a_load(0, st + 2);
-      b_load(X0, st + 2);
-    }
+    a_load(0, st + 2);
+    b_load(X0, st + 2);
+    __builtin_amdgcn_sched_barrier(0);
     mfma_step(X1, 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();

@@ -676,8 +676,12 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
 
   // Pipeline: while the waves run the MFMAs of step s from LDS buffer s & 1,
   // step s + 1 (in registers) is dequantized into the other buffer; each
-  // register stage is loaded two steps before its MFMAs.  The loop covers
-  // step pairs; an odd step count adds one zero-scaled step.
+  // register stage is loaded right after the barrier that frees it, about
+  // one step before its A half is stored and its MFMAs run.  The
+  // scheduling barriers pin the loads there: left to itself the compiler
+  // sinks them into the next MFMA sequence (it reuses their registers as
+  // dequantization temporaries first), and the A half then arrives late.
+  // The loop covers step pairs; an odd step count adds one zero-scaled step.
   Stage<false> X0, X1;
   gload(X0, 0);
   gload(X1, 1);
@@ -688,10 +692,12 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
     a_store(X1, 1, st + 1 < nst);
     __syncthreads();
     gload(X0, st + 2);
+    __builtin_amdgcn_sched_barrier(0);
     mfma_step(X1, 1);
     a_store(X0, 0, st + 2 < nst);
     __syncthreads();
     gload(X1, st + 3);
+    __builtin_amdgcn_sched_barrier(0);
   }
   comp_phase(p, c, acc, lds[0], a_tok, b_n);
   epilogue<kSwiglu>(p, c, acc, &lds[0][0][0]);
