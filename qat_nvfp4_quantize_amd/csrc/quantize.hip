@@ -554,6 +554,104 @@ __global__ __launch_bounds__(512, 2) void k_quantize(
   if (wave_or_u32(bad) && lane == 0) atomicOr(status, (uint32_t)NVQ_STATUS_NONFINITE);
 }
 
+// Scored quantization with one 16-element block per thread, for tensors
+// whose row tile would leave CUs idle (few rows): workgroup = one 128-row
+// score chunk x 64 columns, thread t = row t / 4, block column t % 4.  Each
+// thread writes its block's 16 residual magnitudes to LDS; lane c of wave w
+// then adds column c over rows 16 w .. 16 w + 15 in order (a sub-chunk sum),
+// and thread c < 64 adds the 8 sub-chunk sums in order: the row tile's order,
+// so the chunk partials, and the scores after k_score_reduce, are
+// bit-identical to the row tile's.  Sixteen times the threads of the row
+// tile for the same bytes.
+constexpr int kTbCols = 64;
+constexpr int kTbMaxRowTileWgs = 1;  // row-tile workgroups per CU below which k_quantize_tb runs
+template <bool kBF16>
+__global__ __launch_bounds__(512) void k_quantize_tb(
+    const void* __restrict__ xv, int64_t rows, int64_t K, int64_t ldx,
+    const uint32_t* __restrict__ amax_partial, int n_partial, const float* __restrict__ amax_in,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ tensor_scale,
+    float* __restrict__ chunk_partial, uint32_t* __restrict__ status) {
+  __shared__ float s_r[kQRows][kTbCols + 1];  // +1: a write instruction's rows hit distinct banks
+  __shared__ float s_sub[kQRows / kQSub][kTbCols];
+  __shared__ uint32_t s_slot[512 * (kBF16 ? 8 : 16)];
+  __shared__ uint32_t s_wmax[8];
+  __shared__ float s_amax;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int rr = t >> 2, b = t & 3;
+  uint32_t* slot = s_slot + t * (kBF16 ? 8 : 16);
+  const int64_t nblk = K >> 4;
+  const int64_t blk = (int64_t)blockIdx.x * (kTbCols / 16) + b;
+  const int64_t row = (int64_t)blockIdx.y * kQRows + rr;
+  const bool active = blk < nblk && row < rows;
+  RowBlock<kBF16> rb;
+  if (active) rb.load(xv, row, ldx, blk);  // in flight before the tensor amax is known
+
+  {
+    uint32_t m = 0;
+    if (amax_in) {
+      m = __float_as_uint(amax_in[0]);
+    } else {
+      for (int i = t; i < n_partial; i += 512) m = max(m, amax_partial[i]);
+      m = wave_max_u32(m);
+    }
+    if (lane == 0) s_wmax[wave] = m;
+    __syncthreads();
+    if (t == 0) {
+      uint32_t r = s_wmax[0];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) r = max(r, s_wmax[w]);
+      s_amax = __uint_as_float(r);
+    }
+  }
+  __syncthreads();
+  const float amax = s_amax;
+  const float s_t = (float)((double)amax / 2688.0);  // fl32(amax / 2688), as in k_quantize
+  if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) tensor_scale[0] = s_t;
+  const double six_st = 6.0 * (double)s_t;
+  const bool fast = (s_t >= 0x1p-100f) && (s_t <= 0x1p100f);
+  const float g = fast ? (float)(1.0 / six_st) : 0.0f;
+  const float inv_st = fast ? (float)(1.0 / (double)s_t) : 0.0f;
+
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+  uint32_t bad = 0;
+  if (active) {
+    uint32_t sc;
+    uint2 cw;
+    if (fast)
+      encode_block_fast<kBF16, true>(rb, s_t, g, inv_st, sc, cw, acc, bad, slot);
+    else
+      encode_block_exact<kBF16, true>(rb, s_t, six_st, sc, cw, acc, bad, slot);
+    *reinterpret_cast<uint2*>(codes + row * (K >> 1) + blk * 8) = cw;
+    scales[row * nblk + blk] = (uint8_t)sc;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s_r[rr][16 * b + j] = acc[j];
+  __syncthreads();
+  {
+    // wave w: the sub-chunk sums of rows 16 w .. 16 w + 15, lane = column
+    const int nr = (int)max<int64_t>(0, min<int64_t>(kQRows, rows - (int64_t)blockIdx.y * kQRows));
+    float v[kQSub];
+#pragma unroll
+    for (int q = 0; q < kQSub; ++q) v[q] = s_r[kQSub * wave + q][lane];
+    float sub = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kQSub; ++q)
+      if (kQSub * wave + q < nr) sub += v[q];
+    s_sub[wave][lane] = sub;
+  }
+  __syncthreads();
+  if (t < kTbCols) {
+    const int64_t col = (int64_t)blockIdx.x * kTbCols + t;
+    float P = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kQRows / kQSub; ++w) P += s_sub[w][t];
+    if (col < K) chunk_partial[(int64_t)blockIdx.y * K + col] = P;
+  }
+  if (wave_or_u32(bad) && lane == 0) atomicOr(status, (uint32_t)NVQ_STATUS_NONFINITE);
+}
+
 // Score-free quantization: without residual sums there is no row order to
 // keep, so thread t of item z takes blocks t, t + T, t + 2T, ... of the item's
 // flat block list (block f = elements 16f..16f+15 of the row-major tensor,
@@ -1099,7 +1197,11 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
   // once (two 512-thread workgroups per CU), so both launches place workgroup
   // i on the same XCD at about the same time; larger grids take the flat pass.
   const int64_t qwgs = (int64_t)qgrid.x * qgrid.y;
-  if (!amax_in && score && qwgs <= 1024 && qwgs <= 2 * device_cu_count()) {
+  // A scored row tile with fewer workgroups than CUs leaves the chip mostly
+  // idle (each wave walks 16 rows); the thread-per-block tile computes the
+  // same chunk partials with sixteen times the threads, after the flat amax.
+  const bool tb = score && qwgs < kTbMaxRowTileWgs * (int64_t)device_cu_count();
+  if (!amax_in && score && !tb && qwgs <= 1024 && qwgs <= 2 * device_cu_count()) {
     n_partial = (int)L.n_partial_tiles;
     if (bf16)
       hipLaunchKernelGGL(k_amax_tiles<true>, dim3(qgrid.x, qgrid.y), dim3(512), 0, s, x, rows, K, ldx,
@@ -1144,6 +1246,19 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
     else
       hipLaunchKernelGGL(k_quantize_flat<false>, fgrid, dim3(kFlatThreads), 0, s, x, nb_item,
                          L.amax_partial, L.n_partial, amax_in, codes, scales, tensor_scale, L.status);
+    return last_launch();
+  }
+  if (tb) {
+    const dim3 tgrid((unsigned)((K + kTbCols - 1) / kTbCols), (unsigned)L.nchunks);
+    if (bf16)
+      hipLaunchKernelGGL(k_quantize_tb<true>, tgrid, dim3(512), 0, s, x, rows, K, ldx, L.amax_partial,
+                         n_partial, amax_in, codes, scales, tensor_scale, L.chunk_partial, L.status);
+    else
+      hipLaunchKernelGGL(k_quantize_tb<false>, tgrid, dim3(512), 0, s, x, rows, K, ldx, L.amax_partial,
+                         n_partial, amax_in, codes, scales, tensor_scale, L.chunk_partial, L.status);
+    if (int rc = last_launch()) return rc;
+    hipLaunchKernelGGL(k_score_reduce, dim3((unsigned)((K + kScoreCols - 1) / kScoreCols)), dim3(256), 0, s,
+                       L.chunk_partial, L.nchunks, K, chan_score);
     return last_launch();
   }
 #define NVQ_LAUNCH_Q(B, S)                                                                    \
