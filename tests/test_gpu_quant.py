@@ -260,3 +260,40 @@ def test_row_strided_input(rows, K, ldx, dtype):
         assert_bits_equal(to_np(stb)[b:b + 1], np.array([ost], np.float32), f"item {b} s_t")
         assert_bits_equal(to_np(cb)[b], oc, f"item {b} codes")
         assert_bits_equal(to_np(sb)[b], os_, f"item {b} scales")
+
+
+@pytest.mark.parametrize("case", ["bf16", "f32_tiny_scale", "bf16_strided"])
+def test_row_tile_edges(case):
+    """The row-tile kernel on ragged edges.  Scored calls on tensors with few
+    rows run the thread-per-block tile, so the small cases above exercise
+    that one; 80017 rows x 48 columns gives the row tile 626 workgroups (more
+    than two per CU), with a partial last chunk and 3 of 64 lanes active per
+    row.  Also the fp64 path of extreme tensor scales and a row stride."""
+    import torch
+
+    nvq = _nvq()
+    rows, K = 80017, 48
+    g = np.random.default_rng({"bf16": 1, "f32_tiny_scale": 2, "bf16_strided": 3}[case])
+    x = (g.standard_t(3, (rows, K)) * np.exp(g.uniform(-4, 4, (rows, 1)))).astype(np.float32)
+    x[g.random((rows, K)) < 0.03] = 0.0
+    if case == "f32_tiny_scale":
+        x = (x * np.float32(1e-38)).astype(np.float32)  # tensor scale below 2^-100: the fp64 path
+        _check_quant(x, k=5, what="row tile f32 tiny scale")
+        return
+    if case == "bf16":
+        _check_quant(inputs.to_bf16_bits(x), k=5, what="row tile bf16")
+        return
+    ldx = 64
+    wide = np.full((rows, ldx), 3e38, np.float32)
+    wide[:, :K] = x
+    wide = inputs.to_bf16_bits(wide)
+    log(f"[quant] row tile strided {rows}x{K} ldx={ldx}")
+    xg = to_gpu(wide)[:, :K]
+    codes, scales, st, score, ws = nvq.nvfp4_quantize(xg, score=True)
+    torch.cuda.synchronize()
+    oc, os_, ost = oracle.quantize(wide, K=K)
+    assert_bits_equal(to_np(st), np.array([ost], np.float32), "row tile strided s_t")
+    assert_bits_equal(to_np(codes), oc, "row tile strided codes")
+    assert_bits_equal(to_np(scales), os_, "row tile strided scales")
+    assert_bits_equal(to_np(score), oracle.residual_scores(wide, oc, os_, ost, K=K), "row tile strided scores")
+    assert nvq.device_status(ws) == 0
