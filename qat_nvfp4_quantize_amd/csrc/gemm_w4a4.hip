@@ -260,60 +260,76 @@ __device__ __forceinline__ uint32_t wq_bf16(uint32_t nib, uint32_t sc) {
 }
 
 // The compensation weights from the channel-major record: wcomp[e, n, j] =
-// bf16 of G * s_b at channel idx[j] (0 for j >= k).  Thread = rows n, n + 1
-// of one expert and channels 8 q .. 8 q + 7 (blockIdx.y = q): eight
-// independent (code byte, two scale bytes) loads from those channels'
-// contiguous rows, then one 16-byte store per row.  Lanes run along n, so
-// every load instruction reads consecutive bytes.  k is a multiple of 8, so
-// a group of 8 channels is either wholly below k or wholly past it; all
-// loads are unconditional and issued before the first wait, and the decode
-// is branch-free (the hardware FP4 conversion gives both rows' G, signed;
-// G * s_b has at most 6 significant bits, so its bf16 is exact).
-__global__ __launch_bounds__(256) void k_gather_wcomp_cm(const uint8_t* __restrict__ codes_cm,
-                                                        const uint8_t* __restrict__ scales_cm, int64_t N,
-                                                        int64_t K, const int32_t* __restrict__ idx, int k,
-                                                        int kpad, uint16_t* __restrict__ wcomp) {
+// bf16 of G * s_b at channel idx[j] (0 for j >= k).  Workgroup = 64 weight
+// rows x one 64-channel slice of wcomp (blockIdx.y) of one expert.  Thread t
+// takes rows 2 (t % 32), + 1 and channels 8 (t / 32) .. + 7 of the slice:
+// eight independent (code byte, two scale bytes) loads from those channels'
+// contiguous rows (lanes along the rows, so each load instruction reads
+// consecutive bytes; k is a multiple of 8, so a group of 8 channels is wholly
+// below k or past it), decoded branch-free (the hardware FP4 conversion gives
+// both rows' G, signed; G * s_b has at most 6 significant bits, so its bf16
+// is exact) into an LDS tile.  Then each group of 8 threads stores one row's
+// 128 slice bytes as 16-byte pieces, so every output line is written whole
+// by one workgroup.
+constexpr int kWcRows = 64, kWcCh = 64, kWcPitch = kWcCh + 8;  // tile pitch in bf16 (+16 bytes)
+__global__ __launch_bounds__(256) void k_gather_wcomp_rows(const uint8_t* __restrict__ codes_cm,
+                                                          const uint8_t* __restrict__ scales_cm, int64_t N,
+                                                          int64_t K, const int32_t* __restrict__ idx, int k,
+                                                          int kpad, uint16_t* __restrict__ wcomp) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kWcRows][kWcPitch];
   const int64_t e = blockIdx.z;
-  const int j0 = 8 * (int)blockIdx.y;
-  const int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
-  if (n >= N || j0 >= kpad) return;
-  uint16_t* o0 = wcomp + (e * N + n) * kpad + j0;
-  if (j0 >= k) {
-    *reinterpret_cast<uint4*>(o0) = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(o0 + kpad) = make_uint4(0, 0, 0, 0);
-    return;
-  }
-  const uint8_t* cb = codes_cm + e * K * (N >> 1) + (n >> 1);
-  const uint8_t* sb = scales_cm + e * (K >> 4) * N + n;
-  int64_t ch[8];
+  const int64_t n0 = (int64_t)blockIdx.x * kWcRows;
+  const int c0 = kWcCh * (int)blockIdx.y;
+  const int t = threadIdx.x, q = t >> 5, rp = t & 31;
+  const int j0 = c0 + 8 * q;
+  const int64_t n = n0 + 2 * rp;
+  if (j0 < kpad) {
+    uint4 o0 = make_uint4(0, 0, 0, 0), o1 = make_uint4(0, 0, 0, 0);
+    if (j0 < k && n < N) {
+      const uint8_t* cb = codes_cm + e * K * (N >> 1) + (n >> 1);
+      const uint8_t* sb = scales_cm + e * (K >> 4) * N + n;
+      int64_t ch[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) ch[u] = idx[j0 + u];
-  uint32_t byte[8], sc[8];
+      for (int u = 0; u < 8; ++u) ch[u] = idx[j0 + u];
+      uint32_t byte[8], sc[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    byte[u] = cb[ch[u] * (N >> 1)];
-    sc[u] = *reinterpret_cast<const uint16_t*>(sb + (ch[u] >> 4) * N);
-  }
-  auto e4m3 = [](uint32_t c) {  // c <= 0x7E
-    const float nrm = __uint_as_float(((c & 0x7Fu) << 20) + (120u << 23));
-    const float sub = (float)(c & 7u) * 0x1p-9f;
-    return (c & 0x78u) ? nrm : sub;
-  };
-  uint32_t r0[4], r1[4];
+      for (int u = 0; u < 8; ++u) {
+        byte[u] = cb[ch[u] * (N >> 1)];
+        sc[u] = *reinterpret_cast<const uint16_t*>(sb + (ch[u] >> 4) * N);
+      }
+      auto e4m3 = [](uint32_t c) {  // c <= 0x7E
+        const float nrm = __uint_as_float(((c & 0x7Fu) << 20) + (120u << 23));
+        const float sub = (float)(c & 7u) * 0x1p-9f;
+        return (c & 0x78u) ? nrm : sub;
+      };
+      uint32_t r0[4], r1[4];
 #pragma unroll
-  for (int u = 0; u < 8; u += 2) {
-    uint32_t lo[2], hi[2];
+      for (int u = 0; u < 8; u += 2) {
+        uint32_t lo[2], hi[2];
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const auto g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte[u + v], 1.0f, 0);
-      lo[v] = __float_as_uint(g[0] * e4m3(sc[u + v] & 0xFFu)) >> 16;
-      hi[v] = __float_as_uint(g[1] * e4m3(sc[u + v] >> 8)) >> 16;
+        for (int v = 0; v < 2; ++v) {
+          const auto g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte[u + v], 1.0f, 0);
+          lo[v] = __float_as_uint(g[0] * e4m3(sc[u + v] & 0xFFu)) >> 16;
+          hi[v] = __float_as_uint(g[1] * e4m3(sc[u + v] >> 8)) >> 16;
+        }
+        r0[u >> 1] = lo[0] | (lo[1] << 16);
+        r1[u >> 1] = hi[0] | (hi[1] << 16);
+      }
+      o0 = make_uint4(r0[0], r0[1], r0[2], r0[3]);
+      o1 = make_uint4(r1[0], r1[1], r1[2], r1[3]);
     }
-    r0[u >> 1] = lo[0] | (lo[1] << 16);
-    r1[u >> 1] = hi[0] | (hi[1] << 16);
+    *reinterpret_cast<uint4*>(&tile[2 * rp][8 * q]) = o0;
+    *reinterpret_cast<uint4*>(&tile[2 * rp + 1][8 * q]) = o1;
   }
-  *reinterpret_cast<uint4*>(o0) = make_uint4(r0[0], r0[1], r0[2], r0[3]);
-  *reinterpret_cast<uint4*>(o0 + kpad) = make_uint4(r1[0], r1[1], r1[2], r1[3]);
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = (t >> 3) + 32 * h, cq = t & 7;
+    const int64_t nr = n0 + r;
+    if (nr < N && c0 + 8 * cq < kpad)
+      *reinterpret_cast<uint4*>(wcomp + (e * N + nr) * kpad + c0 + 8 * cq) =
+          *reinterpret_cast<const uint4*>(&tile[r][8 * cq]);
+  }
 }
 
 // The tile of this workgroup.  XCD-aware order: the grid is sized for the
@@ -1214,7 +1230,9 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   p.a_resid = a->a_resid; p.comp_idx = a->comp_idx; p.k = a->k;
   p.kpad = L.kpad; p.wcomp = L.wcomp;
   if (a->k > 0 && has_cm) {
-    hipLaunchKernelGGL(k_gather_wcomp_cm, dim3((unsigned)((a->N + 511) / 512), (unsigned)(L.kpad / 8), (unsigned)a->E),
+    hipLaunchKernelGGL(k_gather_wcomp_rows,
+                       dim3((unsigned)((a->N + kWcRows - 1) / kWcRows), (unsigned)((L.kpad + kWcCh - 1) / kWcCh),
+                            (unsigned)a->E),
                        dim3(256), 0, s, a->w_codes_cm, a->w_scales_cm, a->N, a->K, a->comp_idx, (int)a->k, L.kpad,
                        L.wcomp);
     if (int rc = last_launch()) return rc;
