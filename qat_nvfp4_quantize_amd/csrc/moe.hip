@@ -19,6 +19,7 @@ namespace nvq {
 namespace {
 
 constexpr int kPermChunk = 1024;  // pairs per histogram/scatter chunk
+constexpr int64_t kPermOwnBaseChunks = 64;  // at most this many chunks: no scan kernel
 
 // Order-preserving key of an fp32 logit (non-NaN), -0 folded onto +0.
 __device__ __forceinline__ uint32_t ordered_key(float f) {
@@ -87,26 +88,25 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   }
 }
 
-// Per-chunk expert histogram.
+// Per-chunk expert histogram (ids outside [0, E) are not counted; the
+// scatter reports them).  Also clears the status word, ahead of the scatter.
 __global__ __launch_bounds__(256) void k_perm_hist(const int32_t* __restrict__ ids, int64_t P, int E,
                                                   int32_t* __restrict__ counts,
                                                   uint32_t* __restrict__ status) {
   extern __shared__ int32_t h[];
   for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0u;
   __syncthreads();
   const int64_t p0 = (int64_t)blockIdx.x * kPermChunk;
-  uint32_t bad = 0;
   for (int i = threadIdx.x; i < kPermChunk; i += 256) {
     const int64_t p = p0 + i;
     if (p < P) {
       const int32_t e = ids[p];
       if (e >= 0 && e < E) atomicAdd(&h[e], 1);
-      else bad = 1;
     }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) counts[(int64_t)blockIdx.x * E + e] = h[e];
-  if (bad) atomicOr(status, (uint32_t)NVQ_STATUS_BAD_EXPERT);
 }
 
 // One workgroup: base[c][e] = offset of expert e + pairs of e in chunks < c.
@@ -164,14 +164,69 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts
 // Stable scatter: one wave per chunk walks its pairs in order 64 at a time;
 // the rank of a pair among equal experts in a step is the popcount of the
 // lower lanes whose expert matches (found with log2(E) ballots).
+// kOwnBase: counts holds the chunk histograms (not yet scanned), and the wave
+// derives its chunk's bases itself: expert e's offset (the in-order sum of the
+// totals of experts < e) plus e's pairs in earlier chunks; chunk 0 writes the
+// expert offsets.  For few chunks this replaces k_perm_scan.  Reports ids
+// outside [0, E) in the status word.
+template <bool kOwnBase>
 __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__ ids, int64_t P,
-                                                    int E, const int32_t* __restrict__ base,
+                                                    int E, int64_t nchunks, const int32_t* __restrict__ base,
+                                                    int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ sorted_pair,
-                                                    int32_t* __restrict__ pos) {
+                                                    int32_t* __restrict__ pos, uint32_t* __restrict__ status) {
   extern __shared__ int32_t cnt[];
   const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) cnt[e] = base[(int64_t)blockIdx.x * E + e];
+  if (kOwnBase) {
+    // lane l owns experts [l * per, (l + 1) * per); before: e's pairs in
+    // chunks < this one, tot: in all chunks
+    const int per = (E + 63) / 64;
+    const int c = (int)blockIdx.x;
+    int32_t run = 0;  // this lane's experts' totals, in expert order
+    for (int q = 0; q < per; ++q) {
+      const int e = lane * per + q;
+      int32_t before = 0, tot = 0;
+      if (e < E) {
+        for (int64_t c0 = 0; c0 < nchunks; c0 += 16) {  // 16 loads in flight, then the adds
+          int32_t v[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) v[u] = base[min<int64_t>(c0 + u, nchunks - 1) * E + e];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int64_t cc = c0 + u;
+            tot += cc < nchunks ? v[u] : 0;
+            before += cc < c ? v[u] : 0;
+          }
+        }
+        cnt[e] = run + before;  // offset within this lane's range, fixed below
+      }
+      run += tot;
+    }
+    // exclusive scan of the lane totals over the wave
+    int32_t incl = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    const int32_t lane_off = incl - run;
+    for (int q = 0; q < per; ++q) {
+      const int e = lane * per + q;
+      if (e < E) cnt[e] += lane_off;
+    }
+    if (c == 0) {
+      // offsets[e] = bases of chunk 0 (no earlier chunks); offsets[E] = all pairs
+      for (int q = 0; q < per; ++q) {
+        const int e = lane * per + q;
+        if (e < E) offsets[e] = cnt[e];
+      }
+      if (lane == 63) offsets[E] = incl;
+    }
+  } else {
+    for (int e = lane; e < E; e += 64) cnt[e] = base[(int64_t)blockIdx.x * E + e];
+  }
   __syncthreads();
+  uint32_t bad = 0;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -181,6 +236,7 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__
     const bool in = p < P;
     int32_t e = in ? ids[p] : -1;
     const bool ok = in && e >= 0 && e < E;
+    bad |= (in && !ok) ? 1u : 0u;
     if (!ok) e = -1;
     uint64_t match = __ballot(ok);
     for (int b = 0; b < nbits; ++b) {
@@ -201,6 +257,7 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__
     if (in) pos[p] = dst;
     __syncthreads();
   }
+  if (__any(bad) && lane == 0) atomicOr(status, (uint32_t)NVQ_STATUS_BAD_EXPERT);
 }
 
 // max |value| of the 8 bf16 of a packed uint4, as 16-bit magnitude bits
@@ -472,16 +529,24 @@ extern "C" int nvq_moe_permute(const int32_t* ids, int64_t T, int64_t topk, int6
   int32_t* counts = c.take<int32_t>((size_t)(nchunks * E));
   if (ws_bytes < c.off) return NVQ_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (int rc = clear_status(c.status(), s)) return rc;
   hipLaunchKernelGGL(k_perm_hist, dim3((unsigned)nchunks), dim3(256), E * sizeof(int32_t), s, ids, P,
                      (int)E, counts, c.status());
   if (int rc = last_launch()) return rc;
-  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, counts, nchunks, (int)E,
-                     expert_offsets);
-  if (int rc = last_launch()) return rc;
+  // Few chunks: each scatter wave sums the histograms itself (reading them
+  // all costs less than a separate scan launch); many: one scan workgroup.
+  const bool own_base = nchunks <= kPermOwnBaseChunks && P > 0;
+  if (!own_base) {
+    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, counts, nchunks, (int)E,
+                       expert_offsets);
+    if (int rc = last_launch()) return rc;
+  }
   if (P == 0) return NVQ_OK;
-  hipLaunchKernelGGL(k_perm_scatter, dim3((unsigned)nchunks), dim3(64), E * sizeof(int32_t), s, ids,
-                     P, (int)E, counts, sorted_pair, pos);
+  if (own_base)
+    hipLaunchKernelGGL(k_perm_scatter<true>, dim3((unsigned)nchunks), dim3(64), E * sizeof(int32_t), s, ids,
+                       P, (int)E, nchunks, counts, expert_offsets, sorted_pair, pos, c.status());
+  else
+    hipLaunchKernelGGL(k_perm_scatter<false>, dim3((unsigned)nchunks), dim3(64), E * sizeof(int32_t), s, ids,
+                       P, (int)E, nchunks, counts, expert_offsets, sorted_pair, pos, c.status());
   return last_launch();
 }
 

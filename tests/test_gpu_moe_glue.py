@@ -37,6 +37,25 @@ def test_route_and_permute(shape):
     assert nvq.device_status(ws) == 0
 
 
+@pytest.mark.parametrize("T,topk,E", [(5000, 4, 300), (8192, 8, 1024), (16384, 4, 128), (16385, 4, 128),
+                                     (1, 1, 7)])
+def test_permute_chunk_counts_and_wide_expert_sets(T, topk, E):
+    """The permutation with the scatter deriving its own bases (at most 64
+    chunks of 1024 pairs) and with the scan kernel (65 chunks and more):
+    expert counts above 64 per lane group (E = 300, 1024), the 64 / 65 chunk
+    boundary, a single pair; skewed ids leave experts empty."""
+    nvq = _nvq()
+    g = np.random.default_rng(T + E)
+    ids = np.minimum(g.zipf(1.3, (T, topk)) - 1, E - 1).astype(np.int32)
+    log(f"[permute] T={T} topk={topk} E={E} chunks={(T * topk + 1023) // 1024}")
+    sp, off, pos, ws = nvq.nvq_moe_permute(to_gpu(ids), E)
+    osp, ooff, opos = oracle.permute(ids, E)
+    assert_bits_equal(to_np(off), ooff, "offsets")
+    assert_bits_equal(to_np(sp), osp, "sorted_pair")
+    assert_bits_equal(to_np(pos), opos, "pos")
+    assert nvq.device_status(ws) == 0
+
+
 def test_route_ties_and_negative_zero():
     nvq = _nvq()
     g = np.random.default_rng(3)
