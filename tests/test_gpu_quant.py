@@ -297,3 +297,44 @@ def test_row_tile_edges(case):
     assert_bits_equal(to_np(scales), os_, "row tile strided scales")
     assert_bits_equal(to_np(score), oracle.residual_scores(wide, oc, os_, ost, K=K), "row tile strided scores")
     assert nvq.device_status(ws) == 0
+
+
+@pytest.mark.parametrize("case", ["ragged", "strided", "partial_grid", "tiny_scale", "nonfinite"])
+def test_sweep_size_ragged_edges(case):
+    """Scored bf16 tensors of about the sweep's size with ragged edges:
+    8100 x 7008 has a partial last chunk (36 rows) and a partial last group of
+    block columns; 6200 x 7168 leaves part of the chip idle in the last wave of
+    workgroups; a row stride; a tensor scale below 2^-100 (fp64 decisions);
+    and an infinite element (status)."""
+    import torch
+
+    nvq = _nvq()
+    rows, K, ldx = {"ragged": (8100, 7008, None), "strided": (8192, 7168, 7200),
+                    "partial_grid": (6200, 7168, None), "tiny_scale": (8192, 7168, None),
+                    "nonfinite": (8192, 7168, None)}[case]
+    g = np.random.default_rng({"ragged": 11, "strided": 12, "partial_grid": 13, "tiny_scale": 14,
+                               "nonfinite": 15}[case])
+    x = g.standard_t(4, (rows, K)).astype(np.float32)
+    x[:, g.random(K) < 0.005] *= 50.0
+    if case == "tiny_scale":
+        x = (x * np.float32(1e-31)).astype(np.float32)
+    if case == "nonfinite":
+        x[4097, 3001] = np.inf
+        _, _, _, _, ws = nvq.nvfp4_quantize(to_gpu(inputs.to_bf16_bits(x)), score=True)
+        assert nvq.device_status(ws) & nvq.NVQ_STATUS_NONFINITE
+        return
+    if ldx is None:
+        _check_quant(inputs.to_bf16_bits(x), what=f"sweep-size {case}")
+        return
+    wide = np.full((rows, ldx), 3e38, np.float32)
+    wide[:, :K] = x
+    wide = inputs.to_bf16_bits(wide)
+    log(f"[quant] sweep-size strided {rows}x{K} ldx={ldx}")
+    codes, scales, st, score, ws = nvq.nvfp4_quantize(to_gpu(wide)[:, :K], score=True)
+    torch.cuda.synchronize()
+    oc, os_, ost = oracle.quantize(wide, K=K)
+    assert_bits_equal(to_np(st), np.array([ost], np.float32), "sweep-size strided s_t")
+    assert_bits_equal(to_np(codes), oc, "sweep-size strided codes")
+    assert_bits_equal(to_np(scales), os_, "sweep-size strided scales")
+    assert_bits_equal(to_np(score), oracle.residual_scores(wide, oc, os_, ost, K=K), "sweep-size strided scores")
+    assert nvq.device_status(ws) == 0
