@@ -381,12 +381,63 @@ __device__ __forceinline__ int64_t loader_b_row(const GemmParams& p, const TileC
   return min<int64_t>(b_row_to_n(WN * wave + 32 * j + l32, c.nt, kSwiglu, p.N), p.N - 1);
 }
 
+// Direct global -> LDS load of 16 bytes per lane: lane l lands at LDS byte
+// lds_addr + 16 l (lds_addr wave-uniform, read from the first lane).  Issued
+// from inline assembly, so the compiler places no wait for it in front of
+// unrelated LDS reads; the reader waits (vmcnt) and synchronizes itself.
+#define NVQ_LDS_U8 __attribute__((address_space(3))) uint8_t
+__device__ __forceinline__ void dma16_lds(const void* g, uint32_t lds_addr) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
+}
+
+// The compensation operands of the first 128-channel step, fetched while
+// the last main-loop MFMAs run (path DEQ16): the residual rows of the tile go
+// global -> LDS with direct loads into a compact tile of S = 8 (k <= 64) or
+// 16 slots of 16 bytes per row, slot s of row r stored at s ^ (r & (S - 1));
+// the weight fragments of its first kD sub-steps (16 channels each) go into
+// registers: 4 for the down projection, 3 with the SwiGLU epilogue (a fourth
+// would spill there).  s_tok[r]: the A source row of tile row r.
+template <int kD>
+struct CompPre {
+  uint4 w[2][kD];
+  int S;
+};
+template <int kD>
+__device__ __forceinline__ void comp_prefetch(const GemmParams& p, uint32_t lds0, const int32_t* s_tok,
+                                              const TileCtx& c, const int64_t (&b_n)[2], CompPre<kD>& cp) {
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, h = lane >> 5;
+  const int rem = min(p.k, SE);
+  cp.S = rem > 64 ? 16 : 8;
+  const int S = cp.S, nld = S / 2;  // 1 KB loads per wave: 128 rows x S slots / 4 waves
+  const int rl = lane / S, ps = lane & (S - 1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i < nld) {
+      const int g = nld * wave + i;  // load g covers tile rows (64 / S) g ..
+      const int r = (64 / S) * g + rl;
+      const int ls = ps ^ (r & (S - 1));
+      dma16_lds(p.a_resid + (int64_t)s_tok[r] * p.k + min(8 * ls, p.k - 8), lds0 + 1024u * g);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint16_t* w_src = p.wcomp + ((int64_t)c.e * p.N + b_n[j]) * p.kpad;
+#pragma unroll
+    for (int d = 0; d < kD; ++d)
+      if (16 * d < rem) cp.w[j][d] = *reinterpret_cast<const uint4*>(w_src + min(16 * d + 8 * h, p.kpad - 8));
+  }
+}
+
 // acc *= s_tA, then the compensation: 128-channel bf16 steps with the
 // residual rows through the LDS tile and the packed weight columns loaded in
-// fragment order.  Channels past k (kpad) read as zero.
+// fragment order.  Channels past k (kpad) read as zero.  With kPre, the first
+// step's operands were fetched by comp_prefetch into pre (residual tile at
+// the start of lds); later steps load their own.
+template <bool kPre, int kD>
 __device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c,
                                            floatx16_t (&acc)[4][2], uint8_t (*lds)[LROW],
-                                           int64_t a_tok, const int64_t (&b_n)[2]) {
+                                           int64_t a_tok, const int64_t (&b_n)[2], const CompPre<kD>& pre) {
   const float sta = *p.a_st;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -413,7 +464,47 @@ __device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c
     const uint32_t m = live ? 0xFFFFFFFFu : 0u;
     return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
   };
-  for (int cs = 0; cs < ncs; ++cs) {
+  int cs = 0;
+  if (kPre) {
+    // the prefetched first step: this lane's direct loads landed, then
+    // every wave's
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int rem = min(p.k, SE), S = pre.S;
+    const uint8_t* tile = &lds[0][0];
+    uint4 wl[2][8 - kD];  // sub-steps kD.., loaded now
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint16_t* w_src = p.wcomp + ((int64_t)c.e * p.N + b_n[j]) * p.kpad;
+#pragma unroll
+      for (int d = kD; d < 8; ++d)
+        if (16 * d < rem) wl[j][d - kD] = *reinterpret_cast<const uint4*>(w_src + min(16 * d + 8 * h, p.kpad - 8));
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      if (16 * d >= rem) break;
+      bf16x8_t af[4], bf[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 32 * i + l32;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(tile + 16 * (S * r + ((2 * d + h) ^ (r & (S - 1)))));
+      }
+      const bool live = 16 * d + 8 * h < rem;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4 v = keep(live, d < kD ? pre.w[j][d < kD ? d : 0] : wl[j][d < kD ? 0 : d - kD]);
+        __builtin_memcpy(&bf[j], &v, 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+    cs = 1;
+  }
+  for (; cs < ncs; ++cs) {
     const int rem = p.k - SE * cs;  // channels left, uniform
     uint4 rv[8], wv[2][8];
 #pragma unroll
@@ -615,6 +706,7 @@ struct Stage {
 template <int kSwiglu>
 __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM][LROW];
+  __shared__ int32_t s_tok[BM];  // A source row of each tile row (compensation prefetch)
   const TileCtx c = tile_of_block(p);
   if (!c.valid) return;
   const int64_t K = p.K, N = p.N;
@@ -628,6 +720,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
   // half h.
   const int ar = t >> 1, ahh = t & 1;
   const int64_t a_tok = loader_a_token(p, c, ar);
+  if (ahh == 0) s_tok[ar] = (int32_t)a_tok;  // read after the prologue's barrier
   const uint8_t* a_src = p.a_codes + a_tok * Kh + 32 * ahh;
   const uint8_t* a_ssrc = p.a_scales + a_tok * Kb + 4 * ahh;
   const uint8_t* b_src[2];
@@ -698,12 +791,15 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
   // sinks them into the next MFMA sequence (it reuses their registers as
   // dequantization temporaries first), and the A half then arrives late.
   // The loop covers step pairs; an odd step count adds one zero-scaled step.
+  // The last pair is peeled: instead of loading past the end it fetches the
+  // compensation operands, which then arrive under its last MFMAs.
   Stage<false> X0, X1;
   gload(X0, 0);
   gload(X1, 1);
   a_store(X0, 0, true);
   __syncthreads();
-  for (int st = 0; st < nst; st += 2) {
+  int st = 0;
+  for (; st + 2 < nst; st += 2) {
     mfma_step(X0, 0);
     a_store(X1, 1, st + 1 < nst);
     __syncthreads();
@@ -715,7 +811,15 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
     gload(X1, st + 3);
     __builtin_amdgcn_sched_barrier(0);
   }
-  comp_phase(p, c, acc, lds[0], a_tok, b_n);
+  mfma_step(X0, 0);
+  a_store(X1, 1, st + 1 < nst);
+  __syncthreads();  // buffer 0 is free from here on
+  CompPre<kSwiglu ? 3 : 4> pre;
+  if (p.k > 0) comp_prefetch(p, (uint32_t)(uintptr_t)(NVQ_LDS_U8*)&lds[0][0][0], s_tok, c, b_n, pre);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(X1, 1);
+  __syncthreads();  // buffer 1 is free (the epilogue's LDS staging spans both)
+  comp_phase<true>(p, c, acc, lds[0], a_tok, b_n, pre);
   epilogue<kSwiglu>(p, c, acc, &lds[0][0][0]);
 }
 
@@ -1118,7 +1222,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_moe_gemm_fp8blk(GemmParams p) {
     __syncthreads();
     gload(X1, st + 3);
   }
-  comp_phase(p, c, acc, lds[0], a_tok, b_n);
+  comp_phase<false>(p, c, acc, lds[0], a_tok, b_n, CompPre<1>{});
   epilogue<kSwiglu>(p, c, acc, &lds[0][0][0]);
 }
 
