@@ -404,7 +404,7 @@ struct CompPre {
   int S;
 };
 template <int kD>
-__device__ __forceinline__ void comp_prefetch(const GemmParams& p, uint32_t lds0, const int32_t* s_tok,
+__device__ __forceinline__ void comp_prefetch(const GemmParams& p, uint32_t lds0, const int64_t* s_tok,
                                               const TileCtx& c, const int64_t (&b_n)[2], CompPre<kD>& cp) {
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, h = lane >> 5;
   const int rem = min(p.k, SE);
@@ -417,7 +417,7 @@ __device__ __forceinline__ void comp_prefetch(const GemmParams& p, uint32_t lds0
       const int g = nld * wave + i;  // load g covers tile rows (64 / S) g ..
       const int r = (64 / S) * g + rl;
       const int ls = ps ^ (r & (S - 1));
-      dma16_lds(p.a_resid + (int64_t)s_tok[r] * p.k + min(8 * ls, p.k - 8), lds0 + 1024u * g);
+      dma16_lds(p.a_resid + s_tok[r] * p.k + min(8 * ls, p.k - 8), lds0 + 1024u * g);
     }
   }
 #pragma unroll
@@ -706,7 +706,7 @@ struct Stage {
 template <int kSwiglu>
 __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM][LROW];
-  __shared__ int32_t s_tok[BM];  // A source row of each tile row (compensation prefetch)
+  __shared__ int64_t s_tok[BM];  // A source row of each tile row (compensation prefetch)
   const TileCtx c = tile_of_block(p);
   if (!c.valid) return;
   const int64_t K = p.K, N = p.N;
@@ -720,7 +720,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
   // half h.
   const int ar = t >> 1, ahh = t & 1;
   const int64_t a_tok = loader_a_token(p, c, ar);
-  if (ahh == 0) s_tok[ar] = (int32_t)a_tok;  // read after the prologue's barrier
+  if (ahh == 0) s_tok[ar] = a_tok;  // read after the prologue's barrier
   const uint8_t* a_src = p.a_codes + a_tok * Kh + 32 * ahh;
   const uint8_t* a_ssrc = p.a_scales + a_tok * Kb + 4 * ahh;
   const uint8_t* b_src[2];
