@@ -870,6 +870,17 @@ __global__ __launch_bounds__(256, 2) void k_qat_dgrad2(QatParams p) {
   w_load(W, 0);
   w_store(W, 0);
   __syncthreads();
+  // A wave whose 64 rows all lie past the expert's end (in its last tile)
+  // loads no dy and runs no MFMAs: it only stages its share of the weight
+  // tiles, with the same barriers, and stores nothing.
+  if (__builtin_amdgcn_readfirstlane(64 * wave) >= row_end - row0) {
+    for (int st = 0; st + 1 < nst; ++st) {
+      w_load(W, st + 1);
+      w_store(W, (st & 1) ^ 1);
+      __syncthreads();
+    }
+    return;
+  }
   for (int st = 0; st + 1 < nst; ++st) {
     step(st, W, true);
     __syncthreads();

@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "nvq.h"
 #include "nvq_device.h"
@@ -433,8 +434,9 @@ __device__ __forceinline__ void comp_prefetch(const GemmParams& p, uint32_t lds0
 // residual rows through the LDS tile and the packed weight columns loaded in
 // fragment order.  Channels past k (kpad) read as zero.  With kPre, the first
 // step's operands were fetched by comp_prefetch into pre (residual tile at
-// the start of lds); later steps load their own.
-template <bool kPre, int kD>
+// the start of lds); later steps load their own.  kNI: the live 32-row
+// sub-tiles (the MFMAs of the others are skipped).
+template <bool kPre, int kD, int kNI = 4>
 __device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c,
                                            floatx16_t (&acc)[4][2], uint8_t (*lds)[LROW],
                                            int64_t a_tok, const int64_t (&b_n)[2], const CompPre<kD>& pre) {
@@ -483,9 +485,9 @@ __device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       if (16 * d >= rem) break;
-      bf16x8_t af[4], bf[2];
+      bf16x8_t af[kNI], bf[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kNI; ++i) {
         const int r = 32 * i + l32;
         af[i] = *reinterpret_cast<const bf16x8_t*>(tile + 16 * (S * r + ((2 * d + h) ^ (r & (S - 1)))));
       }
@@ -496,7 +498,7 @@ __device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c
         __builtin_memcpy(&bf[j], &v, 16);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
@@ -524,9 +526,9 @@ __device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       if (16 * d >= rem) break;
-      bf16x8_t af[4], bf[2];
+      bf16x8_t af[kNI], bf[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kNI; ++i)
         af[i] = *reinterpret_cast<const bf16x8_t*>(&lds[32 * i + l32][32 * d + 16 * h]);
       const bool live = 16 * d + 8 * h < rem;
 #pragma unroll
@@ -535,7 +537,7 @@ __device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c
         __builtin_memcpy(&bf[j], &v, 16);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
@@ -765,18 +767,20 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   // one step: 8 sub-steps; A fragments from LDS (rows 32 i + l32, bytes
-  // 128 h + 16 d), B fragments dequantized from registers (dword d).
-  auto mfma_step = [&](const Stage<false>& S, int buf) {
+  // 128 h + 16 d), B fragments dequantized from registers (dword d).  Only
+  // the first NI 32-row sub-tiles take part.
+  auto mfma_step = [&](auto ni_c, const Stage<false>& S, int buf) {
+    constexpr int NI = decltype(ni_c)::value;
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      half8_t af[4], bf[2];
+      half8_t af[NI], bf[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
         af[i] = *reinterpret_cast<const half8_t*>(&lds[buf][32 * i + l32][128 * h + 16 * d]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) bf[j] = dequant8(dword_of(S.b[j], d), scale_pair(S.bs[j][0], d >> 1));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
@@ -793,34 +797,51 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
   // The loop covers step pairs; an odd step count adds one zero-scaled step.
   // The last pair is peeled: instead of loading past the end it fetches the
   // compensation operands, which then arrive under its last MFMAs.
-  Stage<false> X0, X1;
-  gload(X0, 0);
-  gload(X1, 1);
-  a_store(X0, 0, true);
-  __syncthreads();
-  int st = 0;
-  for (; st + 2 < nst; st += 2) {
-    mfma_step(X0, 0);
-    a_store(X1, 1, st + 1 < nst);
-    __syncthreads();
-    gload(X0, st + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(X1, 1);
-    a_store(X0, 0, st + 2 < nst);
-    __syncthreads();
-    gload(X1, st + 3);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  mfma_step(X0, 0);
-  a_store(X1, 1, st + 1 < nst);
-  __syncthreads();  // buffer 0 is free from here on
+  // NI = 1 serves a tile of at most 32 rows (an expert's ragged last tile):
+  // a quarter of the MFMAs, and only wave 0 (A rows 0..31) dequantizes A;
+  // the other rows' accumulators stay unused and are never stored.
   CompPre<kSwiglu ? 3 : 4> pre;
-  if (p.k > 0) comp_prefetch(p, (uint32_t)(uintptr_t)(NVQ_LDS_U8*)&lds[0][0][0], s_tok, c, b_n, pre);
-  __builtin_amdgcn_sched_barrier(0);
-  mfma_step(X1, 1);
-  __syncthreads();  // buffer 1 is free (the epilogue's LDS staging spans both)
-  comp_phase<true>(p, c, acc, lds[0], a_tok, b_n, pre);
-  epilogue<kSwiglu>(p, c, acc, &lds[0][0][0]);
+  auto run = [&](auto ni_c) {
+    constexpr int NI = decltype(ni_c)::value;
+    const bool a_live = NI == 4 || wave < NI;  // this wave's A rows are 32 wave .. + 31
+    Stage<false> X0, X1;
+    gload(X0, 0);
+    gload(X1, 1);
+    if (a_live) a_store(X0, 0, true);
+    __syncthreads();
+    int st = 0;
+    for (; st + 2 < nst; st += 2) {
+      mfma_step(ni_c, X0, 0);
+      if (a_live) a_store(X1, 1, st + 1 < nst);
+      __syncthreads();
+      gload(X0, st + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(ni_c, X1, 1);
+      if (a_live) a_store(X0, 0, st + 2 < nst);
+      __syncthreads();
+      gload(X1, st + 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_step(ni_c, X0, 0);
+    if (a_live) a_store(X1, 1, st + 1 < nst);
+    __syncthreads();  // buffer 0 is free from here on
+    if (p.k > 0) comp_prefetch(p, (uint32_t)(uintptr_t)(NVQ_LDS_U8*)&lds[0][0][0], s_tok, c, b_n, pre);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(ni_c, X1, 1);
+    __syncthreads();  // buffer 1 is free (the epilogue's LDS staging spans both)
+    if constexpr (kSwiglu != 0) {
+      comp_phase<true, 3, NI>(p, c, acc, lds[0], a_tok, b_n, pre);
+      epilogue<kSwiglu>(p, c, acc, &lds[0][0][0]);
+    }
+  };
+  if (c.row_end - c.row0 <= 32)
+    run(std::integral_constant<int, 1>{});
+  else
+    run(std::integral_constant<int, 4>{});
+  if constexpr (kSwiglu == 0) {
+    comp_phase<true>(p, c, acc, lds[0], a_tok, b_n, pre);
+    epilogue<kSwiglu>(p, c, acc, &lds[0][0][0]);
+  }
 }
 
 // ------------------------------------------------ path DEQ16, wide tile --
