@@ -748,13 +748,17 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
     }
   };
   // This thread's 64 A elements of a step -> exact fp16 at LDS row ar, bytes
-  // [128 ahh, 128 ahh + 128).  live == false (a step past K) writes zeros.
+  // [128 ahh, 128 ahh + 128), 16-byte chunk d at slot d ^ 4 ahh: the two
+  // halves of a row, stored by adjacent lanes, then fall in different banks
+  // (their natural offsets differ by 128 bytes, one full turn of the 32
+  // banks that a 16-byte store is served from).  live == false (a step past
+  // K) writes zeros.
   auto a_store = [&](const Stage<false>& S, int buf, bool live) {
     uint8_t* dst = &lds[buf][ar][128 * ahh];
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       const uint32_t pat = live ? scale_pair(S.as, d >> 1) : 0u;
-      *reinterpret_cast<half8_t*>(dst + 16 * d) = dequant8(dword_of(S.a, d), pat);
+      *reinterpret_cast<half8_t*>(dst + 16 * (d ^ (4 * ahh))) = dequant8(dword_of(S.a, d), pat);
     }
   };
 
@@ -766,8 +770,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // one step: 8 sub-steps; A fragments from LDS (rows 32 i + l32, bytes
-  // 128 h + 16 d), B fragments dequantized from registers (dword d).  Only
+  // one step: 8 sub-steps; A fragments from LDS (rows 32 i + l32, chunk d of
+  // half h), B fragments dequantized from registers (dword d).  Only
   // the first NI 32-row sub-tiles take part.
   auto mfma_step = [&](auto ni_c, const Stage<false>& S, int buf) {
     constexpr int NI = decltype(ni_c)::value;
@@ -776,7 +780,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
       half8_t af[NI], bf[2];
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        af[i] = *reinterpret_cast<const half8_t*>(&lds[buf][32 * i + l32][128 * h + 16 * d]);
+        af[i] = *reinterpret_cast<const half8_t*>(&lds[buf][32 * i + l32][128 * h + 16 * (d ^ (4 * h))]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) bf[j] = dequant8(dword_of(S.b[j], d), scale_pair(S.bs[j][0], d >> 1));
 #pragma unroll
