@@ -970,7 +970,21 @@ __global__ __launch_bounds__(512, 1) void k_qat_wgrad2(QatParams p) {
   const int logical = (blockIdx.x & 7) * per + slot;  // XCD blockIdx % 8 takes a contiguous range
   if (logical >= total) return;
   const int e = logical / per_e, rem = logical - e * per_e;
-  const int tn = rem / n_tc, tc = rem - tn * n_tc;
+  // Order of an expert's tiles: the 32 workgroups an XCD runs at once should
+  // touch few dy (n) and x (c) panels.  n-tile-major order covers 32 / n_tc
+  // n-tiles x all c-tiles; with 8 or more c-tiles, bands of 4 n-tiles walked
+  // c-tile-major cover 4 x 8 instead (12 panels rather than 18 at n_tc = 16).
+  int tn, tc;
+  if (n_tc >= 8) {
+    constexpr int kBand = 4;
+    const int band = rem / (kBand * n_tc), ib = rem - band * (kBand * n_tc);
+    const int brows = min(kBand, n_tn - band * kBand);
+    tc = ib / brows;
+    tn = band * kBand + (ib - tc * brows);
+  } else {
+    tn = rem / n_tc;
+    tc = rem - tn * n_tc;
+  }
   const int64_t N = p.N, K = p.K, rows = p.rows;
   const int64_t n0 = (int64_t)tn * GBN, c0 = (int64_t)tc * GBC;
   const int64_t p_beg = p.off[e], p_end = p.off[e + 1];
@@ -1135,7 +1149,7 @@ __global__ __launch_bounds__(512, 1) void k_qat_wgrad2(QatParams p) {
       for (int j = 0; j < 4; ++j) {
         float* const d = p.dw + ((int64_t)e * N + n0 + 64 * wn + 32 * i + 4 * h) * K + c0 + 128 * wc + 32 * j + l32;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) d[idx(v) * K] = acc[i][j][v];
+        for (int v = 0; v < 16; ++v) __builtin_nontemporal_store(acc[i][j][v], &d[idx(v) * K]);
       }
   } else if (full) {
 #pragma unroll

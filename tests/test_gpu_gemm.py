@@ -226,15 +226,29 @@ def test_grouped_gemm_edge_shapes(K, N, k, epi, path):
     multiple of 64, experts with no rows, one expert with more rows than one
     256-row tile and one with more than one 128-row tile, fp32 and bf16
     outputs, and rows read through a_row with a divisor."""
+    # P = 360 sorted rows of 420 pairs
+    _grouped_gemm_case(K, N, k, epi, path, counts=[0, 300, 3, 0, 57], T=140, topk=3)
+
+
+@pytest.mark.parametrize("epi", ["none", "swiglu"])
+def test_grouped_gemm_ragged_tail_tiles(epi):
+    """Experts whose last 128-row tile holds 32 rows (served by the one-sub-tile
+    copy of the main loop), 33 rows (the full loop), 1 row, or exactly fills
+    its tile: every row against the oracle."""
+    _grouped_gemm_case(256, 256, 16, epi, "deq16", counts=[32, 33, 160, 161, 0, 1, 64, 128], T=200, topk=3)
+
+
+def _grouped_gemm_case(K, N, k, epi, path, counts, T, topk):
     import torch
 
     nvq = _nvq()
     gp = _path(path)
     swiglu = epi == "swiglu"
     g = np.random.default_rng(K * 1000 + N + k)
-    E, T, topk = 5, 140, 3
-    counts = np.array([0, 300, 3, 0, 57])  # P = 360 sorted rows of 420 pairs
+    counts = np.asarray(counts)
+    E = len(counts)
     P = int(counts.sum())
+    assert P <= T * topk
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     pair = g.permutation(T * topk)[:P].astype(np.int32)  # sorted pair ids; token = pair // topk
     x = (g.standard_normal((T, K)) * np.exp(g.standard_normal((1, K)))).astype(np.float32)
