@@ -89,6 +89,7 @@ struct GemmParams {
   int bm;                 // row tile of the tile table
   uint32_t* h_amax;       // SwiGLU: max |h| over the stored bf16 h, as fp32 bits; or NULL
   int bf16_rows16;        // out_bf16 rows may be written in 16-byte pieces (N % 8 == 0, aligned)
+  int h_rows16;           // SwiGLU: rows of h (N / 2 wide) may be written in 16-byte pieces
   // fused combine (NULL comb_out: none)
   const int32_t* comb_pair;
   const int32_t* comb_pos;
@@ -656,32 +657,71 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c,
     if (p.comb_out) fused_combine(p, c, lds);
   } else {
     const int64_t I = N >> 1;
-    const int64_t ng = (int64_t)c.nt * (BN / 2) + 32 * wave + l32;
+    const int64_t ng0 = (int64_t)c.nt * (BN / 2);  // first h column of the tile
+    const int64_t ng = ng0 + 32 * wave + l32;
     uint32_t hmax = 0;  // largest |h| stored by this lane, as bf16 bits
-    auto emit = [&](bool check) {
+    // A tile whose 128 h columns lie inside H stages them in LDS (128 rows x
+    // 256 bytes; 16-byte chunk q of row r at slot q ^ 4 s, s = (r & 1) | ((r
+    // >> 2) & 1) << 1, so the four rows one write instruction touches fill
+    // distinct banks) and stores 16-byte pieces, 16 lanes per row, instead of
+    // one 2-byte store per element.
+    const bool h_lds = p.out_bf16 && p.h_rows16 && ng0 + BN / 2 <= I;
+    auto swz = [](int r) { return 4 * ((r & 1) | (((r >> 2) & 1) << 1)); };
+    auto emit = [&](bool check, bool to_lds) {
+      const bool odd = (l32 & 1) != 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t pr = c.row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (check && (pr >= c.row_end || ng >= I)) continue;
-          const float g = acc[i][0][v] * stw;
-          const float u = acc[i][1][v] * stw;
-          if (p.out_f32) {
-            p.out_f32[pr * N + ng] = g;
-            p.out_f32[pr * N + I + ng] = u;
+        for (int v = 0; v < 16; v += 2) {
+          uint32_t hb2[2];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int64_t pr = c.row0 + 32 * i + 8 * (v >> 2) + 4 * h + ((v + s) & 3);
+            const bool live = !check || (pr < c.row_end && ng < I);
+            const float g = acc[i][0][v + s] * stw;
+            const float u = acc[i][1][v + s] * stw;
+            if (p.out_f32 && live) {
+              p.out_f32[pr * N + ng] = g;
+              p.out_f32[pr * N + I + ng] = u;
+            }
+            // silu(g) u; the result is rounded to bf16, so an rcp suffices
+            const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+            const uint32_t hb = f32_to_bf16_rne(hv);
+            if (live) {
+              if (p.out_bf16 && !to_lds) p.out_bf16[pr * I + ng] = (uint16_t)hb;
+              hmax = max(hmax, hb & 0x7FFFu);
+            }
+            hb2[s] = hb;
           }
-          // silu(g) u; the result is rounded to bf16, so an rcp suffices
-          const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-          const uint32_t hb = f32_to_bf16_rne(hv);
-          if (p.out_bf16) p.out_bf16[pr * I + ng] = (uint16_t)hb;
-          hmax = max(hmax, hb & 0x7FFFu);
+          if (to_lds) {
+            // rows r, r + 1 of column l32: the even lane keeps row r and sends
+            // row r + 1 to its odd neighbour, which keeps row r + 1
+            const uint32_t send = odd ? hb2[0] : hb2[1];
+            const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xF, 0xF, false);
+            const uint32_t lo = odd ? recv : hb2[0], hi = odd ? hb2[1] : recv;
+            const int row = 32 * i + 8 * (v >> 2) + 4 * h + (v & 3) + (odd ? 1 : 0);
+            const int col = 32 * wave + l32 - (odd ? 1 : 0);  // even column of the pair
+            *reinterpret_cast<uint32_t*>(lds + row * 256 + (((col >> 3) ^ swz(row)) << 4) + (col & 7) * 2) =
+                lo | (hi << 16);
+          }
         }
     };
-    if (rows_full && (int64_t)c.nt * (BN / 2) + 32 * (wave + 1) <= I)
-      emit(false);
-    else
-      emit(true);
+    if (h_lds) {
+      emit(!rows_full, true);
+      __syncthreads();  // the tile's h is in LDS
+      const int nrows = (int)min<int64_t>(BM, c.row_end - c.row0), q = t & 15;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int row = (t >> 4) + 16 * m;
+        if (row < nrows)
+          *reinterpret_cast<uint4*>(p.out_bf16 + (c.row0 + row) * I + ng0 + 8 * q) =
+              *reinterpret_cast<const uint4*>(lds + row * 256 + ((q ^ swz(row)) << 4));
+      }
+    } else if (rows_full && ng0 + 32 * (wave + 1) <= I) {
+      emit(false, false);
+    } else {
+      emit(true, false);
+    }
     // amax of H for its quantization: bit patterns of non-negative values
     // order as the values; one device-scope atomic per wave.
     if (p.h_amax) {
@@ -1374,6 +1414,7 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   p.w_codes = a->w_codes; p.w_scales = a->w_scales; p.w_st = a->w_tensor_scale;
   p.out_bf16 = a->out_bf16; p.out_f32 = a->out_f32;
   p.bf16_rows16 = (a->N % 8 == 0 && aligned16(a->out_bf16)) ? 1 : 0;
+  p.h_rows16 = (a->N % 16 == 0 && aligned16(a->out_bf16)) ? 1 : 0;
   p.comb_pair = comb ? a->comb_pair : nullptr;
   p.comb_pos = comb ? a->comb_pos : nullptr;
   p.comb_w = comb ? a->comb_weights : nullptr;
