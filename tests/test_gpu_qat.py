@@ -69,9 +69,12 @@ def test_small_qat_all_modes(proj):
                                          a_row=a_row, want_f32=True)
     dxb, dxf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *d["q"][:3], d["off"], s.P, dy=dyg,
                                            want_f32=True)
+    # bf16 alone (staged through LDS for whole column tiles): the same bits
+    dxb_only = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *d["q"][:3], d["off"], s.P, dy=dyg)[0]
     dw = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *d["q"][:3], d["off"], s.P, x=xg, dy=dyg,
                                       a_row=a_row)
     torch.cuda.synchronize()
+    assert_bits_equal(to_np(dxb_only), to_np(dxb), "dx bf16 without the fp32 output")
     X = inputs.bf16_bits_to_f32(d["x"]).astype(np.float64)
     DY = inputs.bf16_bits_to_f32(d["dy"]).astype(np.float64)
     ref_y = oracle.qat_fwd(d["x"], x_row, row_e, wc, wsc, wst)
@@ -132,12 +135,14 @@ def test_fwd_dgrad_edge_shapes(K, N, counts):
                                          a_row=to_gpu(x_row), want_f32=True)
     dxb, dxf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *q[:3], offg, P, dy=to_gpu(dy),
                                            want_f32=True)
+    dxb_only = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *q[:3], offg, P, dy=to_gpu(dy))[0]
     dw = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *q[:3], offg, P, x=to_gpu(x),
                                       dy=to_gpu(dy), a_row=to_gpu(x_row))
     dw2 = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *q[:3], offg, P, x=to_gpu(x),
                                        dy=to_gpu(dy), a_row=to_gpu(x_row), dw=dw.clone(),
                                        accumulate=True)
     torch.cuda.synchronize()
+    assert_bits_equal(to_np(dxb_only), to_np(dxb), "dx bf16 without the fp32 output")
     wq = [oracle.quantize(wm[e]) for e in range(E)]
     wc = np.stack([w[0] for w in wq])
     assert_bits_equal(to_np(q[0]), wc, "weight cache codes")
@@ -235,8 +240,11 @@ def test_qat_layer_full_size_sampled(proj, guided):
     yb, yf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_FWD, *rec_w, off, s.P, x=x, a_row=a_row,
                                          want_f32=True)
     dxb, dxf = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *rec_w, off, s.P, dy=dy, want_f32=True)
+    dxb_only = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_DGRAD, *rec_w, off, s.P, dy=dy)[0]
     dw = nvq.qat_fakequant_gemm_w4a16(nvq.NVQ_QAT_WGRAD, *rec_w, off, s.P, x=x, dy=dy, a_row=a_row)
     torch.cuda.synchronize()
+    assert_bits_equal(to_np(dxb_only), to_np(dxb), "dx bf16 without the fp32 output")
+    del dxb_only
     offn = to_np(off)
     x_of_row = to_np(sp) // s.topk if proj == "gu" else np.arange(s.P)
     xn = to_np(x)
