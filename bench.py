@@ -255,13 +255,14 @@ class MoeLeg:
             ws=self.ws_g, a_row_div=self.s.topk if a_row is not None else 0, out=out, path=path,
             w_cm=self.wcm[proj], h_amax=self.h_amax if epi == nvq.NVQ_EPI_SWIGLU else None)
 
-    def step(self, timer_, comp=True, path=0):
+    def step(self, timer_, comp=True, path=0, tag=""):
         """path 0: the library's choice (exact fp16 dequantization, 128-row
         tiles); 2: the FP8 block-product path; 3: the 256-row tiles; 2 and 3
-        are timed separately for the comparison."""
+        are timed separately for the comparison.  tag: a suffix for the GEMM
+        timer labels of this call (k = 0 and the paths add their own)."""
         nvq, s = self.nvq, self.s
-        tag = ("" if comp else "_k0") + {nvq.NVQ_GEMM_FP8_BLOCK: "_fp8blk",
-                                          nvq.NVQ_GEMM_DEQ16_WIDE: "_wide"}.get(path, "")
+        tag = tag + ("" if comp else "_k0") + {nvq.NVQ_GEMM_FP8_BLOCK: "_fp8blk",
+                                                nvq.NVQ_GEMM_DEQ16_WIDE: "_wide"}.get(path, "")
         timer = lambda label, fn: timer_(self.name + "/" + label, fn)
         r = timer("route", lambda: nvq.nvq_moe_route(self.logits, s.topk))
         self.ids, self.w = r
@@ -404,9 +405,12 @@ class MoeLeg:
                "comp_gflop": round(self.flops_comp / 1e9, 1),
                "stages_ms": {k: round(timer.avg_ms(k), 4) for k in
                              ("route", "permute", "quant_x", "topk_x", "quant_h", "topk_h", "combine")}}
-        if "gemm_gu_k0" in timer.total:
+        if "gemm_gu_k0" in timer.total and "gemm_gu_pair" in timer.total:
+            # k > 0 and k = 0 layer steps alternating, each after a step of
+            # the same layer, so both find the caches in the same state
             k0 = timer.avg_ms("gemm_gu_k0") + timer.avg_ms("gemm_dn_k0")
-            out["comp_overhead_vs_k0"] = round((gu + dn) / k0 - 1.0, 4)
+            kp = timer.avg_ms("gemm_gu_pair") + timer.avg_ms("gemm_dn_pair")
+            out["comp_overhead_vs_k0"] = round(kp / k0 - 1.0, 4)
         if "gemm_gu_fp8blk" in timer.total:
             g8, d8 = timer.avg_ms("gemm_gu_fp8blk"), timer.avg_ms("gemm_dn_fp8blk")
             tf8 = (self.flops_gu + self.flops_dn) / ((g8 + d8) * 1e-3) / 1e12
@@ -816,13 +820,19 @@ def main():
     timer.collect()
     ms_step = wall * 1e3 / args.steps
     # k = 0 reference runs of the MoE legs (outside the timed steps): the
-    # compensation overhead is the GEMM time at k > 0 over the time at k = 0
-    # and the FP8 block-product path, the evaluated alternative to exact fp16
+    # compensation overhead is the GEMM time at k > 0 over the time at k = 0,
+    # from steps that alternate k > 0 and k = 0 after one untimed pair (every
+    # timed one then follows a step of the same layer); and the FP8
+    # block-product path, the evaluated alternative to exact fp16
     # dequantization, on the same layers
     from qat_nvfp4_quantize_amd import nvq as _nvq
+    untimed = lambda label, fn: fn()
     for leg in legs:
         if leg.name.startswith("moe"):
-            for _ in range(2):
+            leg.step(untimed)
+            leg.step(untimed, comp=False)
+            for _ in range(3):
+                leg.step(timer, tag="_pair")
                 leg.step(timer, comp=False)
             for _ in range(2):
                 leg.step(timer, path=_nvq.NVQ_GEMM_FP8_BLOCK)

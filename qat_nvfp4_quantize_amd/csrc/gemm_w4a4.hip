@@ -435,8 +435,9 @@ __device__ __forceinline__ void comp_prefetch(const GemmParams& p, uint32_t lds0
 // residual rows through the LDS tile and the packed weight columns loaded in
 // fragment order.  Channels past k (kpad) read as zero.  With kPre, the first
 // step's operands were fetched by comp_prefetch into pre (residual tile at
-// the start of lds); later steps load their own.  kNI: the live 32-row
-// sub-tiles (the MFMAs of the others are skipped).
+// the start of lds), and the caller has waited for them and synchronized the
+// workgroup; later steps load their own.  kNI: the live 32-row sub-tiles
+// (the MFMAs of the others are skipped).
 template <bool kPre, int kD, int kNI = 4>
 __device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c,
                                            floatx16_t (&acc)[4][2], uint8_t (*lds)[LROW],
@@ -469,10 +470,8 @@ __device__ __forceinline__ void comp_phase(const GemmParams& p, const TileCtx& c
   };
   int cs = 0;
   if (kPre) {
-    // the prefetched first step: this lane's direct loads landed, then
-    // every wave's
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // the prefetched first step: the caller waited for its loads and met
+    // the other waves at a barrier, so every wave's direct loads have landed
     const int rem = min(p.k, SE), S = pre.S;
     const uint8_t* tile = &lds[0][0];
     uint4 wl[2][8 - kD];  // sub-steps kD.., loaded now
@@ -872,7 +871,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_moe_gemm_deq16(GemmParams p) {
     if (p.k > 0) comp_prefetch(p, (uint32_t)(uintptr_t)(NVQ_LDS_U8*)&lds[0][0][0], s_tok, c, b_n, pre);
     __builtin_amdgcn_sched_barrier(0);
     mfma_step(ni_c, X1, 1);
-    __syncthreads();  // buffer 1 is free (the epilogue's LDS staging spans both)
+    // past this barrier buffer 1 is free (the epilogue's LDS staging spans
+    // both) and every wave's compensation prefetch has landed
+    if (p.k > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     if constexpr (kSwiglu != 0) {
       comp_phase<true, 3, NI>(p, c, acc, lds[0], a_tok, b_n, pre);
       epilogue<kSwiglu>(p, c, acc, &lds[0][0][0]);
