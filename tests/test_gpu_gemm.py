@@ -231,11 +231,13 @@ def test_grouped_gemm_edge_shapes(K, N, k, epi, path):
 
 
 @pytest.mark.parametrize("epi", ["none", "swiglu"])
-def test_grouped_gemm_ragged_tail_tiles(epi):
+@pytest.mark.parametrize("k", [16, 200])
+def test_grouped_gemm_ragged_tail_tiles(epi, k):
     """Experts whose last 128-row tile holds 32 rows (served by the one-sub-tile
     copy of the main loop), 33 rows (the full loop), 1 row, or exactly fills
-    its tile: every row against the oracle."""
-    _grouped_gemm_case(256, 256, 16, epi, "deq16", counts=[32, 33, 160, 161, 0, 1, 64, 128], T=200, topk=3)
+    its tile, with one compensation step and with two (k = 200: the second
+    step loads its own operands): every row against the oracle."""
+    _grouped_gemm_case(256, 256, k, epi, "deq16", counts=[32, 33, 160, 161, 0, 1, 64, 128], T=200, topk=3)
 
 
 def _grouped_gemm_case(K, N, k, epi, path, counts, T, topk):
