@@ -564,7 +564,10 @@ __global__ __launch_bounds__(512, 2) void k_quantize(
 // bit-identical to the row tile's.  Sixteen times the threads of the row
 // tile for the same bytes.
 constexpr int kTbCols = 64;
-constexpr int kTbMaxRowTileWgs = 1;  // row-tile workgroups per CU below which k_quantize_tb runs
+// k_quantize_tb runs when the row tile would have fewer workgroups than a
+// third of the CUs (measured: at 64 row-tile workgroups on 256 CUs the
+// thread-per-block tile wins, 28 against 31 us; at 112 and above the row tile)
+constexpr int kTbCuDiv = 3;
 template <bool kBF16>
 __global__ __launch_bounds__(512) void k_quantize_tb(
     const void* __restrict__ xv, int64_t rows, int64_t K, int64_t ldx,
@@ -1197,10 +1200,10 @@ extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t batch, int64_t
   // once (two 512-thread workgroups per CU), so both launches place workgroup
   // i on the same XCD at about the same time; larger grids take the flat pass.
   const int64_t qwgs = (int64_t)qgrid.x * qgrid.y;
-  // A scored row tile with fewer workgroups than CUs leaves the chip mostly
-  // idle (each wave walks 16 rows); the thread-per-block tile computes the
-  // same chunk partials with sixteen times the threads, after the flat amax.
-  const bool tb = score && qwgs < kTbMaxRowTileWgs * (int64_t)device_cu_count();
+  // A scored row tile with few workgroups leaves the chip mostly idle (each
+  // wave walks 16 rows); the thread-per-block tile computes the same chunk
+  // partials with sixteen times the threads, after the flat amax.
+  const bool tb = score && qwgs * kTbCuDiv < (int64_t)device_cu_count();
   if (!amax_in && score && !tb && qwgs <= 1024 && qwgs <= 2 * device_cu_count()) {
     n_partial = (int)L.n_partial_tiles;
     if (bf16)
