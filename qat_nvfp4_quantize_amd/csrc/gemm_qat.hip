@@ -74,14 +74,8 @@ __global__ __launch_bounds__(1024) void k_qat_tile_table(const int32_t* __restri
   const int e = threadIdx.x;
   const int nt = e < E ? (off[e + 1] - off[e] + bm - 1) / bm : 0;
   const int incl = block_inclusive_scan(nt, s_wave);
-  if (e == E - 1) *ntiles = min(incl, max_tiles);
-  if (e < E) {
-    const int base = incl - nt;
-    for (int t = 0; t < nt && base + t < max_tiles; ++t) {
-      tiles[2 * (base + t)] = e;
-      tiles[2 * (base + t) + 1] = off[e] + t * bm;
-    }
-  }
+  __shared__ int32_t s_incl[1024];
+  write_tile_table(off, E, bm, incl, tiles, ntiles, max_tiles, s_incl);
 }
 
 // Two FP4 codes (a byte) times the block scale -> packed bf16 pair, exact

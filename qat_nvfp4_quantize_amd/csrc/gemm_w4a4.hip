@@ -126,14 +126,8 @@ __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__
   if (h_amax && threadIdx.x == 0) *h_amax = 0u;
   const int nt = e < E ? (off[e + 1] - off[e] + BM - 1) / BM : 0;
   const int incl = block_inclusive_scan(nt, s_wave);
-  if (e == E - 1) *ntiles = min(incl, max_tiles);
-  if (e < E) {
-    const int base = incl - nt;
-    for (int t = 0; t < nt && base + t < max_tiles; ++t) {
-      tiles[2 * (base + t)] = e;
-      tiles[2 * (base + t) + 1] = off[e] + t * BM;
-    }
-  }
+  __shared__ int32_t s_incl[1024];
+  write_tile_table(off, E, BM, incl, tiles, ntiles, max_tiles, s_incl);
 }
 
 __global__ void k_clear_word(uint32_t* w) { *w = 0u; }

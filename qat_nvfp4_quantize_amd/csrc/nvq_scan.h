@@ -33,4 +33,34 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* s_wave) {
   return wave > 0 ? v + s_wave[wave - 1] : v;
 }
 
+// Tile table of a row-tiled grouped GEMM, built by one workgroup of blockDim.x
+// >= E threads: expert e's rows [off[e], off[e + 1]) split into bm-row tiles,
+// tile i = (expert, first row), experts in order.  Thread e < E passes its
+// tile count nt and the inclusive prefix incl over the experts.  Tile i is
+// written by thread i % blockDim.x (its expert found by a binary search over
+// the prefixes in LDS), so consecutive tiles go out together however the
+// rows are spread over the experts.  s_incl: blockDim.x ints of LDS.
+__device__ __forceinline__ void write_tile_table(const int32_t* __restrict__ off, int E, int bm, int incl,
+                                                 int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                 int max_tiles, int* s_incl) {
+  const int e = threadIdx.x;
+  if (e < E) s_incl[e] = incl;
+  if (e == E - 1) *ntiles = min(incl, max_tiles);
+  __syncthreads();
+  const int total = min(s_incl[E - 1], max_tiles);
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    int lo = 0, hi = E - 1;  // the first expert whose inclusive prefix exceeds i
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_incl[mid] > i)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    const int base = lo > 0 ? s_incl[lo - 1] : 0;
+    tiles[2 * i] = lo;
+    tiles[2 * i + 1] = off[lo] + (i - base) * bm;
+  }
+}
+
 }  // namespace nvq
