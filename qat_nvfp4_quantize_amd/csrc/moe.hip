@@ -28,14 +28,34 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
+// Wave maximum of a 64-bit key, returned to every lane: DPP steps within
+// each row of 16 lanes (quad swaps, half-row and row mirrors, as in
+// wave_max_u32), then the four row maxima by readlane.  Every lane must be
+// active.
+__device__ __forceinline__ void max_step_u64(uint32_t& hi, uint32_t& lo, uint32_t h2, uint32_t l2) {
+  const bool gt = h2 > hi || (h2 == hi && l2 > lo);
+  hi = gt ? h2 : hi;
+  lo = gt ? l2 : lo;
 }
+#define NVQ_DPP_MAX_U64(ctrl)                                                                   \
+  max_step_u64(hi, lo, (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, ctrl, 0xF, 0xF, false), \
+               (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, ctrl, 0xF, 0xF, false))
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+  NVQ_DPP_MAX_U64(0xB1);   // quad_perm [1,0,3,2]
+  NVQ_DPP_MAX_U64(0x4E);   // quad_perm [2,3,0,1]
+  NVQ_DPP_MAX_U64(0x141);  // row_half_mirror
+  NVQ_DPP_MAX_U64(0x140);  // row_mirror
+  uint64_t best = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                       (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+    best = x > best ? x : best;
+  }
+  return best;
+}
+#undef NVQ_DPP_MAX_U64
 
 // One wave per token: topk rounds of a 64-bit (key, ~id) wave max.  Each
 // lane holds kPer = ceil(E / 64) keys (E <= 64 * kPer).
@@ -77,8 +97,12 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   // their sum in selection order (the same order on every lane).
   if (topk <= 64) {
     const double x = lane < topk ? exp((double)my_lv - lmax) : 0.0;
+    const uint64_t xb = __double_as_longlong(x);
     double den = 0.0;
-    for (int j = 0; j < topk; ++j) den += __shfl(x, j, 64);
+    for (int j = 0; j < topk; ++j)  // lane j's exp, broadcast through scalar registers
+      den += __longlong_as_double(
+          (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(xb >> 32), j) << 32) |
+                    (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)xb, j)));
     if (lane < topk) weights[t * topk + lane] = (float)(x / den);
   } else if (lane == 0) {
     double den = 0.0;
