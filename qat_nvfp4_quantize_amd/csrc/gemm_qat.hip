@@ -71,11 +71,8 @@ __global__ __launch_bounds__(1024) void k_qat_tile_table(const int32_t* __restri
                                                         int32_t* __restrict__ ntiles, int max_tiles,
                                                         int bm) {
   __shared__ int32_t s_wave[16];
-  const int e = threadIdx.x;
-  const int nt = e < E ? (off[e + 1] - off[e] + bm - 1) / bm : 0;
-  const int incl = block_inclusive_scan(nt, s_wave);
   __shared__ int32_t s_incl[1024];
-  write_tile_table(off, E, bm, incl, tiles, ntiles, max_tiles, s_incl);
+  build_tile_table(off, E, bm, tiles, ntiles, max_tiles, s_wave, s_incl);
 }
 
 // Two FP4 codes (a byte) times the block scale -> packed bf16 pair, exact

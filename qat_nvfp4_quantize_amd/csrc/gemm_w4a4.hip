@@ -122,12 +122,9 @@ __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__
                                                     int32_t* __restrict__ ntiles, int max_tiles,
                                                     uint32_t* __restrict__ h_amax) {
   __shared__ int32_t s_wave[16];
-  const int e = threadIdx.x;
   if (h_amax && threadIdx.x == 0) *h_amax = 0u;
-  const int nt = e < E ? (off[e + 1] - off[e] + BM - 1) / BM : 0;
-  const int incl = block_inclusive_scan(nt, s_wave);
   __shared__ int32_t s_incl[1024];
-  write_tile_table(off, E, BM, incl, tiles, ntiles, max_tiles, s_incl);
+  build_tile_table(off, E, BM, tiles, ntiles, max_tiles, s_wave, s_incl);
 }
 
 __global__ void k_clear_word(uint32_t* w) { *w = 0u; }
@@ -266,13 +263,27 @@ __device__ __forceinline__ uint32_t wq_bf16(uint32_t nib, uint32_t sc) {
 // both rows' G, signed; G * s_b has at most 6 significant bits, so its bf16
 // is exact) into an LDS tile.  Then each group of 8 threads stores one row's
 // 128 slice bytes as 16-byte pieces, so every output line is written whole
-// by one workgroup.
+// by one workgroup.  With tiles set, the grid has one more z slice whose
+// first workgroup builds the GEMM's tile table (and clears h_amax) while
+// the others gather: one launch less per call.
 constexpr int kWcRows = 64, kWcCh = 64, kWcPitch = kWcCh + 8;  // tile pitch in bf16 (+16 bytes)
 __global__ __launch_bounds__(256) void k_gather_wcomp_rows(const uint8_t* __restrict__ codes_cm,
                                                           const uint8_t* __restrict__ scales_cm, int64_t N,
                                                           int64_t K, const int32_t* __restrict__ idx, int k,
-                                                          int kpad, uint16_t* __restrict__ wcomp) {
+                                                          int kpad, uint16_t* __restrict__ wcomp,
+                                                          const int32_t* __restrict__ off, int E, int bm,
+                                                          int32_t* __restrict__ tiles,
+                                                          int32_t* __restrict__ ntiles, int max_tiles,
+                                                          uint32_t* __restrict__ h_amax) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kWcRows][kWcPitch];
+  static_assert(sizeof(tile) >= (1024 + 16) * sizeof(int), "tile table prefixes alias the tile");
+  if (tiles && blockIdx.z == (unsigned)E) {  // the extra slice (uniform over the workgroup)
+    if (blockIdx.x | blockIdx.y) return;
+    if (h_amax && threadIdx.x == 0) *h_amax = 0u;
+    int* s_wave = reinterpret_cast<int*>(&tile[0][0]);
+    build_tile_table(off, E, bm, tiles, ntiles, max_tiles, s_wave, s_wave + 16);
+    return;
+  }
   const int64_t e = blockIdx.z;
   const int64_t n0 = (int64_t)blockIdx.x * kWcRows;
   const int c0 = kWcCh * (int)blockIdx.y;
@@ -1385,21 +1396,24 @@ extern "C" int moe_grouped_gemm_w4a4_comp(const nvq_moe_gemm_args* a, void* stre
   const bool wide = a->path == NVQ_GEMM_DEQ16_WIDE;
   const int bm = wide ? W_BM : BM;
   const int max_tiles = wide ? (int)((a->rows + W_BM - 1) / W_BM + a->E) : L.max_tiles;
-  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, a->expert_offsets, (int)a->E, bm, L.tiles,
-                     L.ntiles, max_tiles, h_amax);
-  if (int rc = last_launch()) return rc;
+  const bool fused_table = a->k > 0 && has_cm;  // the gather's extra workgroup builds the table
+  if (!fused_table) {
+    hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(1024), 0, s, a->expert_offsets, (int)a->E, bm, L.tiles,
+                       L.ntiles, max_tiles, h_amax);
+    if (int rc = last_launch()) return rc;
+  }
   GemmParams p;
   p.rows = a->rows; p.K = a->K; p.N = a->N; p.E = a->E; p.a_rows = a->a_rows;
   p.a_row = a->a_row; p.a_row_div = a->a_row_div; p.off = a->expert_offsets;
   p.a_codes = a->a_codes; p.a_scales = a->a_scales; p.a_st = a->a_tensor_scale;
   p.a_resid = a->a_resid; p.comp_idx = a->comp_idx; p.k = a->k;
   p.kpad = L.kpad; p.wcomp = L.wcomp;
-  if (a->k > 0 && has_cm) {
+  if (fused_table) {
     hipLaunchKernelGGL(k_gather_wcomp_rows,
                        dim3((unsigned)((a->N + kWcRows - 1) / kWcRows), (unsigned)((L.kpad + kWcCh - 1) / kWcCh),
-                            (unsigned)a->E),
+                            (unsigned)a->E + 1),
                        dim3(256), 0, s, a->w_codes_cm, a->w_scales_cm, a->N, a->K, a->comp_idx, (int)a->k, L.kpad,
-                       L.wcomp);
+                       L.wcomp, a->expert_offsets, (int)a->E, bm, L.tiles, L.ntiles, max_tiles, h_amax);
     if (int rc = last_launch()) return rc;
   } else if (a->k > 0) {
     const int64_t wrows = a->E * a->N;

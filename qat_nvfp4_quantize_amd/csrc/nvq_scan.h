@@ -33,21 +33,18 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* s_wave) {
   return wave > 0 ? v + s_wave[wave - 1] : v;
 }
 
-// Tile table of a row-tiled grouped GEMM, built by one workgroup of blockDim.x
-// >= E threads: expert e's rows [off[e], off[e + 1]) split into bm-row tiles,
-// tile i = (expert, first row), experts in order.  Thread e < E passes its
-// tile count nt and the inclusive prefix incl over the experts.  Tile i is
-// written by thread i % blockDim.x (its expert found by a binary search over
-// the prefixes in LDS), so consecutive tiles go out together however the
-// rows are spread over the experts.  s_incl: blockDim.x ints of LDS.
-__device__ __forceinline__ void write_tile_table(const int32_t* __restrict__ off, int E, int bm, int incl,
-                                                 int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                 int max_tiles, int* s_incl) {
-  const int e = threadIdx.x;
-  if (e < E) s_incl[e] = incl;
-  if (e == E - 1) *ntiles = min(incl, max_tiles);
+// Tile table of a row-tiled grouped GEMM: expert e's rows [off[e], off[e + 1])
+// split into bm-row tiles, tile i = (expert, first row), experts in order.
+// s_incl[e] holds the inclusive prefix of the experts' tile counts (set by
+// the caller before calling).  Tile i is written by thread i % blockDim.x
+// (its expert found by a binary search over the prefixes), so consecutive
+// tiles go out together however the rows are spread over the experts.
+__device__ __forceinline__ void write_tiles_from_prefix(const int32_t* __restrict__ off, int E, int bm,
+                                                        const int* s_incl, int32_t* __restrict__ tiles,
+                                                        int32_t* __restrict__ ntiles, int max_tiles) {
   __syncthreads();
   const int total = min(s_incl[E - 1], max_tiles);
+  if (threadIdx.x == 0) *ntiles = total;
   for (int i = threadIdx.x; i < total; i += blockDim.x) {
     int lo = 0, hi = E - 1;  // the first expert whose inclusive prefix exceeds i
     while (lo < hi) {
@@ -61,6 +58,30 @@ __device__ __forceinline__ void write_tile_table(const int32_t* __restrict__ off
     tiles[2 * i] = lo;
     tiles[2 * i + 1] = off[lo] + (i - base) * bm;
   }
+}
+
+// The whole tile table from one workgroup of blockDim.x threads (a multiple
+// of 64, at most 1024), E <= 4 blockDim.x: thread t owns experts 4t .. 4t + 3.
+// s_wave: 16 ints of LDS; s_incl: E ints.
+__device__ __forceinline__ void build_tile_table(const int32_t* __restrict__ off, int E, int bm,
+                                                 int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                 int max_tiles, int* s_wave, int* s_incl) {
+  const int t = threadIdx.x;
+  int nt[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * t + q;
+    nt[q] = e < E ? (off[e + 1] - off[e] + bm - 1) / bm : 0;
+    sum += nt[q];
+  }
+  int run = block_inclusive_scan(sum, s_wave) - sum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * t + q;
+    run += nt[q];
+    if (e < E) s_incl[e] = run;
+  }
+  write_tiles_from_prefix(off, E, bm, s_incl, tiles, ntiles, max_tiles);
 }
 
 }  // namespace nvq
