@@ -14,6 +14,7 @@
 #include "nvq.h"
 #include "nvq_device.h"
 #include "nvq_internal.h"
+#include "nvq_scan.h"
 
 namespace nvq {
 namespace {
@@ -134,41 +135,47 @@ __global__ __launch_bounds__(256) void k_perm_hist(const int32_t* __restrict__ i
 }
 
 // One workgroup: base[c][e] = offset of expert e + pairs of e in chunks < c.
-// Each expert's chunk column is split over 1024 / E threads (8 for E = 128):
-// a thread sums its contiguous range of chunks, the partial sums give each
-// range's start, an inclusive scan over the expert totals (Hillis-Steele in
-// LDS) gives the expert offsets, and each thread then rewrites its range in
-// batches of 16 (loads first, then stores, so the loads overlap).
+// Each expert's chunk column is split over 1024 / E threads (8 for E = 128),
+// thread t taking expert t % E, so the lanes of a wave read and write
+// consecutive experts of one chunk (whole lines; with the parts of one expert
+// in adjacent lanes every store touched eight lines).  A thread sums its
+// contiguous range of chunks, the partial sums give each range's start, a
+// workgroup scan over the expert totals gives the expert offsets, and each
+// thread then rewrites its range.  Both passes over the range go in batches
+// of 16 (the loads first, so they overlap).
 __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts, int64_t nchunks,
                                                    int E, int32_t* __restrict__ offsets) {
   __shared__ int32_t part_sum[1024];
-  __shared__ int32_t scan[1024];
+  __shared__ int32_t s_off[1025];
+  __shared__ int32_t s_wave[16];
   const int t = threadIdx.x;
   const int tpe = max(1, 1024 / E);
-  const int e = t / tpe, part = t - e * tpe;
-  const bool live = e < E;
+  const int part = t / E, e = t - part * E;
+  const bool live = part < tpe;
   const int64_t len = (nchunks + tpe - 1) / tpe;
   const int64_t cb = min<int64_t>(part * len, nchunks), ce = min<int64_t>(cb + len, nchunks);
   int32_t sum = 0;
   if (live)
-    for (int64_t c = cb; c < ce; ++c) sum += counts[c * E + e];
+    for (int64_t c = cb; c < ce; c += 16) {  // 16 loads in flight, then the adds
+      int32_t n[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) n[u] = counts[min<int64_t>(c + u, ce - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) sum += c + u < ce ? n[u] : 0;
+    }
   part_sum[t] = sum;
   __syncthreads();
   int32_t tot = 0;
   if (t < E)
-    for (int k = 0; k < tpe; ++k) tot += part_sum[t * tpe + k];
-  scan[t] = tot;
+    for (int k = 0; k < tpe; ++k) tot += part_sum[k * E + t];
+  const int32_t incl = block_inclusive_scan(tot, s_wave);
+  if (t < E) s_off[t] = incl - tot;
+  if (t == E - 1) s_off[E] = incl;
   __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int32_t v = t >= d ? scan[t - d] : 0;
-    __syncthreads();
-    scan[t] += v;
-    __syncthreads();
-  }
   if (live) {
-    const int32_t off_e = e > 0 ? scan[e - 1] : 0;
+    const int32_t off_e = s_off[e];
     int32_t run = off_e;
-    for (int k = 0; k < part; ++k) run += part_sum[e * tpe + k];
+    for (int k = 0; k < part; ++k) run += part_sum[k * E + e];
     for (int64_t c = cb; c < ce; c += 16) {
       int32_t n[16];
 #pragma unroll
@@ -182,33 +189,57 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts
     }
     if (part == 0) offsets[e] = off_e;
   }
-  if (t == 0) offsets[E] = scan[E - 1];
+  if (t == 0) offsets[E] = s_off[E];
 }
 
-// Stable scatter: one wave per chunk walks its pairs in order 64 at a time;
-// the rank of a pair among equal experts in a step is the popcount of the
-// lower lanes whose expert matches (found with log2(E) ballots).
-// kOwnBase: counts holds the chunk histograms (not yet scanned), and the wave
-// derives its chunk's bases itself: expert e's offset (the in-order sum of the
-// totals of experts < e) plus e's pairs in earlier chunks; chunk 0 writes the
-// expert offsets.  For few chunks this replaces k_perm_scan.  Reports ids
-// outside [0, E) in the status word.
+// Stable scatter: one workgroup of kScatWaves waves per chunk, wave w taking
+// the w-th quarter of the chunk's pairs, 64 at a time (its ids loaded into
+// registers first, so no step waits on memory).  The rank of a pair among
+// equal experts in a step is the popcount of the lower lanes whose expert
+// matches (found with log2(E) ballots); each wave first ranks its pairs
+// against its own earlier steps (a per-wave count per expert in LDS), then,
+// after one barrier, adds the counts of the earlier waves of the chunk and
+// the chunk's base.  Four waves shorten the serial chain of steps fourfold.
+// kOwnBase: counts holds the chunk histograms (not yet scanned), and the
+// workgroup derives its chunk's bases itself: expert e's offset (the in-order
+// sum of the totals of experts < e) plus e's pairs in earlier chunks; chunk 0
+// writes the expert offsets.  For few chunks this replaces k_perm_scan.
+// Reports ids outside [0, E) in the status word.  LDS: 5 E ints (dynamic).
+constexpr int kScatWaves = 4;
+constexpr int kScatSteps = kPermChunk / (64 * kScatWaves);  // steps per wave
+
+// Orders one wave's LDS accesses across its lanes (no instruction: a wave's
+// LDS operations complete in program order; this keeps the compiler from
+// moving them across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 template <bool kOwnBase>
-__global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__ ids, int64_t P,
-                                                    int E, int64_t nchunks, const int32_t* __restrict__ base,
-                                                    int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ sorted_pair,
-                                                    int32_t* __restrict__ pos, uint32_t* __restrict__ status) {
-  extern __shared__ int32_t cnt[];
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kScatWaves) void k_perm_scatter(
+    const int32_t* __restrict__ ids, int64_t P, int E, int64_t nchunks, const int32_t* __restrict__ base,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pos,
+    uint32_t* __restrict__ status) {
+  extern __shared__ int32_t cnt[];  // [E] chunk bases, then [kScatWaves][E] per-wave counts
+  __shared__ int32_t s_wave[16];
+  int32_t* wcnt = cnt + E;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t p0 = (int64_t)blockIdx.x * kPermChunk + (int64_t)w * (64 * kScatSteps);
+  int32_t eid[kScatSteps];
+#pragma unroll
+  for (int step = 0; step < kScatSteps; ++step) {
+    const int64_t p = p0 + step * 64 + lane;
+    eid[step] = p < P ? ids[p] : -1;
+  }
   if (kOwnBase) {
-    // lane l owns experts [l * per, (l + 1) * per); before: e's pairs in
+    // thread t owns experts [t * per, (t + 1) * per); before: e's pairs in
     // chunks < this one, tot: in all chunks
-    const int per = (E + 63) / 64;
+    const int per = (E + 64 * kScatWaves - 1) / (64 * kScatWaves);
     const int c = (int)blockIdx.x;
-    int32_t run = 0;  // this lane's experts' totals, in expert order
+    int32_t run = 0;  // this thread's experts' totals, in expert order
     for (int q = 0; q < per; ++q) {
-      const int e = lane * per + q;
+      const int e = tid * per + q;
       int32_t before = 0, tot = 0;
       if (e < E) {
         for (int64_t c0 = 0; c0 < nchunks; c0 += 16) {  // 16 loads in flight, then the adds
@@ -222,64 +253,63 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__
             before += cc < c ? v[u] : 0;
           }
         }
-        cnt[e] = run + before;  // offset within this lane's range, fixed below
+        cnt[e] = run + before;  // offset within this thread's range, fixed below
       }
       run += tot;
     }
-    // exclusive scan of the lane totals over the wave
-    int32_t incl = run;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int32_t v = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += v;
-    }
-    const int32_t lane_off = incl - run;
+    const int32_t incl = block_inclusive_scan(run, s_wave);  // over the thread totals
+    const int32_t t_off = incl - run;
     for (int q = 0; q < per; ++q) {
-      const int e = lane * per + q;
-      if (e < E) cnt[e] += lane_off;
-    }
-    if (c == 0) {
-      // offsets[e] = bases of chunk 0 (no earlier chunks); offsets[E] = all pairs
-      for (int q = 0; q < per; ++q) {
-        const int e = lane * per + q;
-        if (e < E) offsets[e] = cnt[e];
+      const int e = tid * per + q;
+      if (e < E) {
+        cnt[e] += t_off;
+        if (c == 0) offsets[e] = cnt[e];  // chunk 0: no earlier chunks
       }
-      if (lane == 63) offsets[E] = incl;
     }
+    if (c == 0 && tid == 64 * kScatWaves - 1) offsets[E] = incl;  // all pairs
   } else {
-    for (int e = lane; e < E; e += 64) cnt[e] = base[(int64_t)blockIdx.x * E + e];
+    for (int e = tid; e < E; e += 64 * kScatWaves) cnt[e] = base[(int64_t)blockIdx.x * E + e];
   }
-  __syncthreads();
+  int32_t* my = wcnt + w * E;
+  for (int e = lane; e < E; e += 64) my[e] = 0;
+  wave_lds_sync();
   uint32_t bad = 0;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int64_t p0 = (int64_t)blockIdx.x * kPermChunk;
-  for (int step = 0; step < kPermChunk / 64; ++step) {
+  int32_t rank[kScatSteps];
+#pragma unroll
+  for (int step = 0; step < kScatSteps; ++step) {  // ranks within this wave's pairs
     const int64_t p = p0 + step * 64 + lane;
     const bool in = p < P;
-    int32_t e = in ? ids[p] : -1;
+    int32_t e = eid[step];
     const bool ok = in && e >= 0 && e < E;
     bad |= (in && !ok) ? 1u : 0u;
     if (!ok) e = -1;
+    eid[step] = e;
     uint64_t match = __ballot(ok);
     for (int b = 0; b < nbits; ++b) {
       const uint64_t m = __ballot(ok && ((e >> b) & 1));
       match &= (ok && ((e >> b) & 1)) ? m : ~m;
     }
+    rank[step] = 0;
+    if (ok) rank[step] = my[e] + __popcll(match & lt);
+    wave_lds_sync();
+    if (ok && (match >> lane) == 1ull) my[e] += __popcll(match);  // highest lane of its group
+    wave_lds_sync();
+  }
+  __syncthreads();  // every wave's counts and the chunk bases are in LDS
+#pragma unroll
+  for (int step = 0; step < kScatSteps; ++step) {
+    const int64_t p = p0 + step * 64 + lane;
+    const int32_t e = eid[step];
     int32_t dst = -1;
-    if (ok) {
-      const int rank = __popcll(match & lt);
-      dst = cnt[e] + rank;
-    }
-    __syncthreads();
-    if (ok) {
-      const bool last = (match >> lane) == 1ull;  // highest lane of its group
-      if (last) cnt[e] += __popcll(match);
+    if (e >= 0) {
+      dst = cnt[e] + rank[step];
+      for (int v = 0; v < w; ++v) dst += wcnt[v * E + e];  // pairs of e in the chunk's earlier waves
       sorted_pair[dst] = (int32_t)p;
     }
-    if (in) pos[p] = dst;
-    __syncthreads();
+    if (p < P) pos[p] = dst;
   }
   if (__any(bad) && lane == 0) atomicOr(status, (uint32_t)NVQ_STATUS_BAD_EXPERT);
 }
@@ -566,10 +596,12 @@ extern "C" int nvq_moe_permute(const int32_t* ids, int64_t T, int64_t topk, int6
   }
   if (P == 0) return NVQ_OK;
   if (own_base)
-    hipLaunchKernelGGL(k_perm_scatter<true>, dim3((unsigned)nchunks), dim3(64), E * sizeof(int32_t), s, ids,
+    hipLaunchKernelGGL(k_perm_scatter<true>, dim3((unsigned)nchunks), dim3(64 * kScatWaves),
+                       (1 + kScatWaves) * E * sizeof(int32_t), s, ids,
                        P, (int)E, nchunks, counts, expert_offsets, sorted_pair, pos, c.status());
   else
-    hipLaunchKernelGGL(k_perm_scatter<false>, dim3((unsigned)nchunks), dim3(64), E * sizeof(int32_t), s, ids,
+    hipLaunchKernelGGL(k_perm_scatter<false>, dim3((unsigned)nchunks), dim3(64 * kScatWaves),
+                       (1 + kScatWaves) * E * sizeof(int32_t), s, ids,
                        P, (int)E, nchunks, counts, expert_offsets, sorted_pair, pos, c.status());
   return last_launch();
 }

@@ -38,12 +38,14 @@ def test_route_and_permute(shape):
 
 
 @pytest.mark.parametrize("T,topk,E", [(5000, 4, 300), (8192, 8, 1024), (16384, 4, 128), (16385, 4, 128),
-                                     (1, 1, 7)])
+                                     (1, 1, 7), (20000, 4, 300), (9000, 8, 1024), (33000, 2, 7)])
 def test_permute_chunk_counts_and_wide_expert_sets(T, topk, E):
     """The permutation with the scatter deriving its own bases (at most 64
     chunks of 1024 pairs) and with the scan kernel (65 chunks and more):
-    expert counts above 64 per lane group (E = 300, 1024), the 64 / 65 chunk
-    boundary, a single pair; skewed ids leave experts empty."""
+    expert counts above one per thread (E = 300, 1024), the 64 / 65 chunk
+    boundary, a single pair; the scan with expert counts that do not divide
+    its 1024 threads (E = 300, 7) and with one thread per expert (E = 1024);
+    skewed ids leave experts empty."""
     nvq = _nvq()
     g = np.random.default_rng(T + E)
     ids = np.minimum(g.zipf(1.3, (T, topk)) - 1, E - 1).astype(np.int32)
