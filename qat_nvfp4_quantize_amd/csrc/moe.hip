@@ -586,7 +586,7 @@ extern "C" int nvq_moe_permute(const int32_t* ids, int64_t T, int64_t topk, int6
   hipLaunchKernelGGL(k_perm_hist, dim3((unsigned)nchunks), dim3(256), E * sizeof(int32_t), s, ids, P,
                      (int)E, counts, c.status());
   if (int rc = last_launch()) return rc;
-  // Few chunks: each scatter wave sums the histograms itself (reading them
+  // Few chunks: each scatter workgroup sums the histograms itself (reading them
   // all costs less than a separate scan launch); many: one scan workgroup.
   const bool own_base = nchunks <= kPermOwnBaseChunks && P > 0;
   if (!own_base) {
